@@ -1,0 +1,159 @@
+"""FP64 row-softmax oracle: a ctypes wrapper over ``liboracle_softmax.so``.
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+bench's CPU-baseline leg may import this package. The GPU library and its
+Python binding never import it, and the two share no code.
+
+The C source (``oracle_softmax.c``) states the definition it follows and the
+readings taken where the pages are silent. Every function here only marshals
+numpy buffers into that library.
+
+Arrays: FP32 data is passed as ``numpy.float32``; FP16 and BF16 data are passed
+as their raw 16-bit patterns (``numpy.uint16``; ``numpy.float16`` is accepted for
+FP16). A 2-D array may be a row-strided view (column stride must be one
+element); its row stride is taken from the view.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+F32, F16, BF16 = 0, 1, 2
+DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle_softmax.so")
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def _code(dtype) -> int:
+    if isinstance(dtype, str):
+        return DTYPES[dtype]
+    return int(dtype)
+
+
+def _storage(dtype) -> np.dtype:
+    return np.dtype(np.float32) if _code(dtype) == F32 else np.dtype(np.uint16)
+
+
+def _as_storage(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.asarray(a)
+    want = _storage(dtype)
+    if a.dtype == want:
+        return a
+    if a.dtype.itemsize == want.itemsize and a.dtype.kind in "fiu":
+        return a.view(want)
+    raise TypeError(f"array of {a.dtype} cannot hold dtype code {_code(dtype)} data")
+
+
+class Oracle:
+    """One loaded copy of the oracle library (``path`` defaults to the built one)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python oracle/build.py` "
+                "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_decode.argtypes = [vp, ctypes.c_int, i64, _DP]
+        lib.oracle_encode.argtypes = [_DP, ctypes.c_int, i64, vp]
+        lib.oracle_softmax_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, _DP, ctypes.c_int]
+        lib.oracle_max_threads.argtypes = []
+        for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_softmax_rows,
+                  lib.oracle_max_threads):
+            f.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return self.lib.oracle_max_threads()
+
+    def decode(self, bits: np.ndarray, dtype) -> np.ndarray:
+        """Stored elements -> float64, exactly."""
+        src = np.ascontiguousarray(_as_storage(bits, dtype))
+        out = np.empty(src.shape, np.float64)
+        if self.lib.oracle_decode(src.ctypes.data, _code(dtype), src.size, out.ctypes.data_as(_DP)):
+            raise ValueError("oracle_decode rejected its arguments")
+        return out
+
+    def encode(self, y: np.ndarray, dtype) -> np.ndarray:
+        """float64 -> stored elements, one round-to-nearest-even step."""
+        src = np.ascontiguousarray(y, dtype=np.float64)
+        out = np.empty(src.shape, _storage(dtype))
+        if self.lib.oracle_encode(src.ctypes.data_as(_DP), _code(dtype), src.size, out.ctypes.data):
+            raise ValueError("oracle_encode rejected its arguments")
+        return out
+
+    def softmax_f64(self, x: np.ndarray, dtype, rows=None, threads: int = 0) -> np.ndarray:
+        """FP64 softmax of the rows of a stored 2-D matrix ``x`` (row-strided view allowed).
+
+        ``rows``: optional sequence of row indices; the result then has one row per index.
+        """
+        a = _as_storage(x, dtype)
+        if a.ndim != 2:
+            raise ValueError("expected a 2-D matrix")
+        es = a.dtype.itemsize
+        M, N = a.shape
+        nrows = M if rows is None else len(rows)
+        if a.size == 0:
+            return np.empty((nrows, N), np.float64)
+        if N > 1 and a.strides[1] != es:
+            raise ValueError("column stride must be one element")
+        if a.strides[0] % es or a.strides[0] < 0:
+            raise ValueError("row stride must be a non-negative multiple of the element size")
+        in_stride = a.strides[0] // es if M > 1 else N
+        idx = None
+        if rows is not None:
+            idx = np.ascontiguousarray(rows, dtype=np.int64)
+            if idx.size and (idx.min() < 0 or idx.max() >= M):
+                raise IndexError("row index out of range")
+        out = np.empty((nrows, N), np.float64)
+        rc = self.lib.oracle_softmax_rows(
+            a.ctypes.data, _code(dtype), N, in_stride,
+            None if idx is None else idx.ctypes.data, nrows, out.ctypes.data_as(_DP), int(threads))
+        if rc:
+            raise ValueError("oracle_softmax_rows rejected its arguments")
+        return out
+
+    def reference(self, x: np.ndarray, dtype, rows=None, threads: int = 0):
+        """(y_f64, y_rounded): the FP64 softmax and its one RNE cast to ``dtype``."""
+        y = self.softmax_f64(x, dtype, rows=rows, threads=threads)
+        return y, self.encode(y, dtype)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def _load():
+    return default().lib
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+def decode(bits, dtype):
+    return default().decode(bits, dtype)
+
+
+def encode(y, dtype):
+    return default().encode(y, dtype)
+
+
+def softmax_f64(x, dtype, rows=None, threads: int = 0):
+    return default().softmax_f64(x, dtype, rows=rows, threads=threads)
+
+
+def reference(x, dtype, rows=None, threads: int = 0):
+    return default().reference(x, dtype, rows=rows, threads=threads)

@@ -1,0 +1,228 @@
+/*
+ * oracle_softmax.c -- plain FP64 row-softmax oracle (C99 + OpenMP over rows).
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load this library. The GPU product path never calls it, and
+ * it shares no code, header, table or constant with the GPU library.
+ *
+ * What it computes, per row i of an M x N matrix stored row-major with a row
+ * stride in elements (column stride 1):
+ *
+ *   y[i,j] = exp(x[i,j] - m_i) / sum_k exp(x[i,k] - m_i),  m_i = max_k x[i,k]
+ *
+ * This is the softmax the pages define in words: subtract the row maximum,
+ * exponentiate, divide by the sum ("Triton: Writing GPU Kernels in Python,
+ * Measured", section "Step 2: a fused softmax"; "Fused Softmax on GPU",
+ * sections "The Bandwidth Formula" and "Triton -- One Block Per Row", whose
+ * row-stride arguments this API keeps).  The reference value is computed in
+ * FP64 and rounded once to the storage dtype (Warpline README, the paragraph
+ * on how the K2 reference is formed: FP64, then one cast).
+ *
+ * Steps, in the order the definition states them:
+ *   1. decode every stored element exactly to double (FP32 widen; FP16 and
+ *      BF16 by their IEEE bit layouts);
+ *   2. m = max over the row (NaN entries do not win the max; they poison the
+ *      sum in step 4, so a row holding NaN comes out all NaN);
+ *   3. e_j = exp(x_j - m) with libm exp in double;
+ *   4. s = sum of e_j, added left to right in double;
+ *   5. y_j = e_j / s in double.
+ *
+ * Readings where the pages are silent (listed in the design notes too):
+ *   - a row whose entries are all -inf (and an empty row) has no finite
+ *     maximum; the online-merge guard of "Measured optimization case studies",
+ *     section "Wide rows: loop in one program, or split across programs",
+ *     treats such a part as shift 0 with sum 0.  For a whole row this oracle
+ *     returns all zeros (masked entries give 0, and nothing is unmasked);
+ *   - +inf anywhere makes exp(inf - inf) = NaN, so the row is all NaN (plain
+ *     IEEE evaluation of the definition, no special case);
+ *   - the final cast rounds to nearest, ties to even (IEEE default).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* dtype codes of this oracle's own API */
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+static int elem_size(int dtype) {
+    switch (dtype) {
+    case ORC_F32: return 4;
+    case ORC_F16: return 2;
+    case ORC_BF16: return 2;
+    default: return 0;
+    }
+}
+
+/* ---------------------------------------------------------------- decode */
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double decode_f16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1f;
+    int fr = h & 0x3ff;
+    double v;
+    if (ex == 0) {
+        v = ldexp((double)fr, -24); /* zero or subnormal: fr * 2^-24 */
+    } else if (ex == 31) {
+        v = fr ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(fr + 1024), ex - 25); /* 1.fr * 2^(ex-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+static double decode_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double decode_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double load_elem(const unsigned char *p, int dtype) {
+    if (dtype == ORC_F32) {
+        uint32_t u;
+        memcpy(&u, p, 4);
+        return decode_f32(u);
+    }
+    uint16_t h;
+    memcpy(&h, p, 2);
+    return dtype == ORC_F16 ? decode_f16(h) : decode_bf16(h);
+}
+
+/* ---------------------------------------------------------------- encode */
+
+/*
+ * Round a double to a binary format with `mant` stored fraction bits and an
+ * exponent field of `ebits` bits, nearest-even, in one step from the double
+ * (no intermediate rounding).  Returns the bit pattern.
+ *
+ * Method: take E = floor(log2 |v|) clamped below at the format's smallest
+ * normal exponent; scale |v| by 2^(mant - E) so that one unit in the last
+ * place of the target is 1.0 (a power-of-two scaling, exact in double); round
+ * that to an integer with nearbyint (ties to even in the default rounding
+ * mode); rebuild the fields, carrying into the exponent when the rounding
+ * reaches 2^(mant+1), and overflowing to infinity above the largest exponent.
+ */
+static uint32_t encode_binary(double v, int mant, int ebits) {
+    const int bias = (1 << (ebits - 1)) - 1;
+    const int emin = 1 - bias, emax = bias;
+    const uint32_t sign = signbit(v) ? (1u << (mant + ebits)) : 0u;
+    const uint32_t exp_all = ((1u << ebits) - 1u) << mant;
+    if (isnan(v)) return sign | exp_all | (1u << (mant - 1));
+    double a = fabs(v);
+    if (isinf(a)) return sign | exp_all;
+    if (a == 0.0) return sign;
+    int E = ilogb(a);
+    if (E < emin) E = emin;
+    double r = nearbyint(ldexp(a, mant - E));
+    if (r >= ldexp(1.0, mant + 1)) { /* rounded up to the next binade */
+        r = ldexp(1.0, mant);
+        E += 1;
+    }
+    if (E > emax) return sign | exp_all; /* overflow to infinity */
+    uint32_t q = (uint32_t)r;
+    if (q < (1u << mant)) return sign | q; /* subnormal (E == emin) */
+    return sign | ((uint32_t)(E + bias) << mant) | (q - (1u << mant));
+}
+
+/* ---------------------------------------------------------------- API */
+
+int oracle_elem_size(int dtype) { return elem_size(dtype); }
+
+int oracle_decode(const void *src, int dtype, int64_t count, double *dst) {
+    int es = elem_size(dtype);
+    if (!es || count < 0) return -1;
+    const unsigned char *p = (const unsigned char *)src;
+    for (int64_t k = 0; k < count; ++k) dst[k] = load_elem(p + k * es, dtype);
+    return 0;
+}
+
+int oracle_encode(const double *src, int dtype, int64_t count, void *dst) {
+    if (!elem_size(dtype) || count < 0) return -1;
+    for (int64_t k = 0; k < count; ++k) {
+        if (dtype == ORC_F32) {
+            uint32_t u = encode_binary(src[k], 23, 8);
+            memcpy((unsigned char *)dst + 4 * k, &u, 4);
+        } else {
+            uint16_t h = (uint16_t)(dtype == ORC_F16 ? encode_binary(src[k], 10, 5)
+                                                     : encode_binary(src[k], 7, 8));
+            memcpy((unsigned char *)dst + 2 * k, &h, 2);
+        }
+    }
+    return 0;
+}
+
+/* Softmax of one decoded row x[0..n) into y[0..n). */
+static void softmax_row(const double *x, int64_t n, double *y) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j)
+        if (x[j] > m) m = x[j];
+    if (m == -INFINITY) { /* all entries -inf (or NaN-free empty row): zeros */
+        int has_nan = 0;
+        for (int64_t j = 0; j < n; ++j) has_nan |= isnan(x[j]);
+        for (int64_t j = 0; j < n; ++j) y[j] = has_nan ? NAN : 0.0;
+        return;
+    }
+    double s = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        y[j] = exp(x[j] - m);
+        s += y[j];
+    }
+    for (int64_t j = 0; j < n; ++j) y[j] = y[j] / s;
+}
+
+/*
+ * Softmax of selected rows.
+ *   in        : base of the stored matrix (row r starts at in + r*in_stride elements)
+ *   rows      : row indices to evaluate, or NULL for rows 0..nrows-1
+ *   y         : output, nrows x cols doubles, contiguous
+ *   threads   : OpenMP threads (<= 0: the runtime default)
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_softmax_rows(const void *in, int dtype, int64_t cols, int64_t in_stride,
+                        const int64_t *rows, int64_t nrows, double *y, int threads) {
+    int es = elem_size(dtype);
+    if (!es || cols < 0 || nrows < 0 || in_stride < cols) return -1;
+    if (nrows == 0 || cols == 0) return 0;
+    const unsigned char *base = (const unsigned char *)in;
+#ifdef _OPENMP
+    if (threads <= 0) threads = omp_get_max_threads();
+#else
+    threads = 1;
+#endif
+    int bad = 0;
+#pragma omp parallel num_threads(threads) reduction(| : bad)
+    {
+        double *x = (double *)malloc(sizeof(double) * (size_t)cols);
+        if (!x) bad = 1;
+#pragma omp for schedule(static)
+        for (int64_t k = 0; k < nrows; ++k) {
+            if (!x) continue;
+            int64_t r = rows ? rows[k] : k;
+            const unsigned char *row = base + (size_t)(r * in_stride) * (size_t)es;
+            for (int64_t j = 0; j < cols; ++j) x[j] = load_elem(row + (size_t)j * es, dtype);
+            softmax_row(x, cols, y + (size_t)k * (size_t)cols);
+        }
+        free(x);
+    }
+    return bad ? -1 : 0;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

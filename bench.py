@@ -1,0 +1,361 @@
+"""Bench: cold BF16 4096 x 4096 row softmax on one MI355X through the C ABI.
+
+One step is one cold call of ``sm_softmax_fwd`` over the seeded 4096 x 4096 BF16
+matrix (x ~ N(0, 2^2), seed 2026), after a 1 GiB read-modify-write sweep that
+evicts the input from L2 and MALL. The sweep runs outside the timed events.
+
+Protocol (the pages' methodology, restated):
+  * a correctness gate before any timing (Warpline README, the correctness
+    paragraph): output properties on the GPU first, then, in the CPU-baseline leg,
+    the FP64 oracle's result on the same input compared element by element with
+    the timed call's output (the run fails if they disagree);
+  * a 200 ms burst of calls to bring the clocks up ("Measured optimization case
+    studies", section "GPU clocks: the first calls after an idle pause");
+  * W untimed cold steps, then K timed cold steps, each bracketed by its own pair
+    of HIP events on the launch stream; median, p10, p90, MAD, min, max and mean
+    are reported (Warpline README, the suite-protocol paragraph);
+  * throughput from the byte model 2 * M * N * elem (one read and one write of
+    every element: "Fused Softmax on GPU", section "The Bandwidth Formula"), as a
+    fraction of the 8 TB/s HBM3E peak and of a measured 16-byte copy moving the
+    same bytes cold;
+  * the FP64 oracle timed on this host's cores on the same input (a baseline,
+    not the target).
+
+Prints ONE JSON line on stdout. ``--sweep`` also times every workload and plan and
+writes those lines to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
+FLUSH_BYTES = 1 << 30
+WORKLOAD = "normal_bf16_4096x4096"
+KERNEL_SOURCES = ["include/sm_softmax.h", "memory_bound_row_sm_amd/csrc/sm_device.hpp",
+                  "memory_bound_row_sm_amd/csrc/sm_kernels.hpp",
+                  "memory_bound_row_sm_amd/csrc/sm_rows_inst.inl",
+                  "memory_bound_row_sm_amd/csrc/sm_softmax.hip"]
+
+
+def byte_model(M: int, N: int, elem_bytes: int, wide: bool = False) -> int:
+    """Algorithmic bytes of one call: every element read once and written once
+    (2 M N elem), or read twice and written once on the two-pass wide path."""
+    return (3 if wide else 2) * M * N * elem_bytes
+
+
+def stats_us(samples_ms) -> dict:
+    a = np.asarray(samples_ms, dtype=np.float64) * 1e3
+    med = float(np.median(a))
+    return {"median_us": med, "mean_us": float(a.mean()), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "mad_us": float(np.median(np.abs(a - med))),
+            "min_us": float(a.min()), "max_us": float(a.max()), "n": int(a.size)}
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, launch_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Per-call HIP event pairs on the launch stream (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def time(self, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        self.pairs.append((ev0, ev1))
+
+    def samples_ms(self):
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sweep", action="store_true", help="also time every workload and plan (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the oracle timing on the host")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(rows shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import memory_bound_row_sm_amd as sm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    sm.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    s_handle = stream.cuda_stream
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- input
+    x_cpu = workloads.generate(WORKLOAD)
+    sha = workloads.sha256(x_cpu)
+    x = x_cpu.to(dev)
+    out = torch.full_like(x, float("nan"))
+    M, N = x.shape
+    es = x.element_size()
+    info = sm.plan_for(x, out)
+    model_bytes = byte_model(M, N, es, wide=info["plan_name"] == "wide")
+    assert model_bytes == info["model_bytes"]
+    log(f"[bench] {WORKLOAD}: {M}x{N} bf16, sha256 {sha[:16]}, plan {info['plan_name']} "
+        f"G={info['lanes_per_row']} V={info['vecs_per_lane']} grid={info['grid']}")
+
+    def call(xi=x, oi=out):
+        rc = sm.sm_softmax_fwd(xi.data_ptr(), oi.data_ptr(), xi.shape[0], xi.shape[1],
+                               xi.stride(0), oi.stride(0), sm.SM_BF16 if xi.dtype == torch.bfloat16
+                               else (sm.SM_F16 if xi.dtype == torch.float16 else sm.SM_F32),
+                               s_handle)
+        if rc != 0:
+            raise sm.SoftmaxError(rc, "sm_softmax_fwd")
+
+    # ---------------------------------------------------------------- correctness gate
+    # Properties every correct output has (finite, in [0, 1], rows summing to 1
+    # within the BF16 rounding bound); the element-wise oracle comparison runs in
+    # the CPU-baseline leg below, on the same input.
+    call()
+    torch.cuda.synchronize()
+    sums = out.sum(dim=1, dtype=torch.float64)
+    gate_ok = bool(torch.isfinite(out).all()) and bool(((out >= 0) & (out <= 1)).all()) and \
+        float((sums - 1).abs().max()) <= 2.0 ** -8 + 1e-5
+    if not gate_ok:
+        log("[bench] property gate FAILED")
+        return 1
+    log("[bench] property gate passed")
+
+    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def flush():
+        rc = sm.sm_bench_flush(flush_buf.data_ptr(), FLUSH_BYTES, s_handle)
+        if rc != 0:
+            raise sm.SoftmaxError(rc, "sm_bench_flush")
+
+    # ---------------------------------------------------------------- clocks up
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- cold lane
+    for _ in range(args.warmup):
+        flush()
+        call()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        flush()
+        timer.time(call)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cold = stats_us(timer.samples_ms())
+
+    # ---------------------------------------------------------------- warm lane (diagnostic)
+    wt = Timer(torch)
+    for _ in range(args.steps):
+        wt.time(call)
+    warm = stats_us(wt.samples_ms())
+
+    # ---------------------------------------------------------------- copy ceiling, same bytes, cold
+    src = torch.empty(model_bytes // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+
+    def copy():
+        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), 0, s_handle)
+        if rc != 0:
+            raise sm.SoftmaxError(rc, "sm_bench_copy")
+
+    for _ in range(args.warmup):
+        flush()
+        copy()
+    ct = Timer(torch)
+    for _ in range(args.steps):
+        flush()
+        ct.time(copy)
+    copy_cold = stats_us(ct.samples_ms())
+    del src, dst
+
+    gbps = model_bytes / (cold["mean_us"] * 1e-6) / 1e9
+    gbps_median = model_bytes / (cold["median_us"] * 1e-6) / 1e9
+    copy_gbps = model_bytes / (copy_cold["mean_us"] * 1e-6) / 1e9
+    log(f"[bench] cold mean {cold['mean_us']:.2f} us median {cold['median_us']:.2f} us -> "
+        f"{gbps:.0f} GB/s ({100 * gbps / PEAK_GBPS:.1f}% of 8 TB/s); copy ceiling {copy_gbps:.0f} GB/s; "
+        f"warm median {warm['median_us']:.2f} us")
+
+    # ---------------------------------------------------------------- sweep (stderr)
+    if args.sweep:
+        sweep(torch, sm, workloads, flush, s_handle, log, args)
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu, parity = None, {"passed": None, "note": "oracle leg skipped (--no-cpu-baseline)"}
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(x_cpu, out, model_bytes, args.cpu_seconds, log)
+        if not parity.get("passed"):
+            log(f"[bench] oracle parity FAILED: {parity}")
+
+    traffic = load_traffic(WORKLOAD, model_bytes)
+    result = {
+        "metric": "achieved HBM GB/s (and % of MI355X peak) for cold BF16 softmax, 4096x4096",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cold["mean_us"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": M, "N": N, "cold": True,
+                   "plan": info["plan_name"], "lanes_per_row": info["lanes_per_row"],
+                   "vecs_per_lane": info["vecs_per_lane"], "grid": info["grid"],
+                   "input_sha256": sha},
+        "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+        "value_median_GBps": round(gbps_median, 1),
+        "cold_us": {k: round(v, 3) if isinstance(v, float) else v for k, v in cold.items()},
+        "warm_us": {k: round(v, 3) if isinstance(v, float) else v for k, v in warm.items()},
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
+        "timed_region_wall_s": round(wall, 4),
+        "parity": parity,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if parity.get("passed") is not False else 1
+
+
+def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
+    """The FP64 oracle, as it stands, on this host's cores: repetitions of the whole
+    4096 x 4096 input until the budget is spent (median per repetition), and one
+    single-thread run for reference. The oracle's result on this input is also
+    compared element by element with the GPU output of the timed call."""
+    import oracle
+    import workloads
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import compare
+    s = workloads.storage_numpy(x_cpu)
+    threads = oracle.max_threads()
+    oracle.softmax_f64(s, "bf16", threads=threads)  # warm-up
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or len(times) < 3:
+        t = time.perf_counter()
+        oracle.softmax_f64(s, "bf16", threads=threads)
+        times.append(time.perf_counter() - t)
+    med = statistics.median(times)
+    t = time.perf_counter()
+    oracle.softmax_f64(s, "bf16", threads=1)
+    t1 = time.perf_counter() - t
+    res = {"value": round(model_bytes / med / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"the whole 4096x4096 BF16 input, {len(times)} repetitions in "
+                     f"{sum(times):.1f} s, median per repetition {med * 1e3:.1f} ms",
+           "value_1_thread": round(model_bytes / t1 / 1e9, 3)}
+    log(f"[bench] cpu oracle: {res}")
+    try:
+        parity = {"passed": True, **compare(gpu_out, x_cpu, what="bench output")}
+    except AssertionError as e:
+        parity = {"passed": False, "error": str(e)[:500]}
+    log(f"[bench] oracle parity: {parity}")
+    return res, parity
+
+
+def sweep(torch, sm, workloads, flush, s_handle, log, args):
+    """Cold timing of every workload under every plan that can take it."""
+    names = ["normal_f32_128x781", "normal_bf16_4096x4096",
+             *[f"spiky_f16_8192x{n}" for n in workloads.SPIKE_WIDTHS],
+             "offset_bf16_64x131072", "causal_bf16_524288x2048"]
+    plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3}
+    steps = max(20, args.steps // 4)
+    for name in names:
+        x = workloads.generate(name).to("cuda")
+        out = torch.empty_like(x)
+        M, N = x.shape
+        dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[x.dtype]
+        for pname, p in plans.items():
+            if p in (1, 2) and N > 8192:
+                continue
+            opts = {"plan": p, "prefetch": -1}
+            info = sm.plan_for(x, out, opts)
+
+            def call():
+                rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N, dt, opts, 0, 0,
+                                          s_handle)
+                if rc != 0:
+                    raise sm.SoftmaxError(rc)
+
+            for _ in range(5):
+                flush()
+                call()
+            t = Timer(torch)
+            for _ in range(steps):
+                flush()
+                t.time(call)
+            st = stats_us(t.samples_ms())
+            gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
+            line = {"workload": name, "plan": pname, "resolved": info["plan_name"],
+                    "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
+                    "cpw": info["chunks_per_wave"], "grid": info["grid"],
+                    "model_bytes": info["model_bytes"], "mean_us": round(st["mean_us"], 3),
+                    "median_us": round(st["median_us"], 3), "GBps": round(gb, 1),
+                    "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
+            log("[sweep] " + json.dumps(line))
+        del x, out
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    sys.exit(main())

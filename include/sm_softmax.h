@@ -1,0 +1,167 @@
+/*
+ * sm_softmax.h -- C ABI of the MI355X (gfx950) fused row-softmax library.
+ *
+ * Operation (every entry point below computes exactly this):
+ *
+ *     y[i,j] = exp(x[i,j] - m_i) / sum_k exp(x[i,k] - m_i),   m_i = max_k x[i,k]
+ *
+ * over an M x N matrix, softmax along the last dimension. This is the fused
+ * softmax of "Triton: Writing GPU Kernels in Python, Measured" (section "Step 2:
+ * a fused softmax") and of "Fused Softmax on GPU: From Naive PyTorch to
+ * Persistent Triton Kernels" (section "Triton -- One Block Per Row", whose
+ * kernel takes explicit input and output row strides). As in the Warpline
+ * README's description of its softmax kernel, the reduction state (maximum and
+ * sum) is FP32, irregular widths are masked, and the result is rounded once to
+ * the storage dtype (round to nearest, ties to even).
+ *
+ * Layout: row i of the input starts at in + i*in_stride elements, row i of the
+ * output at out + i*out_stride elements; columns are contiguous (stride 1).
+ * Input and output share one dtype. Strides are in elements, not bytes.
+ *
+ * Ownership: `in` and `out` are device pointers on the current HIP device,
+ * owned by the caller (hipMalloc, a torch tensor, ...). The library keeps only
+ * a per-device cache of device properties and kernel occupancy. All launches
+ * are asynchronous on `stream`; faults inside a kernel surface at the caller's
+ * next synchronisation.
+ *
+ * Special values (readings where the pages say nothing, kept by every plan):
+ *   - -inf entries give exactly 0; a row whose entries are all -inf gives a
+ *     row of zeros (the pages' online-merge guard gives such a part a zero
+ *     sum; this library then outputs 0 instead of 0/0);
+ *   - a row holding NaN or +inf gives a row of NaN.
+ *
+ * Errors: every argument check runs on the host before any HIP call, so a
+ * rejected call has no side effect. A zero-sized problem (M == 0 or N == 0)
+ * returns SM_OK without launching anything and without touching the pointers.
+ */
+#ifndef SM_SOFTMAX_H
+#define SM_SOFTMAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SM_SOFTMAX_VERSION 10000 /* 1.0.0 */
+
+typedef enum sm_dtype { SM_F32 = 0, SM_F16 = 1, SM_BF16 = 2 } sm_dtype;
+
+typedef enum sm_status {
+    SM_OK = 0,
+    SM_ERR_INVALID = -1,   /* bad size, stride, pointer or alignment */
+    SM_ERR_DTYPE = -2,     /* unknown dtype code */
+    SM_ERR_OVERLAP = -3,   /* out overlaps in other than exactly in place */
+    SM_ERR_HIP = -4,       /* a HIP runtime call or kernel launch failed */
+    SM_ERR_NO_DEVICE = -5, /* no usable HIP device */
+    SM_ERR_WORKSPACE = -6, /* caller workspace too small or misaligned */
+    SM_ERR_PLAN = -7       /* forced plan or shape cannot cover this problem */
+} sm_status;
+
+/* Plans: the three kernel paths.
+ *   RESIDENT   -- one-pass; every row is held in registers by one group of
+ *                 lanes (a sub-wave, a wave, or a workgroup of up to 16 waves
+ *                 with a cross-wave step in LDS); the grid covers every row
+ *                 once. Each element is read once and written once.
+ *   PERSISTENT -- the same one-pass row body, launched on occupancy x CUs
+ *                 workgroups that walk the rows with a grid stride and load
+ *                 the next row while computing the current one ("Fused
+ *                 Softmax on GPU", section "Persistent Triton Kernel").
+ *   WIDE       -- rows too wide to hold: pass 1 runs the online (max, sum)
+ *                 recurrence over 1024-element chunks and writes one FP32
+ *                 (max, sum) pair per wave; pass 2 merges a row's pairs and
+ *                 re-reads the row to normalise and write ("Measured
+ *                 optimization case studies", section "Wide rows: loop in one
+ *                 program, or split across programs"; Warpline README, the
+ *                 description of its online path).
+ * AUTO picks RESIDENT/PERSISTENT for N <= 8192 and WIDE above. */
+typedef enum sm_plan {
+    SM_PLAN_AUTO = 0,
+    SM_PLAN_RESIDENT = 1,
+    SM_PLAN_PERSISTENT = 2,
+    SM_PLAN_WIDE = 3
+} sm_plan;
+
+/* Optional launch overrides (zero-initialise for "automatic"). */
+typedef struct sm_softmax_opts {
+    int plan;            /* sm_plan */
+    int lanes_per_row;   /* RESIDENT/PERSISTENT: 16, 32, 64, 128, 256, 512 or 1024; 0 = auto */
+    int vecs_per_lane;   /* RESIDENT/PERSISTENT: 16-byte vectors per lane, 1, 2, 4 or 8; 0 = auto */
+    int grid;            /* workgroups to launch; 0 = auto */
+    int chunks_per_wave; /* WIDE: 1024-element chunks per wave; 0 = auto */
+    int prefetch;        /* PERSISTENT: 1 = load the next row early, 0 = no; -1 = auto */
+} sm_softmax_opts;
+
+/* What a call would launch (filled by sm_softmax_plan_query). */
+typedef struct sm_plan_info {
+    int plan;              /* resolved sm_plan (never AUTO) */
+    int lanes_per_row;
+    int vecs_per_lane;
+    int prefetch;
+    int block;             /* threads per workgroup */
+    int64_t grid;          /* workgroups per launch */
+    int chunks_per_wave;   /* WIDE only */
+    int64_t waves_per_row; /* WIDE only */
+    int launches;          /* 1, or 2 for WIDE */
+    int same_phase;        /* input and output rows share their 16-byte phase */
+    int64_t workspace_bytes; /* WIDE scratch: M * waves_per_row * 8 bytes */
+    int64_t model_bytes;   /* algorithmic bytes: 2*M*N*elem one-pass, 3*M*N*elem WIDE */
+} sm_plan_info;
+
+/*
+ * Fused row softmax, asynchronous on `stream` (0 = the null stream).
+ *   in, out     : device pointers, element-aligned; out == in with
+ *                 out_stride == in_stride is allowed (in place); any other
+ *                 overlap of the two row sets -> SM_ERR_OVERLAP
+ *   M, N        : rows and columns (N <= 2^31 - 1)
+ *   in_stride,
+ *   out_stride  : row strides in elements, >= N when M > 1
+ *   dtype       : sm_dtype of both tensors
+ * The WIDE plan takes its scratch stream-ordered from the device's default
+ * memory pool (hipMallocAsync / hipFreeAsync on `stream`), so concurrent calls
+ * on different streams never share scratch.
+ * Returns SM_OK or a negative sm_status.
+ */
+int sm_softmax_fwd(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,
+                   int64_t out_stride, int dtype, hipStream_t stream);
+
+/*
+ * As sm_softmax_fwd, with launch overrides and optional caller scratch.
+ *   opts        : NULL = automatic
+ *   workspace   : device memory of at least plan_info.workspace_bytes, 16-byte
+ *                 aligned, used only by the WIDE plan; NULL = allocate
+ *                 stream-ordered as sm_softmax_fwd does. The caller must not
+ *                 reuse it until the call's work on `stream` has finished.
+ */
+int sm_softmax_fwd_ex(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,
+                      int64_t out_stride, int dtype, const sm_softmax_opts *opts,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Resolve the plan a call would use, without launching anything.
+ *   num_cus > 0 : evaluate on the host only for a device with that many
+ *                 compute units (occupancy assumed: 8 workgroups of 256
+ *                 threads per CU); no HIP call is made
+ *   num_cus == 0: use the current HIP device and its measured occupancy
+ * Pointers are used only for their alignment and overlap.
+ */
+int sm_softmax_plan_query(const void *in, const void *out, int64_t M, int64_t N,
+                          int64_t in_stride, int64_t out_stride, int dtype,
+                          const sm_softmax_opts *opts, int num_cus, sm_plan_info *info);
+
+/* Static text for a status code. */
+const char *sm_softmax_strerror(int status);
+
+/* SM_SOFTMAX_VERSION of the built library. */
+int sm_softmax_version(void);
+
+/* The hipError_t of the most recent SM_ERR_HIP on the calling thread (0 if none). */
+int sm_softmax_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SM_SOFTMAX_H */

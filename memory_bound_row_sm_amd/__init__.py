@@ -1,0 +1,232 @@
+"""Python binding of the gfx950 row-softmax library (``libsm_softmax.so``).
+
+Argument marshalling only: every function calls the C entry point of the same
+name declared in ``include/sm_softmax.h`` / ``include/sm_bench.h``; all work runs
+in the library's HIP kernels. PyTorch is used for device memory and streams in
+``softmax()``, a convenience wrapper that passes a tensor's pointer, row stride
+and the current stream to ``sm_softmax_fwd_ex``.
+
+There is no fallback: if the library is not built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "SM_F32", "SM_F16", "SM_BF16", "SM_PLAN_AUTO", "SM_PLAN_RESIDENT", "SM_PLAN_PERSISTENT",
+    "SM_PLAN_WIDE", "SmOpts", "SmPlanInfo", "SoftmaxError", "lib", "lib_path",
+    "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_strerror",
+    "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
+    "softmax", "plan_for", "EXPORTED_SYMBOLS",
+]
+
+SM_F32, SM_F16, SM_BF16 = 0, 1, 2
+SM_PLAN_AUTO, SM_PLAN_RESIDENT, SM_PLAN_PERSISTENT, SM_PLAN_WIDE = 0, 1, 2, 3
+PLAN_NAMES = {SM_PLAN_AUTO: "auto", SM_PLAN_RESIDENT: "resident",
+              SM_PLAN_PERSISTENT: "persistent", SM_PLAN_WIDE: "wide"}
+STATUS = {0: "SM_OK", -1: "SM_ERR_INVALID", -2: "SM_ERR_DTYPE", -3: "SM_ERR_OVERLAP",
+          -4: "SM_ERR_HIP", -5: "SM_ERR_NO_DEVICE", -6: "SM_ERR_WORKSPACE", -7: "SM_ERR_PLAN"}
+
+EXPORTED_SYMBOLS = (
+    "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_strerror",
+    "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libsm_softmax.so")
+
+
+class SmOpts(ctypes.Structure):
+    _fields_ = [("plan", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
+                ("vecs_per_lane", ctypes.c_int), ("grid", ctypes.c_int),
+                ("chunks_per_wave", ctypes.c_int), ("prefetch", ctypes.c_int)]
+
+
+class SmPlanInfo(ctypes.Structure):
+    _fields_ = [("plan", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
+                ("vecs_per_lane", ctypes.c_int), ("prefetch", ctypes.c_int),
+                ("block", ctypes.c_int), ("grid", ctypes.c_int64),
+                ("chunks_per_wave", ctypes.c_int), ("waves_per_row", ctypes.c_int64),
+                ("launches", ctypes.c_int), ("same_phase", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_int64), ("model_bytes", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["plan_name"] = PLAN_NAMES.get(self.plan, str(self.plan))
+        return d
+
+
+class SoftmaxError(RuntimeError):
+    def __init__(self, status: int, where: str = "sm_softmax"):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({sm_softmax_strerror(status)})"
+        if status == -4:
+            msg += f", hipError {sm_softmax_last_hip_error()}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        try:
+            # torch ships its own copy of the HIP runtime under the same soname; loading
+            # torch first makes this library bind to that copy, so torch's device pointers
+            # and stream handles belong to the runtime our kernels are launched through
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        if not os.path.exists(lib_path):
+            raise RuntimeError(
+                f"{lib_path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python memory_bound_row_sm_amd/build.py`")
+        L = ctypes.CDLL(lib_path)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.sm_softmax_fwd.argtypes = [vp, vp, i64, i64, i64, i64, ci, vp]
+        L.sm_softmax_fwd_ex.argtypes = [vp, vp, i64, i64, i64, i64, ci, ctypes.POINTER(SmOpts),
+                                        vp, ctypes.c_size_t, vp]
+        L.sm_softmax_plan_query.argtypes = [vp, vp, i64, i64, i64, i64, ci,
+                                            ctypes.POINTER(SmOpts), ci, ctypes.POINTER(SmPlanInfo)]
+        L.sm_softmax_strerror.argtypes = [ci]
+        L.sm_softmax_strerror.restype = ctypes.c_char_p
+        L.sm_softmax_version.argtypes = []
+        L.sm_softmax_last_hip_error.argtypes = []
+        L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, vp]
+        L.sm_bench_flush.argtypes = [vp, ctypes.c_size_t, vp]
+        for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
+                  L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_bench_copy,
+                  L.sm_bench_flush):
+            f.restype = ci
+        _lib = L
+    return _lib
+
+
+def _opts(opts) -> SmOpts | None:
+    if opts is None:
+        return None
+    if isinstance(opts, SmOpts):
+        return opts
+    o = SmOpts(0, 0, 0, 0, 0, -1)
+    for k, v in dict(opts).items():
+        setattr(o, k, int(v))
+    return o
+
+
+# ---------------------------------------------------------------- C entry points
+
+def sm_softmax_fwd(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: int, out_stride: int,
+                   dtype: int, stream: int = 0) -> int:
+    return lib().sm_softmax_fwd(in_ptr, out_ptr, M, N, in_stride, out_stride, dtype, stream)
+
+
+def sm_softmax_fwd_ex(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: int, out_stride: int,
+                      dtype: int, opts=None, workspace: int = 0, workspace_bytes: int = 0,
+                      stream: int = 0) -> int:
+    o = _opts(opts)
+    return lib().sm_softmax_fwd_ex(in_ptr, out_ptr, M, N, in_stride, out_stride, dtype,
+                                   ctypes.byref(o) if o is not None else None,
+                                   workspace or None, workspace_bytes, stream)
+
+
+def sm_softmax_plan_query(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: int,
+                          out_stride: int, dtype: int, opts=None, num_cus: int = 0):
+    """(status, SmPlanInfo)."""
+    o = _opts(opts)
+    info = SmPlanInfo()
+    rc = lib().sm_softmax_plan_query(in_ptr, out_ptr, M, N, in_stride, out_stride, dtype,
+                                     ctypes.byref(o) if o is not None else None, num_cus,
+                                     ctypes.byref(info))
+    return rc, info
+
+
+def sm_softmax_strerror(status: int) -> str:
+    return lib().sm_softmax_strerror(status).decode()
+
+
+def sm_softmax_version() -> int:
+    return lib().sm_softmax_version()
+
+
+def sm_softmax_last_hip_error() -> int:
+    return lib().sm_softmax_last_hip_error()
+
+
+def sm_bench_copy(src: int, dst: int, nbytes: int, grid: int = 0, stream: int = 0) -> int:
+    return lib().sm_bench_copy(src, dst, nbytes, grid, stream)
+
+
+def sm_bench_flush(buf: int, nbytes: int, stream: int = 0) -> int:
+    return lib().sm_bench_flush(buf, nbytes, stream)
+
+
+# ---------------------------------------------------------------- torch marshalling
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: SM_F32, torch.float16: SM_F16, torch.bfloat16: SM_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _rows_view(t):
+    """(M, N, row_stride) of a tensor softmaxed along its last dimension."""
+    if t.dim() == 0:
+        raise ValueError("expected at least one dimension")
+    if t.stride(-1) != 1 and t.size(-1) > 1:
+        raise ValueError("the last dimension must be contiguous")
+    N = t.size(-1)
+    if t.dim() == 1:
+        return 1, N, N
+    lead = t.shape[:-1]
+    M = 1
+    for s in lead:
+        M *= s
+    # leading dimensions must collapse to one row stride
+    stride = t.stride(-2)
+    exp = stride
+    for d in range(t.dim() - 2, -1, -1):
+        if t.size(d) != 1 and t.stride(d) != exp:
+            raise ValueError("leading dimensions do not collapse to one row stride")
+        exp *= t.size(d)
+    return M, N, (stride if M > 1 else N)
+
+
+def softmax(x, out=None, opts=None, workspace=None, stream=None):
+    """Row softmax of a CUDA(HIP) tensor along its last dimension, on the current
+    stream (or ``stream``). Returns ``out`` (allocated like ``x`` if None)."""
+    import torch
+    if not x.is_cuda:
+        raise ValueError("softmax expects a device tensor (the library has no CPU path)")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device:
+        raise ValueError("out must match x in shape, dtype and device")
+    M, N, si = _rows_view(x)
+    _, _, so = _rows_view(out)
+    s = (stream if stream is not None else torch.cuda.current_stream(x.device)).cuda_stream
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        rc = sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, si, so, _torch_dtype_code(x),
+                               opts, ws_ptr, ws_bytes, s)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_softmax_fwd_ex")
+    return out
+
+
+def plan_for(x, out=None, opts=None, num_cus: int = 0) -> dict:
+    """The plan ``softmax(x, out, opts)`` would launch, as a dict."""
+    out = x if out is None else out
+    M, N, si = _rows_view(x)
+    _, _, so = _rows_view(out)
+    rc, info = sm_softmax_plan_query(x.data_ptr(), out.data_ptr(), M, N, si, so,
+                                     _torch_dtype_code(x), opts, num_cus)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_softmax_plan_query")
+    return info.as_dict()

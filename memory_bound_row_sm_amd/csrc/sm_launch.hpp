@@ -1,0 +1,36 @@
+// sm_launch.hpp -- host-side view of the kernel instances (one table per dtype).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smx {
+
+using RowKernelFn = void (*)(const unsigned char*, unsigned char*, int64_t, int, int64_t, int64_t,
+                             int);
+using StatsKernelFn = void (*)(const unsigned char*, float2*, int64_t, int, int64_t, int, int64_t);
+using NormKernelFn = void (*)(const unsigned char*, unsigned char*, const float2*, int64_t, int,
+                              int64_t, int64_t, int, int64_t, int);
+
+// Row-kernel instance for (lanes per row G, vectors per lane V, prefetch), or
+// nullptr when that combination is not built. Defined per dtype in
+// sm_rows_{f32,f16,bf16}.hip.
+RowKernelFn row_kernel_f32(int G, int V, int PF);
+RowKernelFn row_kernel_f16(int G, int V, int PF);
+RowKernelFn row_kernel_bf16(int G, int V, int PF);
+StatsKernelFn wide_stats_kernel(int dtype);
+NormKernelFn wide_norm_kernel(int dtype);
+
+inline RowKernelFn row_kernel(int dtype, int G, int V, int PF) {
+    switch (dtype) {
+    case 0: return row_kernel_f32(G, V, PF);
+    case 1: return row_kernel_f16(G, V, PF);
+    case 2: return row_kernel_bf16(G, V, PF);
+    default: return nullptr;
+    }
+}
+
+// Threads per workgroup of the row kernel for G lanes per row.
+inline int row_block(int G) { return G >= 256 ? G : 256; }
+
+}  // namespace smx

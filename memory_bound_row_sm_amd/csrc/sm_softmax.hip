@@ -1,0 +1,470 @@
+// sm_softmax.hip -- host side of the gfx950 row-softmax library: argument
+// validation, plan selection, per-device occupancy cache, launches, and the C
+// ABI declared in include/sm_softmax.h and include/sm_bench.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+
+#include "sm_bench.h"
+#include "sm_kernels.hpp"
+#include "sm_launch.hpp"
+#include "sm_softmax.h"
+
+namespace smx {
+
+// ------------------------------------------------------------ measurement kernels
+// 16-byte copy (bandwidth ceiling, counter calibration) and a read-modify-write
+// sweep that evicts earlier data from L2 and MALL.
+__global__ void __launch_bounds__(256) k_copy16(const uint4* src, uint4* dst, int64_t n) {
+    const int64_t step = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) dst[i] = src[i];
+}
+
+__global__ void __launch_bounds__(256) k_touch16(uint4* buf, int64_t n) {
+    const int64_t step = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
+        uint4 v = buf[i];
+        v.x += 1u;
+        v.y += 1u;
+        v.z += 1u;
+        v.w += 1u;
+        buf[i] = v;
+    }
+}
+
+// ------------------------------------------------------------ wide kernels
+StatsKernelFn wide_stats_kernel(int dtype) {
+    switch (dtype) {
+    case kF32: return &k_wide_stats<kF32>;
+    case kF16: return &k_wide_stats<kF16>;
+    case kBF16: return &k_wide_stats<kBF16>;
+    default: return nullptr;
+    }
+}
+NormKernelFn wide_norm_kernel(int dtype) {
+    switch (dtype) {
+    case kF32: return &k_wide_norm<kF32>;
+    case kF16: return &k_wide_norm<kF16>;
+    case kBF16: return &k_wide_norm<kBF16>;
+    default: return nullptr;
+    }
+}
+
+namespace {
+
+constexpr int64_t kResidentMaxCols = 8192;  // widest row the one-pass plans take by default
+constexpr int kChunk = 1024;                // elements per online-recurrence chunk (wide path)
+constexpr int64_t kMaxThreadsPerLaunch = 0xFFFFFFFFLL;
+
+thread_local int t_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    t_last_hip_error = (int)e;
+    return SM_ERR_HIP;
+}
+
+int elem_bytes(int dtype) { return dtype == SM_F32 ? 4 : 2; }
+
+// ------------------------------------------------------------ validation
+struct Problem {
+    uintptr_t in, out;
+    int64_t M, N, in_stride, out_stride;
+    int dtype;
+};
+
+// Byte span covered by rows 0..M-1 (M >= 1, N >= 1), or -1 on overflow.
+int64_t span_bytes(int64_t M, int64_t N, int64_t stride, int es) {
+    if (M == 1) return N * es;
+    const int64_t lim = INT64_MAX / es - N;
+    if (lim < 0 || (M - 1) > lim / stride) return -1;
+    return ((M - 1) * stride + N) * es;
+}
+
+int validate(const Problem& p) {
+    if (p.dtype != SM_F32 && p.dtype != SM_F16 && p.dtype != SM_BF16) return SM_ERR_DTYPE;
+    if (p.M < 0 || p.N < 0) return SM_ERR_INVALID;
+    if (p.M == 0 || p.N == 0) return SM_OK;
+    if (p.N > INT32_MAX) return SM_ERR_INVALID;
+    if (!p.in || !p.out) return SM_ERR_INVALID;
+    const int es = elem_bytes(p.dtype);
+    if ((p.in % es) || (p.out % es)) return SM_ERR_INVALID;
+    if (p.M > 1 && (p.in_stride < p.N || p.out_stride < p.N)) return SM_ERR_INVALID;
+    const int64_t si = span_bytes(p.M, p.N, p.in_stride, es);
+    const int64_t so = span_bytes(p.M, p.N, p.out_stride, es);
+    if (si < 0 || so < 0) return SM_ERR_INVALID;
+    if (p.in > UINTPTR_MAX - (uint64_t)si || p.out > UINTPTR_MAX - (uint64_t)so) return SM_ERR_INVALID;
+
+    // Overlap: disjoint byte ranges are fine; so is exactly in place.
+    const bool disjoint = p.in + (uint64_t)si <= p.out || p.out + (uint64_t)so <= p.in;
+    if (disjoint) return SM_OK;
+    if (p.in == p.out && (p.M == 1 || p.in_stride == p.out_stride)) return SM_OK;
+    if (p.M > 1 && p.in_stride == p.out_stride) {
+        // Interleaved rows with a common stride S: row i of out meets row j of
+        // in iff |D - k*S| < N (elements) for k = i - j, |k| <= M - 1.
+        const int64_t S = p.in_stride;
+        const int64_t D = ((int64_t)p.out - (int64_t)p.in) / es;
+        int64_t k0 = D / S;
+        if (D % S != 0 && D < 0) --k0;  // floor
+        for (int64_t k = k0; k <= k0 + 1; ++k) {
+            if (k < -(p.M - 1) || k > p.M - 1) continue;
+            const int64_t gap = D - k * S;
+            if (gap > -p.N && gap < p.N) return SM_ERR_OVERLAP;
+        }
+        return SM_OK;
+    }
+    return SM_ERR_OVERLAP;
+}
+
+// ------------------------------------------------------------ plan selection
+struct RowShape {
+    int G, V;
+};
+// Preferred (lanes per row, vectors per lane) by windows needed, narrowest first.
+constexpr RowShape kShapes[] = {{16, 1},  {32, 1},  {64, 1},  {64, 2},   {64, 4},
+                                {64, 8},  {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+
+bool built_shape(int G, int V, int PF) {
+    const bool g_ok = G == 16 || G == 32 || G == 64 || G == 128 || G == 256 || G == 512 || G == 1024;
+    const bool v_ok = V == 1 || V == 2 || V == 4 || V == 8;
+    return g_ok && v_ok && (!PF || G <= 256);
+}
+
+struct DeviceView {
+    int cus;
+    // workgroups per CU for a row-kernel instance / for the wide kernels
+    int (*occ_row)(void* ctx, int dtype, int G, int V, int PF);
+    int (*occ_wide)(void* ctx, int dtype);
+    void* ctx;
+};
+
+int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev, sm_plan_info* pi) {
+    *pi = sm_plan_info{};
+    const int es = elem_bytes(p.dtype);
+    const int E = 16 / es;
+    const bool in_aligned = (p.in % 16 == 0) && (p.M == 1 || (p.in_stride * es) % 16 == 0);
+    const int max_head = in_aligned ? 0 : E - 1;
+    const int64_t nw_max = (max_head + p.N + E - 1) / E;
+    pi->same_phase = ((p.in - p.out) % 16 == 0) &&
+                     (p.M == 1 || (((p.in_stride - p.out_stride) * es) % 16 == 0));
+
+    int plan = o.plan;
+    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_WIDE) return SM_ERR_PLAN;
+    if (plan == SM_PLAN_AUTO) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_PERSISTENT : SM_PLAN_WIDE;
+
+    if (plan == SM_PLAN_WIDE) {
+        const int WPC = kChunk / E;
+        const int64_t nchunks = (nw_max + WPC - 1) / WPC;
+        int64_t cpw = o.chunks_per_wave;
+        if (cpw <= 0) {
+            const int64_t target = (int64_t)dev.cus * 32;  // one full wave slot set
+            cpw = std::max<int64_t>(1, (p.M * nchunks + target - 1) / target);
+        }
+        cpw = std::min<int64_t>(cpw, nchunks);
+        if (cpw > INT32_MAX) return SM_ERR_PLAN;
+        const int64_t wpr = (nchunks + cpw - 1) / cpw;
+        if (p.M > INT64_MAX / wpr) return SM_ERR_PLAN;
+        const int64_t waves = p.M * wpr;
+        const int64_t grid = (waves + 3) / 4;
+        if (grid * 256 > kMaxThreadsPerLaunch) return SM_ERR_PLAN;
+        pi->plan = SM_PLAN_WIDE;
+        pi->block = 256;
+        pi->grid = grid;
+        pi->chunks_per_wave = (int)cpw;
+        pi->waves_per_row = wpr;
+        pi->launches = 2;
+        pi->workspace_bytes = ((waves * 8 + 255) / 256) * 256;
+        pi->model_bytes = 3 * p.M * p.N * es;
+        return SM_OK;
+    }
+
+    // One-pass plans: pick a row shape that holds the whole row.
+    int G = o.lanes_per_row, V = o.vecs_per_lane;
+    if (G == 0 || V == 0) {
+        bool found = false;
+        for (const RowShape& s : kShapes) {
+            if ((G && s.G != G) || (V && s.V != V)) continue;
+            if ((int64_t)s.G * s.V >= nw_max) {
+                G = s.G;
+                V = s.V;
+                found = true;
+                break;
+            }
+        }
+        if (!found) {
+            if (G && !V) {  // fixed G: smallest V that fits
+                for (int v : {1, 2, 4, 8})
+                    if ((int64_t)G * v >= nw_max) { V = v; found = true; break; }
+            } else if (V && !G) {
+                for (int g : {16, 32, 64, 128, 256, 512, 1024})
+                    if ((int64_t)g * V >= nw_max) { G = g; found = true; break; }
+            }
+        }
+        if (!found) return SM_ERR_PLAN;
+    }
+    if (!built_shape(G, V, 0) || (int64_t)G * V < nw_max) return SM_ERR_PLAN;
+    int PF;
+    if (plan == SM_PLAN_PERSISTENT) {
+        PF = (o.prefetch < 0) ? 1 : (o.prefetch ? 1 : 0);
+        if (PF && !built_shape(G, V, 1)) PF = 0;
+    } else {
+        PF = 0;
+    }
+    const int block = row_block(G);
+    const int gpb = block / G;
+    const int64_t groups = (p.M + gpb - 1) / gpb;
+    const int64_t cap = kMaxThreadsPerLaunch / block;
+    int64_t grid;
+    if (o.grid > 0) {
+        grid = o.grid;
+    } else if (plan == SM_PLAN_PERSISTENT) {
+        const int occ = std::max(1, dev.occ_row(dev.ctx, p.dtype, G, V, PF));
+        grid = (int64_t)occ * dev.cus;
+    } else {
+        grid = groups;
+    }
+    grid = std::max<int64_t>(1, std::min<int64_t>(std::min(grid, groups), cap));
+    pi->plan = plan;
+    pi->lanes_per_row = G;
+    pi->vecs_per_lane = V;
+    pi->prefetch = PF;
+    pi->block = block;
+    pi->grid = grid;
+    pi->launches = 1;
+    pi->model_bytes = 2 * p.M * p.N * es;
+    return SM_OK;
+}
+
+// ------------------------------------------------------------ device cache
+struct DevCache {
+    int cus = 0;
+    std::map<const void*, int> occ;
+};
+std::mutex g_mu;
+std::map<int, DevCache> g_dev;
+
+int occ_of(const void* fn, int block) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DevCache& d = g_dev[dev];
+    auto it = d.occ.find(fn);
+    if (it != d.occ.end()) return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block, 0) != hipSuccess || n < 1) n = 1;
+    d.occ[fn] = n;
+    return n;
+}
+
+int occ_row_live(void*, int dtype, int G, int V, int PF) {
+    RowKernelFn fn = row_kernel(dtype, G, V, PF);
+    return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
+}
+int occ_wide_live(void*, int dtype) {
+    return occ_of(reinterpret_cast<const void*>(wide_stats_kernel(dtype)), 256);
+}
+int occ_row_host(void*, int, int G, int, int) { return std::max(1, 2048 / row_block(G)); }
+int occ_wide_host(void*, int) { return 8; }
+
+int live_device(DeviceView* v) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        t_last_hip_error = (int)e;
+        return SM_ERR_NO_DEVICE;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        DevCache& d = g_dev[dev];
+        if (d.cus == 0) {
+            int cus = 0;
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess || cus <= 0) {
+                t_last_hip_error = (int)e;
+                return SM_ERR_NO_DEVICE;
+            }
+            d.cus = cus;
+        }
+        v->cus = d.cus;
+    }
+    v->occ_row = occ_row_live;
+    v->occ_wide = occ_wide_live;
+    v->ctx = nullptr;
+    return SM_OK;
+}
+
+sm_softmax_opts opts_or_default(const sm_softmax_opts* o) {
+    sm_softmax_opts d{};
+    d.prefetch = -1;
+    return o ? *o : d;
+}
+
+// ------------------------------------------------------------ launches
+int launch(const Problem& p, const sm_plan_info& pi, void* ws, hipStream_t stream) {
+    const int es = elem_bytes(p.dtype);
+    const auto* in = reinterpret_cast<const unsigned char*>(p.in);
+    auto* out = reinterpret_cast<unsigned char*>(p.out);
+    const int64_t isb = p.in_stride * es, osb = p.out_stride * es;
+    const int N = (int)p.N;
+    if (pi.plan == SM_PLAN_WIDE) {
+        auto* st = reinterpret_cast<float2*>(ws);
+        hipLaunchKernelGGL(wide_stats_kernel(p.dtype), dim3((unsigned)pi.grid), dim3(256), 0, stream,
+                           in, st, p.M, N, isb, pi.chunks_per_wave, pi.waves_per_row);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+        hipLaunchKernelGGL(wide_norm_kernel(p.dtype), dim3((unsigned)pi.grid), dim3(256), 0, stream,
+                           in, out, (const float2*)st, p.M, N, isb, osb, pi.chunks_per_wave,
+                           pi.waves_per_row, pi.same_phase);
+        e = hipGetLastError();
+        return e == hipSuccess ? SM_OK : hip_fail(e);
+    }
+    RowKernelFn fn = row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.prefetch);
+    if (!fn) return SM_ERR_PLAN;
+    hipLaunchKernelGGL(fn, dim3((unsigned)pi.grid), dim3(pi.block), 0, stream, in, out, p.M, N, isb,
+                       osb, pi.same_phase);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+void keep_pool_memory(int dev) {
+    static std::mutex mu;
+    static std::map<int, bool> done;
+    std::lock_guard<std::mutex> lk(mu);
+    if (done[dev]) return;
+    done[dev] = true;
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t thr = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+}
+
+int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes,
+        hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != SM_OK || p.M == 0 || p.N == 0) return rc;
+    DeviceView dv;
+    rc = live_device(&dv);
+    if (rc != SM_OK) return rc;
+    sm_plan_info pi;
+    rc = make_plan(p, opts_or_default(opts), dv, &pi);
+    if (rc != SM_OK) return rc;
+    if (pi.plan != SM_PLAN_WIDE) return launch(p, pi, nullptr, stream);
+
+    if (ws) {
+        if (ws_bytes < (size_t)pi.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
+            return SM_ERR_WORKSPACE;
+        return launch(p, pi, ws, stream);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    keep_pool_memory(dev);
+    void* tmp = nullptr;
+    e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = launch(p, pi, tmp, stream);
+    e = hipFreeAsync(tmp, stream);
+    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
+    return rc;
+}
+
+}  // namespace
+}  // namespace smx
+
+using namespace smx;
+
+extern "C" {
+
+int sm_softmax_fwd(const void* in, void* out, int64_t M, int64_t N, int64_t in_stride,
+                   int64_t out_stride, int dtype, hipStream_t stream) {
+    const Problem p{reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out), M, N,
+                    in_stride, out_stride, dtype};
+    return run(p, nullptr, nullptr, 0, stream);
+}
+
+int sm_softmax_fwd_ex(const void* in, void* out, int64_t M, int64_t N, int64_t in_stride,
+                      int64_t out_stride, int dtype, const sm_softmax_opts* opts, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    const Problem p{reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out), M, N,
+                    in_stride, out_stride, dtype};
+    return run(p, opts, workspace, workspace_bytes, stream);
+}
+
+int sm_softmax_plan_query(const void* in, const void* out, int64_t M, int64_t N, int64_t in_stride,
+                          int64_t out_stride, int dtype, const sm_softmax_opts* opts, int num_cus,
+                          sm_plan_info* info) {
+    if (!info) return SM_ERR_INVALID;
+    const Problem p{reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out), M, N,
+                    in_stride, out_stride, dtype};
+    int rc = validate(p);
+    if (rc != SM_OK) return rc;
+    if (M == 0 || N == 0) {
+        *info = sm_plan_info{};
+        return SM_OK;
+    }
+    DeviceView dv;
+    if (num_cus > 0) {
+        dv.cus = num_cus;
+        dv.occ_row = occ_row_host;
+        dv.occ_wide = occ_wide_host;
+        dv.ctx = nullptr;
+    } else {
+        rc = live_device(&dv);
+        if (rc != SM_OK) return rc;
+    }
+    return make_plan(p, opts_or_default(opts), dv, info);
+}
+
+const char* sm_softmax_strerror(int status) {
+    switch (status) {
+    case SM_OK: return "success";
+    case SM_ERR_INVALID: return "invalid argument (size, stride, pointer or alignment)";
+    case SM_ERR_DTYPE: return "unknown dtype";
+    case SM_ERR_OVERLAP: return "output overlaps input other than exactly in place";
+    case SM_ERR_HIP: return "HIP runtime error";
+    case SM_ERR_NO_DEVICE: return "no usable HIP device";
+    case SM_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
+    case SM_ERR_PLAN: return "plan or row shape cannot cover this problem";
+    default: return "unknown status";
+    }
+}
+
+int sm_softmax_version(void) { return SM_SOFTMAX_VERSION; }
+
+int sm_softmax_last_hip_error(void) { return t_last_hip_error; }
+
+int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream) {
+    if (!src || !dst || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) ||
+        (reinterpret_cast<uintptr_t>(dst) & 15))
+        return SM_ERR_INVALID;
+    if (bytes == 0) return SM_OK;
+    if (grid <= 0) {
+        DeviceView dv;
+        int rc = live_device(&dv);
+        if (rc != SM_OK) return rc;
+        grid = 8 * dv.cus;
+    }
+    hipLaunchKernelGGL(k_copy16, dim3(grid), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst),
+                       (int64_t)(bytes / 16));
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+int sm_bench_flush(void* buf, size_t bytes, hipStream_t stream) {
+    if (!buf || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15)) return SM_ERR_INVALID;
+    if (bytes == 0) return SM_OK;
+    DeviceView dv;
+    int rc = live_device(&dv);
+    if (rc != SM_OK) return rc;
+    hipLaunchKernelGGL(k_touch16, dim3(8 * dv.cus), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(buf), (int64_t)(bytes / 16));
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -30,3 +30,18 @@ def oracle_mod():
     import oracle
     oracle._load()
     return oracle
+
+
+def _ensure_built():
+    """Tests load what is built; they build only when nothing is."""
+    import memory_bound_row_sm_amd as sm
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        from oracle import build as ob
+        ob.build()
+    if not os.path.exists(sm.lib_path):
+        from memory_bound_row_sm_amd import build as sb
+        sb.build()
+
+
+_ensure_built()

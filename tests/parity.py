@@ -1,0 +1,78 @@
+"""Comparison of GPU outputs with the FP64 oracle (helper for the GPU tests).
+
+Rule (Warpline README, its correctness-check paragraph): an output g passes
+when |g - r| <= atol + rtol * |r|, with r the oracle's FP64 result rounded once
+to the storage dtype. Tolerances:
+
+* FP16 and BF16: atol = rtol = 4e-3 (the BF16 softmax tolerance that README
+  lists, applied to FP16 as well);
+* FP32: rtol = 1e-6 against the FP64 result itself (not its rounding), with
+  atol = 2^-126 (the smallest normal FP32) so that results that underflow
+  compare absolutely.
+
+Positions where the oracle gives NaN must be NaN on the GPU and vice versa.
+The helper also reports the maximum absolute error against the FP64 result and
+a relative error taken only where |y| > 1e-3 (the README's thresholded
+relative error).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+TOL = {"f32": (2.0 ** -126, 1e-6), "f16": (4e-3, 4e-3), "bf16": (4e-3, 4e-3)}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().double().numpy()
+
+
+def compare(g: torch.Tensor, x: torch.Tensor, rows=None, what: str = "") -> dict:
+    """Check GPU result ``g`` (rows x N, any device) against the oracle for the CPU
+    input ``x`` (M x N; ``rows`` selects the rows ``g`` holds). Raises AssertionError."""
+    dt = workloads.dtype_name(x)
+    y, yr = oracle.reference(workloads.storage_numpy(x), dt, rows=rows)
+    gd = to_f64(g)
+    atol, rtol = TOL[dt]
+    if dt == "f32":
+        ref = y
+    else:
+        ref = oracle.decode(yr, dt)
+    nan_ref = np.isnan(ref)
+    nan_g = np.isnan(gd)
+    assert np.array_equal(nan_ref, nan_g), f"{what}: NaN pattern differs ({nan_ref.sum()} vs {nan_g.sum()})"
+    ok = ~nan_ref
+    err = np.abs(gd[ok] - ref[ok])
+    bound = atol + rtol * np.abs(ref[ok])
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(ok)[np.argmax(err - bound)]
+        i, j = int(idx[0]), int(idx[1])
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst at ({i},{j}): "
+            f"gpu={gd[i, j]!r} ref={ref[i, j]!r} y={y[i, j]!r}")
+    fin = ok & np.isfinite(y)
+    abs_err = np.abs(gd[fin] - y[fin])
+    big = np.abs(y[fin]) > 1e-3
+    rel = abs_err[big] / np.abs(y[fin][big]) if big.any() else np.zeros(1)
+    margin = float(np.max(err / bound)) if err.size else 0.0
+    return {"max_abs": float(abs_err.max()) if abs_err.size else 0.0,
+            "max_rel_thr": float(rel.max()), "worst_frac_of_tol": margin, "n": int(err.size)}
+
+
+def row_sum_bound(dt: str) -> float:
+    """|sum_j g_j - 1| bound per row: half a unit in the last place of the output
+    dtype for every rounding, plus 1e-5 slack (FP32: 2e-5, the row-normalisation
+    tolerance of "Measured optimization case studies", section "CUDA: parallel
+    reduction, online statistics and a numerical fix")."""
+    return {"bf16": 2.0 ** -8 + 1e-5, "f16": 2.0 ** -11 + 1e-5, "f32": 2e-5}[dt]

@@ -1,0 +1,155 @@
+"""The C ABI on the host: exported symbols, argument validation (which runs before
+any HIP call, so it is testable without a GPU), and the plan rule evaluated for a
+256-CU device without touching one."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import memory_bound_row_sm_amd as sm
+from conftest import gpu_available
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+F32, F16, BF16 = sm.SM_F32, sm.SM_F16, sm.SM_BF16
+OK, INVALID, DTYPE, OVERLAP, NO_DEVICE, PLAN = 0, -1, -2, -3, -5, -7
+BASE = 1 << 32  # a fake, 256-byte aligned device address: never dereferenced on these paths
+
+
+def declared_functions():
+    names = []
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sm_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(sm.EXPORTED_SYMBOLS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", sm.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\S+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing
+    lib = sm.lib()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_strerror():
+    assert sm.sm_softmax_version() == 10000
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert sm.sm_softmax_strerror(code) and sm.sm_softmax_strerror(code) != "unknown status"
+    assert sm.sm_softmax_strerror(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,want", [
+    ((BASE, BASE * 2, 4, 8, 8, 8, 7), DTYPE),           # unknown dtype
+    ((BASE, BASE * 2, -1, 8, 8, 8, F32), INVALID),      # negative M
+    ((BASE, BASE * 2, 4, -8, 8, 8, F32), INVALID),      # negative N
+    ((0, BASE * 2, 4, 8, 8, 8, F32), INVALID),          # null input
+    ((BASE, 0, 4, 8, 8, 8, F32), INVALID),              # null output
+    ((BASE, BASE * 2, 4, 8, 7, 8, F32), INVALID),       # input stride < N
+    ((BASE, BASE * 2, 4, 8, 8, 7, F32), INVALID),       # output stride < N
+    ((BASE + 2, BASE * 2, 4, 8, 8, 8, F32), INVALID),   # input not element aligned
+    ((BASE, BASE * 2 + 1, 4, 8, 8, 8, BF16), INVALID),  # output not element aligned
+    ((BASE, BASE * 2, 4, 1 << 31, 1 << 31, 1 << 31, F16), INVALID),  # N > 2^31 - 1
+    ((BASE, BASE * 2, 1 << 62, 8, 1 << 40, 8, F32), INVALID),        # byte span overflows
+    ((BASE, BASE + 16, 4, 8, 8, 8, F32), OVERLAP),      # shifted by 4 elements
+    ((BASE, BASE, 4, 8, 8, 16, F32), OVERLAP),          # same base, different strides
+    ((BASE, BASE, 0, 8, 8, 8, F32), OK),                # M == 0: nothing to do
+    ((0, 0, 4, 0, 0, 0, F32), OK),                      # N == 0: nothing to do, pointers unused
+])
+def test_argument_validation(args, want):
+    got = sm.sm_softmax_fwd(*args, 0)
+    assert got == want, (args, got, sm.sm_softmax_strerror(got))
+    # the extended entry point validates the same way
+    assert sm.sm_softmax_fwd_ex(*args, None, 0, 0, 0) == want
+
+
+def test_interleaved_rows_overlap_rule():
+    # common stride 16 (elements, f32): out shifted by D elements
+    for D, want in [(8, OK), (4, OVERLAP), (-8, OK), (-9, OVERLAP), (16, OVERLAP), (24, OK)]:
+        rc = sm.sm_softmax_fwd(BASE, BASE + 4 * D if D >= 0 else BASE, 4, 8, 16, 16, F32, 0) \
+            if D >= 0 else sm.sm_softmax_fwd(BASE - 4 * D, BASE, 4, 8, 16, 16, F32, 0)
+        if rc == NO_DEVICE:
+            rc = OK  # validation passed; no device on this host
+        assert rc == want, (D, rc)
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
+def test_valid_call_without_device_reports_no_device():
+    rc = sm.sm_softmax_fwd(BASE, BASE * 2, 4, 8, 8, 8, F32, 0)
+    assert rc == NO_DEVICE
+
+
+def plan(M, N, dtype, opts=None, in_ptr=BASE, out_ptr=BASE * 2, si=None, so=None):
+    rc, info = sm.sm_softmax_plan_query(in_ptr, out_ptr, M, N, si or N, so or N, dtype, opts, 256)
+    return rc, info.as_dict()
+
+
+def test_plan_rule_one_pass_shapes():
+    cases = {  # (M, N, dtype) -> (lanes per row, vectors per lane)
+        (8192, 127, F16): (16, 1),     # 16 windows of 8 (misaligned rows: 17 needed -> 32)
+        (8192, 256, F16): (32, 1),
+        (8192, 1000, F16): (64, 2),
+        (4096, 4096, BF16): (64, 8),
+        (8192, 8192, F16): (256, 4),
+        (128, 781, F32): (64, 4),
+        (16, 8192, F32): (512, 4),
+    }
+    for (M, N, dt), (G, V) in cases.items():
+        rc, p = plan(M, N, dt)
+        assert rc == OK
+        want_g = 32 if (N, dt) == (127, F16) else G  # rows of 254 bytes are not 16-byte aligned
+        assert (p["lanes_per_row"], p["vecs_per_lane"]) == (want_g, V), (M, N, dt, p)
+        assert p["plan_name"] in ("resident", "persistent")
+        assert p["model_bytes"] == 2 * M * N * (4 if dt == F32 else 2)
+        assert p["lanes_per_row"] * p["vecs_per_lane"] * 16 >= N * (4 if dt == F32 else 2)
+
+
+def test_plan_rule_wide():
+    rc, p = plan(64, 131072, BF16)
+    assert rc == OK and p["plan_name"] == "wide"
+    assert p["chunks_per_wave"] == 1 and p["waves_per_row"] == 128
+    assert p["workspace_bytes"] == 64 * 128 * 8
+    assert p["model_bytes"] == 3 * 64 * 131072 * 2
+    assert p["launches"] == 2 and p["grid"] == 64 * 128 // 4
+    rc, p = plan(1024, 16384, BF16)  # 16384 chunks over 8192 wave slots -> 2 per wave
+    assert p["chunks_per_wave"] == 2 and p["waves_per_row"] == 8
+    rc, p = plan(4, 8193, F32)  # just past the resident limit
+    assert p["plan_name"] == "wide" and p["waves_per_row"] == 9
+
+
+def test_plan_forcing_and_limits():
+    rc, p = plan(100, 5000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
+    assert rc == OK and p["plan_name"] == "resident" and p["grid"] == 100
+    rc, p = plan(100, 5000, BF16, {"plan": sm.SM_PLAN_WIDE})
+    assert rc == OK and p["plan_name"] == "wide"
+    rc, p = plan(100, 5000, BF16, {"plan": sm.SM_PLAN_PERSISTENT, "lanes_per_row": 64,
+                                   "vecs_per_lane": 1})
+    assert rc == PLAN  # 64 windows hold 512 elements, not 5000
+    rc, p = plan(100, 40000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
+    assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (1024, 8)
+    rc, p = plan(100, 70000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
+    assert rc == PLAN
+    rc, p = plan(100, 500, BF16, {"plan": 9})
+    assert rc == PLAN
+    rc, p = plan(10 ** 6, 100, F16, {"plan": sm.SM_PLAN_PERSISTENT})
+    assert p["grid"] == 256 * 8  # occupancy assumed 8 workgroups per CU on the host path
+
+
+def test_plan_phase_flag():
+    rc, p = plan(4, 64, F16)
+    assert p["same_phase"] == 1
+    rc, p = plan(4, 64, F16, out_ptr=BASE * 2 + 2)
+    assert p["same_phase"] == 0
+    rc, p = plan(4, 60, F16, si=64, so=60)
+    assert p["same_phase"] == 0
+    rc, p = plan(4, 60, F16, si=64, so=72)
+    assert p["same_phase"] == 1

@@ -27,6 +27,7 @@ writes those lines to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -83,24 +84,56 @@ def load_traffic(workload: str, launch_bytes: int):
     return t.get("hbm_bytes_per_launch")
 
 
-class Timer:
-    """Per-call HIP event pairs on the launch stream (torch's current stream)."""
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
 
-    def time(self, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        fn()
-        ev1.record()
-        self.pairs.append((ev0, ev1))
+class DispatchEvents:
+    """HIP event pairs that the library attaches to its kernel dispatches
+    (hipExtLaunchKernel), so each pair spans exactly the call's kernels on the
+    launch stream: no host launch latency, no queue gaps. The events are created
+    without the system-scope fence that a default event performs when it is
+    recorded (that fence, not the kernel, cost about 3 us per cold call). Created
+    through the HIP runtime that torch already loaded (the library binds to the
+    same one)."""
 
-    def samples_ms(self):
-        self.torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in self.pairs]
+    def __init__(self, n: int, flags=HIP_EVENT_DISABLE_SYSTEM_FENCE):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            rc = (self.hip.hipEventCreate(ctypes.byref(e)) if flags is None else
+                  self.hip.hipEventCreateWithFlags(ctypes.byref(e), flags))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events.append(e)
+        self.used = 0
+
+    def next_pair(self):
+        a, b = self.events[2 * self.used], self.events[2 * self.used + 1]
+        self.used += 1
+        return a, b
+
+    def samples_ms(self, torch):
+        torch.cuda.synchronize()
+        out = []
+        for i in range(self.used):
+            ms = ctypes.c_float()
+            rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * i],
+                                              self.events[2 * i + 1])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
 
 
 def main(argv=None) -> int:
@@ -110,10 +143,17 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true", help="also time every workload and plan (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm diagnostic lane (profiling runs: every softmax call is cold)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="summarise a rocprofv3 kernel trace of this bench (cold/warm per kernel) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing on the host")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(rows shard across GPUs with no communication; see the design notes).",
@@ -148,19 +188,24 @@ def main(argv=None) -> int:
     log(f"[bench] {WORKLOAD}: {M}x{N} bf16, sha256 {sha[:16]}, plan {info['plan_name']} "
         f"G={info['lanes_per_row']} V={info['vecs_per_lane']} grid={info['grid']}")
 
-    def call(xi=x, oi=out):
-        rc = sm.sm_softmax_fwd(xi.data_ptr(), oi.data_ptr(), xi.shape[0], xi.shape[1],
-                               xi.stride(0), oi.stride(0), sm.SM_BF16 if xi.dtype == torch.bfloat16
-                               else (sm.SM_F16 if xi.dtype == torch.float16 else sm.SM_F32),
-                               s_handle)
+    dt_code = {torch.float32: sm.SM_F32, torch.float16: sm.SM_F16, torch.bfloat16: sm.SM_BF16}[x.dtype]
+    opts = sm.SmOpts()  # all zero: the automatic plan, as sm_softmax_fwd
+
+    def call(events=None):
+        opts.start_event, opts.stop_event = events if events else (None, None)
+        rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, x.stride(0), out.stride(0),
+                                  dt_code, opts, 0, 0, s_handle)
         if rc != 0:
-            raise sm.SoftmaxError(rc, "sm_softmax_fwd")
+            raise sm.SoftmaxError(rc, "sm_softmax_fwd_ex")
 
     # ---------------------------------------------------------------- correctness gate
     # Properties every correct output has (finite, in [0, 1], rows summing to 1
     # within the BF16 rounding bound); the element-wise oracle comparison runs in
     # the CPU-baseline leg below, on the same input.
-    call()
+    rc = sm.sm_softmax_fwd(x.data_ptr(), out.data_ptr(), M, N, x.stride(0), out.stride(0),
+                           dt_code, s_handle)
+    if rc != 0:
+        raise sm.SoftmaxError(rc, "sm_softmax_fwd")
     torch.cuda.synchronize()
     sums = out.sum(dim=1, dtype=torch.float64)
     gate_ok = bool(torch.isfinite(out).all()) and bool(((out >= 0) & (out <= 1)).all()) and \
@@ -178,59 +223,66 @@ def main(argv=None) -> int:
             raise sm.SoftmaxError(rc, "sm_bench_flush")
 
     # ---------------------------------------------------------------- clocks up
+    # 200 ms of cache sweeps keep the GPU busy without calling the timed kernel, so
+    # a profiler's per-kernel average covers only the calls below
     t_end = time.perf_counter() + 0.2
     while time.perf_counter() < t_end:
         for _ in range(20):
-            call()
+            flush()
         torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- cold lane
     for _ in range(args.warmup):
         flush()
         call()
-    torch.cuda.synchronize()
-    timer = Timer(torch)
+    ev = DispatchEvents(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         flush()
-        timer.time(call)
+        call(ev.next_pair())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    cold = stats_us(timer.samples_ms())
+    cold = stats_us(ev.samples_ms(torch))
+    ev.close()
+    log(f"[bench] timed {args.steps} cold steps in {wall:.3f} s wall (flush sweeps included)")
 
     # ---------------------------------------------------------------- warm lane (diagnostic)
-    wt = Timer(torch)
-    for _ in range(args.steps):
-        wt.time(call)
-    warm = stats_us(wt.samples_ms())
+    warm = None
+    if not args.no_warm:
+        ev = DispatchEvents(args.steps)
+        for _ in range(args.steps):
+            call(ev.next_pair())
+        warm = stats_us(ev.samples_ms(torch))
+        ev.close()
 
     # ---------------------------------------------------------------- copy ceiling, same bytes, cold
     src = torch.empty(model_bytes // 2, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
 
-    def copy():
-        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), 0, s_handle)
+    def copy(events=(None, None)):
+        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), 0, s_handle, *events)
         if rc != 0:
             raise sm.SoftmaxError(rc, "sm_bench_copy")
 
     for _ in range(args.warmup):
         flush()
         copy()
-    ct = Timer(torch)
+    ev = DispatchEvents(args.steps)
     for _ in range(args.steps):
         flush()
-        ct.time(copy)
-    copy_cold = stats_us(ct.samples_ms())
+        copy(ev.next_pair())
+    copy_cold = stats_us(ev.samples_ms(torch))
+    ev.close()
     del src, dst
 
     gbps = model_bytes / (cold["mean_us"] * 1e-6) / 1e9
     gbps_median = model_bytes / (cold["median_us"] * 1e-6) / 1e9
     copy_gbps = model_bytes / (copy_cold["mean_us"] * 1e-6) / 1e9
     log(f"[bench] cold mean {cold['mean_us']:.2f} us median {cold['median_us']:.2f} us -> "
-        f"{gbps:.0f} GB/s ({100 * gbps / PEAK_GBPS:.1f}% of 8 TB/s); copy ceiling {copy_gbps:.0f} GB/s; "
-        f"warm median {warm['median_us']:.2f} us")
+        f"{gbps:.0f} GB/s ({100 * gbps / PEAK_GBPS:.1f}% of 8 TB/s); copy ceiling {copy_gbps:.0f} GB/s"
+        + (f"; warm median {warm['median_us']:.2f} us" if warm else ""))
 
     # ---------------------------------------------------------------- sweep (stderr)
     if args.sweep:
@@ -264,7 +316,8 @@ def main(argv=None) -> int:
         "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
         "value_median_GBps": round(gbps_median, 1),
         "cold_us": {k: round(v, 3) if isinstance(v, float) else v for k, v in cold.items()},
-        "warm_us": {k: round(v, 3) if isinstance(v, float) else v for k, v in warm.items()},
+        "warm_us": ({k: round(v, 3) if isinstance(v, float) else v for k, v in warm.items()}
+                    if warm else None),
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
         "timed_region_wall_s": round(wall, 4),
@@ -275,6 +328,29 @@ def main(argv=None) -> int:
     }
     print(json.dumps(result), flush=True)
     return 0 if parity.get("passed") is not False else 1
+
+
+def summarize_trace(path: str) -> str:
+    """Per kernel: dispatch count and mean/median/min duration of the dispatches that
+    follow a cache sweep (cold) and of the others (warm), from a rocprofv3
+    kernel-trace CSV."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    groups = {}
+    prev = ""
+    for r in rows:
+        name = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        lane = "cold" if "sweep" in prev else "warm"
+        key = (name.split("(")[0].replace("void ", ""), r["Grid_Size_X"], r["Workgroup_Size_X"], lane)
+        groups.setdefault(key, []).append(dur)
+        prev = name
+    lines = [f"{'kernel':48s} {'grid(items)':>11s} {'wg':>5s} {'lane':5s} {'calls':>6s} "
+             f"{'mean_us':>9s} {'median_us':>9s} {'min_us':>8s}"]
+    for (k, g, w, lane), v in sorted(groups.items()):
+        lines.append(f"{k[:48]:48s} {g:>11s} {w:>5s} {lane:5s} {len(v):6d} "
+                     f"{statistics.mean(v):9.3f} {statistics.median(v):9.3f} {min(v):8.3f}")
+    return "\n".join(lines)
 
 
 def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
@@ -328,11 +404,15 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
         for pname, p in plans.items():
             if p in (1, 2) and N > 8192:
                 continue
-            opts = {"plan": p, "prefetch": -1}
+            opts = {"plan": p}
             info = sm.plan_for(x, out, opts)
 
-            def call():
-                rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N, dt, opts, 0, 0,
+            o = sm.SmOpts()
+            o.plan = p
+
+            def call(events=(None, None)):
+                o.start_event, o.stop_event = events
+                rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N, dt, o, 0, 0,
                                           s_handle)
                 if rc != 0:
                     raise sm.SoftmaxError(rc)
@@ -340,11 +420,12 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
             for _ in range(5):
                 flush()
                 call()
-            t = Timer(torch)
+            t = DispatchEvents(steps)
             for _ in range(steps):
                 flush()
-                t.time(call)
-            st = stats_us(t.samples_ms())
+                call(t.next_pair())
+            st = stats_us(t.samples_ms(torch))
+            t.close()
             gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
             line = {"workload": name, "plan": pname, "resolved": info["plan_name"],
                     "G": info["lanes_per_row"], "V": info["vecs_per_lane"],

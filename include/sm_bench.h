@@ -28,18 +28,22 @@ extern "C" {
  *   bytes    : a multiple of 16
  *   grid     : workgroups of 256 threads (0 = 8 per CU); each thread moves
  *              16 bytes per step of a grid-stride loop
+ *   start_event, stop_event : optional (NULL) events attached to the kernel
+ *              dispatch, as in sm_softmax_opts
  * Returns SM_OK (0) or a negative sm_status (SM_ERR_INVALID for bad
  * alignment or size, SM_ERR_HIP for a failed launch).
  */
-int sm_bench_copy(const void *src, void *dst, size_t bytes, int grid, hipStream_t stream);
+int sm_bench_copy(const void *src, void *dst, size_t bytes, int grid, hipStream_t stream,
+                  hipEvent_t start_event, hipEvent_t stop_event);
 
 /*
- * Read and rewrite every 16-byte word of `buf` (adds one to each 32-bit
- * lane), so that afterwards the L2 caches and the MALL hold this buffer's
- * lines instead of any earlier data. Use a buffer of at least 1 GiB on MI355X
+ * Read every 16-byte word of `buf` and write nothing, so that afterwards the L2
+ * caches and the MALL hold this buffer's clean lines instead of any earlier
+ * data (dirty lines of earlier work are written back during the sweep, not
+ * during the next timed call). Use a buffer of at least 1 GiB on MI355X
  * (256 MiB MALL, 8 x 4 MiB L2). Same argument rules as sm_bench_copy.
  */
-int sm_bench_flush(void *buf, size_t bytes, hipStream_t stream);
+int sm_bench_flush(const void *buf, size_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

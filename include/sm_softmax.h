@@ -76,7 +76,10 @@ typedef enum sm_status {
  *                 optimization case studies", section "Wide rows: loop in one
  *                 program, or split across programs"; Warpline README, the
  *                 description of its online path).
- * AUTO picks RESIDENT/PERSISTENT for N <= 8192 and WIDE above. */
+ * AUTO takes WIDE for N > 8192. Otherwise it holds the row in the narrowest
+ * measured-best group (16 to 1024 lanes, 1 to 8 vectors per lane), and takes
+ * PERSISTENT when the row groups fit in at most two rounds of resident
+ * workgroups, RESIDENT when there are more. */
 typedef enum sm_plan {
     SM_PLAN_AUTO = 0,
     SM_PLAN_RESIDENT = 1,
@@ -91,7 +94,17 @@ typedef struct sm_softmax_opts {
     int vecs_per_lane;   /* RESIDENT/PERSISTENT: 16-byte vectors per lane, 1, 2, 4 or 8; 0 = auto */
     int grid;            /* workgroups to launch; 0 = auto */
     int chunks_per_wave; /* WIDE: 1024-element chunks per wave; 0 = auto */
-    int prefetch;        /* PERSISTENT: 1 = load the next row early, 0 = no; -1 = auto */
+    int prefetch;        /* PERSISTENT: 1 = load the next row early, -1 = no; 0 = auto */
+    int nontemporal;     /* streaming cache hints on the row data: 1 = loads, 2 = loads and
+                            stores, -1 = none; 0 = auto (loads when the call moves at least
+                            256 MiB, the size of the MI355X MALL) */
+    /* Optional timing events (created by the caller with hipEventCreate), or NULL.
+     * They are attached to the kernel dispatches themselves (hipExtLaunchKernel):
+     * start_event takes the start time of the call's first kernel and stop_event
+     * the end time of its last, so their elapsed time is the device time of the
+     * call without host-side launch latency. */
+    hipEvent_t start_event;
+    hipEvent_t stop_event;
 } sm_softmax_opts;
 
 /* What a call would launch (filled by sm_softmax_plan_query). */
@@ -100,6 +113,7 @@ typedef struct sm_plan_info {
     int lanes_per_row;
     int vecs_per_lane;
     int prefetch;
+    int io_flags;          /* 1 = nontemporal loads, 2 = nontemporal stores */
     int block;             /* threads per workgroup */
     int64_t grid;          /* workgroups per launch */
     int chunks_per_wave;   /* WIDE only */

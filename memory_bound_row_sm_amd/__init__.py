@@ -40,13 +40,15 @@ lib_path = os.path.join(_HERE, "libsm_softmax.so")
 class SmOpts(ctypes.Structure):
     _fields_ = [("plan", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
                 ("vecs_per_lane", ctypes.c_int), ("grid", ctypes.c_int),
-                ("chunks_per_wave", ctypes.c_int), ("prefetch", ctypes.c_int)]
+                ("chunks_per_wave", ctypes.c_int), ("prefetch", ctypes.c_int),
+                ("nontemporal", ctypes.c_int),
+                ("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p)]
 
 
 class SmPlanInfo(ctypes.Structure):
     _fields_ = [("plan", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
                 ("vecs_per_lane", ctypes.c_int), ("prefetch", ctypes.c_int),
-                ("block", ctypes.c_int), ("grid", ctypes.c_int64),
+                ("io_flags", ctypes.c_int), ("block", ctypes.c_int), ("grid", ctypes.c_int64),
                 ("chunks_per_wave", ctypes.c_int), ("waves_per_row", ctypes.c_int64),
                 ("launches", ctypes.c_int), ("same_phase", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_int64), ("model_bytes", ctypes.c_int64)]
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.sm_softmax_strerror.restype = ctypes.c_char_p
         L.sm_softmax_version.argtypes = []
         L.sm_softmax_last_hip_error.argtypes = []
-        L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, vp]
+        L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, vp, vp, vp]
         L.sm_bench_flush.argtypes = [vp, ctypes.c_size_t, vp]
         for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
                   L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_bench_copy,
@@ -110,9 +112,9 @@ def _opts(opts) -> SmOpts | None:
         return None
     if isinstance(opts, SmOpts):
         return opts
-    o = SmOpts(0, 0, 0, 0, 0, -1)
+    o = SmOpts()  # all zero: automatic
     for k, v in dict(opts).items():
-        setattr(o, k, int(v))
+        setattr(o, k, v if k.endswith("_event") else int(v))
     return o
 
 
@@ -155,8 +157,9 @@ def sm_softmax_last_hip_error() -> int:
     return lib().sm_softmax_last_hip_error()
 
 
-def sm_bench_copy(src: int, dst: int, nbytes: int, grid: int = 0, stream: int = 0) -> int:
-    return lib().sm_bench_copy(src, dst, nbytes, grid, stream)
+def sm_bench_copy(src: int, dst: int, nbytes: int, grid: int = 0, stream: int = 0,
+                  start_event=None, stop_event=None) -> int:
+    return lib().sm_bench_copy(src, dst, nbytes, grid, stream, start_event, stop_event)
 
 
 def sm_bench_flush(buf: int, nbytes: int, stream: int = 0) -> int:

@@ -81,6 +81,28 @@ __device__ __forceinline__ uint4 encode(const float* f) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ------------------------------------------------------------ 16-byte global I/O
+// Row data moves in 16-byte vectors. `nt` selects the nontemporal (streaming)
+// cache hint, which the host turns on for inputs larger than the MALL.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+enum : int { kNtLoad = 1, kNtStore = 2 };  // io flag bits
+
+__device__ __forceinline__ uint4 load16(const unsigned char* p, bool nt) {
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t v = nt ? __builtin_nontemporal_load(q) : *q;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store16(unsigned char* p, const uint4 v, bool nt) {
+    u32x4_t* q = reinterpret_cast<u32x4_t*>(p);
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    if (nt)
+        __builtin_nontemporal_store(w, q);
+    else
+        *q = w;
+}
+
 // Store one element (already encoded) of an encoded vector: element k of `v`.
 template <int DT>
 __device__ __forceinline__ void store_elem(unsigned char* p, const uint4 v, int k) {
@@ -205,21 +227,22 @@ __device__ __forceinline__ CSum group_allreduce_csum(CSum c) {
 // ------------------------------------------------------------ online merge
 // Merge of two partial states (m, s), s = sum exp(x - m) over each part. A part
 // whose maximum is -inf (all of it masked) contributes nothing, and two such
-// parts give (-inf, 0) without evaluating exp(-inf - (-inf)) ("Measured
-// optimization case studies", section "Wide rows: loop in one program, or
-// split across programs": the merge guard).
+// parts keep the sum of their sums (0, or NaN if a NaN was seen) without
+// evaluating exp(-inf - (-inf)) ("Measured optimization case studies", section
+// "Wide rows: loop in one program, or split across programs": the merge guard).
 __device__ __forceinline__ void merge_fast(float& m, float& s, float m2, float s2) {
     const float mn = __builtin_fmaxf(m, m2);
     const float r = s * exp2_fast((m - mn) * kLog2e) + s2 * exp2_fast((m2 - mn) * kLog2e);
-    s = (mn == kNegInf) ? 0.f : r;
+    s = (mn == kNegInf) ? s + s2 : r;
     m = mn;
 }
 
 // FP32-accurate merge: rescale factors from exp_diff_acc, compensated sums.
 __device__ __forceinline__ void merge_acc(float& m, CSum& s, float m2, CSum s2) {
     const float mn = __builtin_fmaxf(m, m2);
-    if (mn == kNegInf) {
-        s.hi = s.lo = 0.f;
+    if (mn == kNegInf) {  // both parts fully masked: 0, or NaN if a NaN was seen
+        s.hi = s.hi + s2.hi;
+        s.lo = s.lo + s2.lo;
         m = mn;
         return;
     }

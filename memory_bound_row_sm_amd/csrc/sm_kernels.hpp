@@ -43,7 +43,7 @@ struct RowGeom {
 // as that element, so it can always be read).
 template <int DT, int G, int V>
 __device__ __forceinline__ void load_row(uint4 (&raw)[V], const unsigned char* in, int64_t row,
-                                         int64_t M, int N, int64_t in_sb, int lane) {
+                                         int64_t M, int N, int64_t in_sb, int lane, int io) {
     if (row >= M) return;
     const RowGeom<DT> g(in + row * in_sb, N);
     const uint32_t ni = Elem<DT>::neg_inf_word;
@@ -51,7 +51,7 @@ __device__ __forceinline__ void load_row(uint4 (&raw)[V], const unsigned char* i
     for (int v = 0; v < V; ++v) {
         const int w = lane + G * v;
         if (w < g.nwin)
-            raw[v] = *reinterpret_cast<const uint4*>(g.base + 16 * (size_t)w);
+            raw[v] = load16(g.base + 16 * (size_t)w, io & kNtLoad);
         else
             raw[v] = make_uint4(ni, ni, ni, ni);
     }
@@ -122,8 +122,8 @@ __device__ __forceinline__ float row_sum_acc(CSum c, float* lds_hi, float* lds_l
 template <int DT, int G, int V>
 __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigned char* in,
                                             unsigned char* out, int64_t row, int N, int64_t in_sb,
-                                            int64_t out_sb, int same_phase, int lane, float* lds_a,
-                                            float* lds_b, float* lds_c) {
+                                            int64_t out_sb, int same_phase, int io, int lane,
+                                            float* lds_a, float* lds_b, float* lds_c) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
     const RowGeom<DT> g(in + row * in_sb, N);
@@ -210,7 +210,7 @@ __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigne
             const uint4 enc = encode<DT>(y);
             const int c0 = w * E - g.head;
             if (same_phase && c0 >= 0 && c0 + E <= N) {
-                *reinterpret_cast<uint4*>(orow + (size_t)c0 * ES) = enc;
+                store16(orow + (size_t)c0 * ES, enc, io & kNtStore);
             } else {
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
@@ -222,16 +222,20 @@ __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigne
     }
 }
 
+// Workgroup shape: rows that fit in a wave share 256-thread workgroups (several
+// row groups per workgroup, no barriers); a row spread over several waves gets
+// a workgroup of exactly its G lanes, so its barriers are uniform.
 template <int G>
 struct RowLaunch {
-    static constexpr int block = G >= 256 ? G : 256;
+    static constexpr int block = G > 64 ? G : 256;
     static constexpr int groups = block / G;  // rows in flight per workgroup
+    static_assert(G <= 64 || groups == 1, "multi-wave rows own their workgroup");
 };
 
 template <int DT, int G, int V, bool PF>
 __global__ void __launch_bounds__(RowLaunch<G>::block)
 k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, int64_t in_sb,
-               int64_t out_sb, int same_phase) {
+               int64_t out_sb, int same_phase, int io) {
     constexpr int GPB = RowLaunch<G>::groups;
     constexpr int NW = G > 64 ? G / 64 : 1;
     __shared__ float lds_a[NW], lds_b[NW], lds_c[NW];
@@ -243,20 +247,20 @@ k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, in
     int64_t row = (int64_t)blockIdx.x * GPB + grp;
 
     uint4 cur[V];
-    load_row<DT, G, V>(cur, in, row, M, N, in_sb, lane);
+    load_row<DT, G, V>(cur, in, row, M, N, in_sb, lane, io);
     while (row < M) {
         const int64_t next = row + rstep;
         if constexpr (PF) {
             uint4 nxt[V];
-            load_row<DT, G, V>(nxt, in, next, M, N, in_sb, lane);
-            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, lane, lds_a,
+            load_row<DT, G, V>(nxt, in, next, M, N, in_sb, lane, io);
+            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, io, lane, lds_a,
                                   lds_b, lds_c);
 #pragma unroll
             for (int v = 0; v < V; ++v) cur[v] = nxt[v];
         } else {
-            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, lane, lds_a,
+            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, io, lane, lds_a,
                                   lds_b, lds_c);
-            load_row<DT, G, V>(cur, in, next, M, N, in_sb, lane);
+            load_row<DT, G, V>(cur, in, next, M, N, in_sb, lane, io);
         }
         row = next;
     }
@@ -275,14 +279,14 @@ struct Wide {
 
 template <int DT>
 __device__ __forceinline__ void load_chunk(uint4 (&raw)[Wide<DT>::VPL], const RowGeom<DT>& g,
-                                           int64_t c, int lane) {
+                                           int64_t c, int lane, int io) {
     constexpr int WPC = Wide<DT>::WPC;
     const uint32_t ni = Elem<DT>::neg_inf_word;
 #pragma unroll
     for (int v = 0; v < Wide<DT>::VPL; ++v) {
         const int64_t w = c * WPC + lane + 64 * v;
         if (w < g.nwin)
-            raw[v] = *reinterpret_cast<const uint4*>(g.base + 16 * (size_t)w);
+            raw[v] = load16(g.base + 16 * (size_t)w, io & kNtLoad);
         else
             raw[v] = make_uint4(ni, ni, ni, ni);
     }
@@ -316,7 +320,7 @@ __device__ __forceinline__ void decode_chunk(const uint4 (&raw)[Wide<DT>::VPL],
 template <int DT>
 __global__ void __launch_bounds__(256)
 k_wide_stats(const unsigned char* in, float2* stats, int64_t M, int N, int64_t in_sb, int cpw,
-             int64_t wpr) {
+             int64_t wpr, int io) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int VPL = Wide<DT>::VPL;
     constexpr int WPC = Wide<DT>::WPC;
@@ -335,7 +339,7 @@ k_wide_stats(const unsigned char* in, float2* stats, int64_t M, int N, int64_t i
     CSum cs;
     for (int64_t c = c_begin; c < c_end; ++c) {
         uint4 raw[VPL];
-        load_chunk<DT>(raw, g, c, lane);
+        load_chunk<DT>(raw, g, c, lane, io);
         float x[VPL][E];
         decode_chunk<DT>(raw, x, g, N, c, lane);
         float cm = m;
@@ -344,36 +348,37 @@ k_wide_stats(const unsigned char* in, float2* stats, int64_t M, int N, int64_t i
 #pragma unroll
             for (int k = 0; k + 1 < E; k += 2) cm = max3f(cm, x[v][k], x[v][k + 1]);
         }
-        if (cm != kNegInf) {  // lanes that have seen only -inf keep (-inf, 0)
-            if constexpr (DT == kF32) {
-                const float f = exp_diff_acc(m, cm);  // m = -inf -> 0
-                cs.hi *= f;
-                cs.lo *= f;
+        // A lane that has seen only -inf (or NaN) shifts by 0: its sum stays 0, or
+        // becomes NaN if a NaN went by, and exp(-inf - (-inf)) is never formed.
+        const float sh = (cm == kNegInf) ? 0.f : cm;
+        if constexpr (DT == kF32) {
+            const float f = exp_diff_acc(m, sh);  // m = -inf -> 0
+            cs.hi *= f;
+            cs.lo *= f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+                for (int k = 0; k < E; ++k) cs.add(exp_diff_acc(x[v][k], sh));
+            }
+        } else {
+            float acc = s * exp2_fast((m - sh) * kLog2e);
+            if (__builtin_fabsf(sh) <= 0x1p125f) {
+                const float mL = sh * kLog2e;
 #pragma unroll
                 for (int v = 0; v < VPL; ++v) {
 #pragma unroll
-                    for (int k = 0; k < E; ++k) cs.add(exp_diff_acc(x[v][k], cm));
+                    for (int k = 0; k < E; ++k) acc += exp2_fast(__builtin_fmaf(x[v][k], kLog2e, -mL));
                 }
             } else {
-                float acc = s * exp2_fast((m - cm) * kLog2e);
-                if (__builtin_fabsf(cm) <= 0x1p125f) {
-                    const float mL = cm * kLog2e;
 #pragma unroll
-                    for (int v = 0; v < VPL; ++v) {
+                for (int v = 0; v < VPL; ++v) {
 #pragma unroll
-                        for (int k = 0; k < E; ++k) acc += exp2_fast(__builtin_fmaf(x[v][k], kLog2e, -mL));
-                    }
-                } else {
-#pragma unroll
-                    for (int v = 0; v < VPL; ++v) {
-#pragma unroll
-                        for (int k = 0; k < E; ++k) acc += exp2_fast((x[v][k] - cm) * kLog2e);
-                    }
+                    for (int k = 0; k < E; ++k) acc += exp2_fast((x[v][k] - sh) * kLog2e);
                 }
-                s = acc;
             }
-            m = cm;
+            s = acc;
         }
+        m = cm;
     }
     if constexpr (DT == kF32) {
         group_merge_acc<64>(m, cs);
@@ -415,7 +420,7 @@ __device__ __forceinline__ void row_stats(const float2* st, int64_t wpr, int lan
 template <int DT>
 __global__ void __launch_bounds__(256)
 k_wide_norm(const unsigned char* in, unsigned char* out, const float2* stats, int64_t M, int N,
-            int64_t in_sb, int64_t out_sb, int cpw, int64_t wpr, int same_phase) {
+            int64_t in_sb, int64_t out_sb, int cpw, int64_t wpr, int same_phase, int io) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
     constexpr int VPL = Wide<DT>::VPL;
@@ -440,7 +445,7 @@ k_wide_norm(const unsigned char* in, unsigned char* out, const float2* stats, in
 
     for (int64_t c = c_begin; c < c_end; ++c) {
         uint4 raw[VPL];
-        load_chunk<DT>(raw, g, c, lane);
+        load_chunk<DT>(raw, g, c, lane, io);
         float x[VPL][E];
 #pragma unroll
         for (int v = 0; v < VPL; ++v) decode<DT>(raw[v], x[v]);
@@ -463,7 +468,7 @@ k_wide_norm(const unsigned char* in, unsigned char* out, const float2* stats, in
                 const uint4 enc = encode<DT>(y);
                 const int64_t c0 = w * E - g.head;
                 if (same_phase && c0 >= 0 && c0 + E <= N) {
-                    *reinterpret_cast<uint4*>(orow + (size_t)c0 * ES) = enc;
+                    store16(orow + (size_t)c0 * ES, enc, io & kNtStore);
                 } else {
 #pragma unroll
                     for (int k = 0; k < E; ++k) {

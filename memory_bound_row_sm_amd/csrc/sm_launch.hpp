@@ -7,10 +7,11 @@
 namespace smx {
 
 using RowKernelFn = void (*)(const unsigned char*, unsigned char*, int64_t, int, int64_t, int64_t,
-                             int);
-using StatsKernelFn = void (*)(const unsigned char*, float2*, int64_t, int, int64_t, int, int64_t);
+                             int, int);
+using StatsKernelFn = void (*)(const unsigned char*, float2*, int64_t, int, int64_t, int, int64_t,
+                               int);
 using NormKernelFn = void (*)(const unsigned char*, unsigned char*, const float2*, int64_t, int,
-                              int64_t, int64_t, int, int64_t, int);
+                              int64_t, int64_t, int, int64_t, int, int);
 
 // Row-kernel instance for (lanes per row G, vectors per lane V, prefetch), or
 // nullptr when that combination is not built. Defined per dtype in
@@ -31,6 +32,6 @@ inline RowKernelFn row_kernel(int dtype, int G, int V, int PF) {
 }
 
 // Threads per workgroup of the row kernel for G lanes per row.
-inline int row_block(int G) { return G >= 256 ? G : 256; }
+inline int row_block(int G) { return G > 64 ? G : 256; }
 
 }  // namespace smx

@@ -1,6 +1,7 @@
 // sm_softmax.hip -- host side of the gfx950 row-softmax library: argument
 // validation, plan selection, per-device occupancy cache, launches, and the C
 // ABI declared in include/sm_softmax.h and include/sm_bench.h.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -17,23 +18,21 @@
 namespace smx {
 
 // ------------------------------------------------------------ measurement kernels
-// 16-byte copy (bandwidth ceiling, counter calibration) and a read-modify-write
-// sweep that evicts earlier data from L2 and MALL.
+// 16-byte copy (bandwidth ceiling, counter calibration) and a read-only sweep
+// that evicts earlier data from L2 and MALL without leaving dirty lines behind.
 __global__ void __launch_bounds__(256) k_copy16(const uint4* src, uint4* dst, int64_t n) {
     const int64_t step = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) dst[i] = src[i];
 }
 
-__global__ void __launch_bounds__(256) k_touch16(uint4* buf, int64_t n) {
+__global__ void __launch_bounds__(256) k_sweep_read16(const uint4* buf, int64_t n) {
     const int64_t step = (int64_t)gridDim.x * 256;
+    uint32_t acc = 0;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
-        uint4 v = buf[i];
-        v.x += 1u;
-        v.y += 1u;
-        v.z += 1u;
-        v.w += 1u;
-        buf[i] = v;
+        const uint4 v = buf[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
+    asm volatile("" ::"v"(acc));  // the loads stay; nothing is written
 }
 
 // ------------------------------------------------------------ wide kernels
@@ -123,9 +122,15 @@ int validate(const Problem& p) {
 struct RowShape {
     int G, V;
 };
-// Preferred (lanes per row, vectors per lane) by windows needed, narrowest first.
-constexpr RowShape kShapes[] = {{16, 1},  {32, 1},  {64, 1},  {64, 2},   {64, 4},
-                                {64, 8},  {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+// Preferred (lanes per row, vectors per lane) by 16-byte windows needed, narrowest
+// first. Measured on MI355X (cold calls, FP16/BF16): rows of up to 64 windows
+// take one vector per lane in a sub-wave or wave; wider rows spread over 2-16
+// waves with 2-4 vectors per lane, which beat 4-8 vectors per lane in one wave
+// (fewer registers, more waves in flight, shorter per-row latency).
+constexpr RowShape kShapes[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {128, 2},
+                                {256, 2}, {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+// Calls that move at least this many bytes stream their input past the MALL.
+constexpr int64_t kNtLoadBytes = int64_t(256) << 20;
 
 bool built_shape(int G, int V, int PF) {
     const bool g_ok = G == 16 || G == 32 || G == 64 || G == 128 || G == 256 || G == 512 || G == 1024;
@@ -153,7 +158,15 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
 
     int plan = o.plan;
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_WIDE) return SM_ERR_PLAN;
-    if (plan == SM_PLAN_AUTO) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_PERSISTENT : SM_PLAN_WIDE;
+    const bool auto_plan = plan == SM_PLAN_AUTO;
+    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_WIDE;
+    const int64_t model = (plan == SM_PLAN_WIDE ? 3 : 2) * p.M * p.N * es;
+    int io = 0;
+    if (o.nontemporal == 0) io = model >= kNtLoadBytes ? kNtLoad : 0;
+    else if (o.nontemporal == 1) io = kNtLoad;
+    else if (o.nontemporal == 2) io = kNtLoad | kNtStore;
+    else if (o.nontemporal != -1) return SM_ERR_PLAN;
+    pi->io_flags = io;
 
     if (plan == SM_PLAN_WIDE) {
         const int WPC = kChunk / E;
@@ -177,7 +190,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
         pi->waves_per_row = wpr;
         pi->launches = 2;
         pi->workspace_bytes = ((waves * 8 + 255) / 256) * 256;
-        pi->model_bytes = 3 * p.M * p.N * es;
+        pi->model_bytes = model;
         return SM_OK;
     }
 
@@ -206,23 +219,29 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
         if (!found) return SM_ERR_PLAN;
     }
     if (!built_shape(G, V, 0) || (int64_t)G * V < nw_max) return SM_ERR_PLAN;
-    int PF;
-    if (plan == SM_PLAN_PERSISTENT) {
-        PF = (o.prefetch < 0) ? 1 : (o.prefetch ? 1 : 0);
-        if (PF && !built_shape(G, V, 1)) PF = 0;
-    } else {
-        PF = 0;
-    }
     const int block = row_block(G);
     const int gpb = block / G;
     const int64_t groups = (p.M + gpb - 1) / gpb;
     const int64_t cap = kMaxThreadsPerLaunch / block;
+    // Prefetching the next row paid off for rows held inside one wave, not for
+    // rows spread over several waves (measured).
+    int PF = (o.prefetch > 0) ? 1 : (o.prefetch < 0 ? 0 : (G <= 64 ? 1 : 0));
+    if (PF && !built_shape(G, V, 1)) PF = 0;
+    int64_t slots = 0;  // workgroups resident at once
+    if (plan == SM_PLAN_PERSISTENT || auto_plan) {
+        const int occ = std::max(1, dev.occ_row(dev.ctx, p.dtype, G, V, PF));
+        slots = (int64_t)occ * dev.cus;
+    }
+    // Auto: a grid-stride loop avoids relaunching workgroups when the rows fit in
+    // at most two rounds of resident workgroups; with more rows, one workgroup per
+    // row group kept memory streaming better (524288 x 2048 BF16: 617 vs 810 us).
+    if (auto_plan && groups <= 2 * slots) plan = SM_PLAN_PERSISTENT;
+    if (plan != SM_PLAN_PERSISTENT) PF = 0;
     int64_t grid;
     if (o.grid > 0) {
         grid = o.grid;
     } else if (plan == SM_PLAN_PERSISTENT) {
-        const int occ = std::max(1, dev.occ_row(dev.ctx, p.dtype, G, V, PF));
-        grid = (int64_t)occ * dev.cus;
+        grid = slots;
     } else {
         grid = groups;
     }
@@ -234,7 +253,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     pi->block = block;
     pi->grid = grid;
     pi->launches = 1;
-    pi->model_bytes = 2 * p.M * p.N * es;
+    pi->model_bytes = model;
     return SM_OK;
 }
 
@@ -298,34 +317,46 @@ int live_device(DeviceView* v) {
 
 sm_softmax_opts opts_or_default(const sm_softmax_opts* o) {
     sm_softmax_opts d{};
-    d.prefetch = -1;
     return o ? *o : d;
 }
 
 // ------------------------------------------------------------ launches
-int launch(const Problem& p, const sm_plan_info& pi, void* ws, hipStream_t stream) {
+// Launch `fn` with its arguments; with events, through hipExtLaunchKernel so
+// that the events carry the dispatch's own start/end times.
+template <typename... Args>
+hipError_t launch_k(const void* fn, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1, Args... args) {
+    void* argv[] = {reinterpret_cast<void*>(&args)...};
+    if (e0 || e1) return hipExtLaunchKernel(fn, grid, block, argv, 0, s, e0, e1, 0);
+    return hipLaunchKernel(fn, grid, block, argv, 0, s);
+}
+
+int launch(const Problem& p, const sm_plan_info& pi, void* ws, hipEvent_t ev0, hipEvent_t ev1,
+           hipStream_t stream) {
     const int es = elem_bytes(p.dtype);
     const auto* in = reinterpret_cast<const unsigned char*>(p.in);
     auto* out = reinterpret_cast<unsigned char*>(p.out);
     const int64_t isb = p.in_stride * es, osb = p.out_stride * es;
     const int N = (int)p.N;
+    hipError_t e;
     if (pi.plan == SM_PLAN_WIDE) {
         auto* st = reinterpret_cast<float2*>(ws);
-        hipLaunchKernelGGL(wide_stats_kernel(p.dtype), dim3((unsigned)pi.grid), dim3(256), 0, stream,
-                           in, st, p.M, N, isb, pi.chunks_per_wave, pi.waves_per_row);
-        hipError_t e = hipGetLastError();
+        const int cpw = pi.chunks_per_wave;
+        const int64_t wpr = pi.waves_per_row;
+        e = launch_k(reinterpret_cast<const void*>(wide_stats_kernel(p.dtype)),
+                     dim3((unsigned)pi.grid), dim3(256), stream, ev0, nullptr, in, st, p.M, N, isb,
+                     cpw, wpr, (int)pi.io_flags);
         if (e != hipSuccess) return hip_fail(e);
-        hipLaunchKernelGGL(wide_norm_kernel(p.dtype), dim3((unsigned)pi.grid), dim3(256), 0, stream,
-                           in, out, (const float2*)st, p.M, N, isb, osb, pi.chunks_per_wave,
-                           pi.waves_per_row, pi.same_phase);
-        e = hipGetLastError();
+        e = launch_k(reinterpret_cast<const void*>(wide_norm_kernel(p.dtype)),
+                     dim3((unsigned)pi.grid), dim3(256), stream, nullptr, ev1, in, out,
+                     (const float2*)st, p.M, N, isb, osb, cpw, wpr, (int)pi.same_phase,
+                     (int)pi.io_flags);
         return e == hipSuccess ? SM_OK : hip_fail(e);
     }
     RowKernelFn fn = row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.prefetch);
     if (!fn) return SM_ERR_PLAN;
-    hipLaunchKernelGGL(fn, dim3((unsigned)pi.grid), dim3(pi.block), 0, stream, in, out, p.M, N, isb,
-                       osb, pi.same_phase);
-    hipError_t e = hipGetLastError();
+    e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(pi.block), stream,
+                 ev0, ev1, in, out, p.M, N, isb, osb, (int)pi.same_phase, (int)pi.io_flags);
     return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 
@@ -350,14 +381,15 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     rc = live_device(&dv);
     if (rc != SM_OK) return rc;
     sm_plan_info pi;
-    rc = make_plan(p, opts_or_default(opts), dv, &pi);
+    const sm_softmax_opts o = opts_or_default(opts);
+    rc = make_plan(p, o, dv, &pi);
     if (rc != SM_OK) return rc;
-    if (pi.plan != SM_PLAN_WIDE) return launch(p, pi, nullptr, stream);
+    if (pi.plan != SM_PLAN_WIDE) return launch(p, pi, nullptr, o.start_event, o.stop_event, stream);
 
     if (ws) {
         if (ws_bytes < (size_t)pi.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
             return SM_ERR_WORKSPACE;
-        return launch(p, pi, ws, stream);
+        return launch(p, pi, ws, o.start_event, o.stop_event, stream);
     }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -366,7 +398,7 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     void* tmp = nullptr;
     e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
     if (e != hipSuccess) return hip_fail(e);
-    rc = launch(p, pi, tmp, stream);
+    rc = launch(p, pi, tmp, o.start_event, o.stop_event, stream);
     e = hipFreeAsync(tmp, stream);
     if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
     return rc;
@@ -437,7 +469,8 @@ int sm_softmax_version(void) { return SM_SOFTMAX_VERSION; }
 
 int sm_softmax_last_hip_error(void) { return t_last_hip_error; }
 
-int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream) {
+int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream,
+                  hipEvent_t start_event, hipEvent_t stop_event) {
     if (!src || !dst || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) ||
         (reinterpret_cast<uintptr_t>(dst) & 15))
         return SM_ERR_INVALID;
@@ -448,21 +481,20 @@ int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_
         if (rc != SM_OK) return rc;
         grid = 8 * dv.cus;
     }
-    hipLaunchKernelGGL(k_copy16, dim3(grid), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst),
-                       (int64_t)(bytes / 16));
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_k(reinterpret_cast<const void*>(&k_copy16), dim3(grid), dim3(256), stream,
+                            start_event, stop_event, reinterpret_cast<const uint4*>(src),
+                            reinterpret_cast<uint4*>(dst), (int64_t)(bytes / 16));
     return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 
-int sm_bench_flush(void* buf, size_t bytes, hipStream_t stream) {
+int sm_bench_flush(const void* buf, size_t bytes, hipStream_t stream) {
     if (!buf || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15)) return SM_ERR_INVALID;
     if (bytes == 0) return SM_OK;
     DeviceView dv;
     int rc = live_device(&dv);
     if (rc != SM_OK) return rc;
-    hipLaunchKernelGGL(k_touch16, dim3(8 * dv.cus), dim3(256), 0, stream,
-                       reinterpret_cast<uint4*>(buf), (int64_t)(bytes / 16));
+    hipLaunchKernelGGL(k_sweep_read16, dim3(8 * dv.cus), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(buf), (int64_t)(bytes / 16));
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? SM_OK : hip_fail(e);
 }

@@ -94,23 +94,42 @@ def plan(M, N, dtype, opts=None, in_ptr=BASE, out_ptr=BASE * 2, si=None, so=None
 
 
 def test_plan_rule_one_pass_shapes():
-    cases = {  # (M, N, dtype) -> (lanes per row, vectors per lane)
-        (8192, 127, F16): (16, 1),     # 16 windows of 8 (misaligned rows: 17 needed -> 32)
-        (8192, 256, F16): (32, 1),
-        (8192, 1000, F16): (64, 2),
-        (4096, 4096, BF16): (64, 8),
-        (8192, 8192, F16): (256, 4),
-        (128, 781, F32): (64, 4),
-        (16, 8192, F32): (512, 4),
+    # (M, N, dtype) -> (lanes per row, vectors per lane, plan); the host-only query
+    # assumes 2048 threads per CU, i.e. 2048 / block workgroups per CU, 256 CUs
+    cases = {
+        (8192, 127, F16): (32, 1, "persistent"),      # 254-byte rows: 17 windows when misaligned
+        (8192, 256, F16): (32, 1, "persistent"),
+        (8192, 1000, F16): (64, 2, "persistent"),
+        (4096, 4096, BF16): (256, 2, "persistent"),   # 4096 groups = 2 rounds of 2048
+        (8192, 4096, F16): (256, 2, "resident"),      # 8192 groups: 4 rounds
+        (8192, 8192, F16): (256, 4, "resident"),
+        (524288, 2048, BF16): (128, 2, "resident"),
+        (128, 781, F32): (128, 2, "persistent"),      # 3124-byte rows: 196 windows
+        (16, 8192, F32): (512, 4, "persistent"),
     }
-    for (M, N, dt), (G, V) in cases.items():
+    for (M, N, dt), (G, V, name) in cases.items():
         rc, p = plan(M, N, dt)
         assert rc == OK
-        want_g = 32 if (N, dt) == (127, F16) else G  # rows of 254 bytes are not 16-byte aligned
-        assert (p["lanes_per_row"], p["vecs_per_lane"]) == (want_g, V), (M, N, dt, p)
-        assert p["plan_name"] in ("resident", "persistent")
-        assert p["model_bytes"] == 2 * M * N * (4 if dt == F32 else 2)
-        assert p["lanes_per_row"] * p["vecs_per_lane"] * 16 >= N * (4 if dt == F32 else 2)
+        assert (p["lanes_per_row"], p["vecs_per_lane"], p["plan_name"]) == (G, V, name), (M, N, dt, p)
+        es = 4 if dt == F32 else 2
+        assert p["model_bytes"] == 2 * M * N * es
+        assert p["lanes_per_row"] * p["vecs_per_lane"] * 16 >= N * es
+        # streaming loads from 256 MiB of traffic up
+        assert p["io_flags"] == (1 if 2 * M * N * es >= 256 << 20 else 0)
+        if name == "persistent":
+            assert p["grid"] == min(256 * 2048 // p["block"], -(-M // (p["block"] // G)))
+            assert p["prefetch"] == (1 if G <= 64 else 0)
+
+
+def test_nontemporal_option():
+    rc, p = plan(4096, 4096, BF16, {"nontemporal": 1})
+    assert p["io_flags"] == 1
+    rc, p = plan(4096, 4096, BF16, {"nontemporal": 2})
+    assert p["io_flags"] == 3
+    rc, p = plan(524288, 2048, BF16, {"nontemporal": -1})
+    assert p["io_flags"] == 0
+    rc, p = plan(524288, 2048, BF16, {"nontemporal": 5})
+    assert rc == PLAN
 
 
 def test_plan_rule_wide():
@@ -128,7 +147,7 @@ def test_plan_rule_wide():
 
 def test_plan_forcing_and_limits():
     rc, p = plan(100, 5000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
-    assert rc == OK and p["plan_name"] == "resident" and p["grid"] == 100
+    assert rc == OK and p["plan_name"] == "resident" and p["grid"] == 100 and p["prefetch"] == 0
     rc, p = plan(100, 5000, BF16, {"plan": sm.SM_PLAN_WIDE})
     assert rc == OK and p["plan_name"] == "wide"
     rc, p = plan(100, 5000, BF16, {"plan": sm.SM_PLAN_PERSISTENT, "lanes_per_row": 64,

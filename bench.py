@@ -147,12 +147,17 @@ def main(argv=None) -> int:
                     help="skip the warm diagnostic lane (profiling runs: every softmax call is cold)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="summarise a rocprofv3 kernel trace of this bench (cold/warm per kernel) and exit")
+    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
+                    help="per-kernel mean of each rocprofv3 --pmc counter (per dispatch) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing on the host")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -261,20 +266,24 @@ def main(argv=None) -> int:
     dst = torch.empty_like(src)
     src.fill_(1)
 
-    def copy(events=(None, None)):
-        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), 0, s_handle, *events)
+    def copy(grid, events=(None, None)):
+        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), grid, s_handle, *events)
         if rc != 0:
             raise sm.SoftmaxError(rc, "sm_bench_copy")
 
-    for _ in range(args.warmup):
-        flush()
-        copy()
-    ev = DispatchEvents(args.steps)
-    for _ in range(args.steps):
-        flush()
-        copy(ev.next_pair())
-    copy_cold = stats_us(ev.samples_ms(torch))
-    ev.close()
+    copy_cold, copy_grid = None, None
+    for grid in (512, 1024, 2048):  # the ceiling is the best of a few launch shapes
+        for _ in range(args.warmup):
+            flush()
+            copy(grid)
+        ev = DispatchEvents(args.steps)
+        for _ in range(args.steps):
+            flush()
+            copy(grid, ev.next_pair())
+        st = stats_us(ev.samples_ms(torch))
+        ev.close()
+        if copy_cold is None or st["mean_us"] < copy_cold["mean_us"]:
+            copy_cold, copy_grid = st, grid
     del src, dst
 
     gbps = model_bytes / (cold["mean_us"] * 1e-6) / 1e9
@@ -319,6 +328,8 @@ def main(argv=None) -> int:
         "warm_us": ({k: round(v, 3) if isinstance(v, float) else v for k, v in warm.items()}
                     if warm else None),
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "copy_ceiling_us": round(copy_cold["mean_us"], 3),
+        "copy_ceiling_grid": copy_grid,
         "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
         "timed_region_wall_s": round(wall, 4),
         "parity": parity,
@@ -351,6 +362,22 @@ def summarize_trace(path: str) -> str:
         lines.append(f"{k[:48]:48s} {g:>11s} {w:>5s} {lane:5s} {len(v):6d} "
                      f"{statistics.mean(v):9.3f} {statistics.median(v):9.3f} {min(v):8.3f}")
     return "\n".join(lines)
+
+
+def summarize_counters(path: str) -> dict:
+    """{kernel: {counter: mean value per dispatch, "dispatches": n}} from a rocprofv3
+    --pmc counter-collection CSV (FETCH_SIZE / WRITE_SIZE are KiB per dispatch)."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        d = acc.setdefault(k, {})
+        d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {}
+    for k, d in acc.items():
+        out[k] = {c: round(statistics.mean(v), 3) for c, v in d.items()}
+        out[k]["dispatches"] = max(len(v) for v in d.values())
+    return out
 
 
 def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):

@@ -1,0 +1,56 @@
+"""The bench's byte model and the test tolerances, pinned to figures the pages print
+(tests/golden/page_figures.json names the page and section of each)."""
+import json
+import os
+
+import pytest
+
+import bench
+from parity import TOL, row_sum_bound
+
+FIG = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def test_one_pass_model_reproduces_logical_bandwidth():
+    f = FIG["fused_fp16_1024x1024_warm"]
+    gbps = bench.byte_model(f["M"], f["N"], f["elem_bytes"]) / (f["us"] * 1e-6) / 1e9
+    assert round(gbps / 10) * 10 == f["printed_GBps"]  # 1639.7 -> "about 1,640"
+
+
+def test_one_pass_model_reproduces_traffic_and_roof_fraction():
+    f = FIG["fused_bf16_8192x4096"]
+    bf16 = bench.byte_model(f["M"], f["N"], 2)
+    fp32 = bench.byte_model(f["M"], f["N"], 4)
+    assert round(bf16 / 1e6) == f["printed_MB_bf16"]
+    assert round(fp32 / 1e6) == f["printed_MB_fp32"]
+    frac = bf16 / (f["us"] * 1e-6) / 1e9 / f["roof_GBps"]
+    lo, hi = f["printed_fraction_range"]
+    assert lo <= frac <= hi
+
+
+def test_wide_model_is_three_passes_over_the_matrix():
+    f = FIG["warpline_k2_online_4x32768"]
+    ops = f["useful_TOPs"] * 1e12 * f["ms"] * 1e-3
+    requested = ops / f["ops_per_requested_byte"]
+    wide = bench.byte_model(f["M"], f["N"], f["elem_bytes"], wide=True)
+    one_pass = bench.byte_model(f["M"], f["N"], f["elem_bytes"])
+    assert abs(requested / wide - 1) < 0.005          # 786,584 vs 786,432
+    assert abs(requested / one_pass - 1) > 0.4        # the 2MN model does not fit
+    # the memory branch is the ceiling times the same intensity
+    assert f["ops_per_requested_byte"] * f["ceiling_GBps"] / 1e3 == pytest.approx(
+        f["memory_branch_TOPs"], rel=1e-3)
+
+
+def test_tolerances_follow_the_pages():
+    t = FIG["softmax_tolerance_bf16"]
+    assert TOL["bf16"] == (t["atol"], t["rtol"])
+    assert TOL["f16"] == (t["atol"], t["rtol"])   # the same tolerance applied to FP16
+    r = FIG["row_sum_tolerance_fp32"]
+    assert row_sum_bound("f32") == r["tolerance"]
+    assert r["failing_row_sum"] - 1 > row_sum_bound("f32")
+
+
+def test_stats_and_summaries():
+    st = bench.stats_us([0.001, 0.002, 0.003, 0.004])
+    assert st["median_us"] == 2.5 and st["min_us"] == 1.0 and st["max_us"] == 4.0
+    assert st["mean_us"] == 2.5 and st["n"] == 4

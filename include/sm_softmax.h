@@ -95,9 +95,10 @@ typedef struct sm_softmax_opts {
     int grid;            /* workgroups to launch; 0 = auto */
     int chunks_per_wave; /* WIDE: 1024-element chunks per wave; 0 = auto */
     int prefetch;        /* PERSISTENT: 1 = load the next row early, -1 = no; 0 = auto */
-    int nontemporal;     /* streaming cache hints on the row data: 1 = loads, 2 = loads and
-                            stores, -1 = none; 0 = auto (loads when the call moves at least
-                            256 MiB, the size of the MI355X MALL) */
+    int nontemporal;     /* streaming (nontemporal) loads of the input: 1 = yes, -1 = no,
+                            0 = auto (yes when the call moves at least 1 GiB, four times the
+                            MI355X MALL); one-pass plans have them on 128- to 1024-lane
+                            rows without prefetch, the WIDE plan on both passes */
     /* Optional timing events (created by the caller with hipEventCreate), or NULL.
      * They are attached to the kernel dispatches themselves (hipExtLaunchKernel):
      * start_event takes the start time of the call's first kernel and stop_event
@@ -113,7 +114,7 @@ typedef struct sm_plan_info {
     int lanes_per_row;
     int vecs_per_lane;
     int prefetch;
-    int io_flags;          /* 1 = nontemporal loads, 2 = nontemporal stores */
+    int nt_loads;          /* 1 = streaming (nontemporal) loads */
     int block;             /* threads per workgroup */
     int64_t grid;          /* workgroups per launch */
     int chunks_per_wave;   /* WIDE only */

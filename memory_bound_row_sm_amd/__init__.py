@@ -48,7 +48,7 @@ class SmOpts(ctypes.Structure):
 class SmPlanInfo(ctypes.Structure):
     _fields_ = [("plan", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
                 ("vecs_per_lane", ctypes.c_int), ("prefetch", ctypes.c_int),
-                ("io_flags", ctypes.c_int), ("block", ctypes.c_int), ("grid", ctypes.c_int64),
+                ("nt_loads", ctypes.c_int), ("block", ctypes.c_int), ("grid", ctypes.c_int64),
                 ("chunks_per_wave", ctypes.c_int), ("waves_per_row", ctypes.c_int64),
                 ("launches", ctypes.c_int), ("same_phase", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_int64), ("model_bytes", ctypes.c_int64)]

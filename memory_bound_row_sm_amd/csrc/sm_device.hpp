@@ -82,25 +82,24 @@ __device__ __forceinline__ uint4 encode(const float* f) {
 }
 
 // ------------------------------------------------------------ 16-byte global I/O
-// Row data moves in 16-byte vectors. `nt` selects the nontemporal (streaming)
-// cache hint, which the host turns on for inputs larger than the MALL.
+// Row data moves in 16-byte vectors. NT selects the nontemporal (streaming)
+// load hint; it is a template parameter because the compiler merges two loads
+// that differ only in their cache hint into one plain load.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-enum : int { kNtLoad = 1, kNtStore = 2 };  // io flag bits
-
-__device__ __forceinline__ uint4 load16(const unsigned char* p, bool nt) {
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const unsigned char* p) {
     const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
-    const u32x4_t v = nt ? __builtin_nontemporal_load(q) : *q;
+    u32x4_t v;
+    if constexpr (NT)
+        v = __builtin_nontemporal_load(q);
+    else
+        v = *q;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void store16(unsigned char* p, const uint4 v, bool nt) {
-    u32x4_t* q = reinterpret_cast<u32x4_t*>(p);
-    const u32x4_t w = {v.x, v.y, v.z, v.w};
-    if (nt)
-        __builtin_nontemporal_store(w, q);
-    else
-        *q = w;
+__device__ __forceinline__ void store16(unsigned char* p, const uint4 v) {
+    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{v.x, v.y, v.z, v.w};
 }
 
 // Store one element (already encoded) of an encoded vector: element k of `v`.

@@ -1,6 +1,6 @@
 // sm_kernels.hpp -- the gfx950 row-softmax kernels.
 //
-//   k_softmax_rows<DT, G, V, PF>  one-pass row body. A group of G lanes owns a
+//   k_softmax_rows<DT, G, V, PF, NT>  one-pass row body (NT: streaming loads). A group of G lanes owns a
 //       row and holds all of it in registers: lane l of the group loads the
 //       16-byte windows l, l + G, ..., l + (V-1)G of the row's 16-byte-aligned
 //       window grid, so every load instruction of a wave covers contiguous
@@ -41,9 +41,9 @@ struct RowGeom {
 // Load the V windows of one lane (windows past the row read as -inf words; a
 // window that holds at least one row element lies inside the same 4 KiB page
 // as that element, so it can always be read).
-template <int DT, int G, int V>
+template <int DT, int G, int V, bool NT>
 __device__ __forceinline__ void load_row(uint4 (&raw)[V], const unsigned char* in, int64_t row,
-                                         int64_t M, int N, int64_t in_sb, int lane, int io) {
+                                         int64_t M, int N, int64_t in_sb, int lane) {
     if (row >= M) return;
     const RowGeom<DT> g(in + row * in_sb, N);
     const uint32_t ni = Elem<DT>::neg_inf_word;
@@ -51,7 +51,7 @@ __device__ __forceinline__ void load_row(uint4 (&raw)[V], const unsigned char* i
     for (int v = 0; v < V; ++v) {
         const int w = lane + G * v;
         if (w < g.nwin)
-            raw[v] = load16(g.base + 16 * (size_t)w, io & kNtLoad);
+            raw[v] = load16<NT>(g.base + 16 * (size_t)w);
         else
             raw[v] = make_uint4(ni, ni, ni, ni);
     }
@@ -122,8 +122,8 @@ __device__ __forceinline__ float row_sum_acc(CSum c, float* lds_hi, float* lds_l
 template <int DT, int G, int V>
 __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigned char* in,
                                             unsigned char* out, int64_t row, int N, int64_t in_sb,
-                                            int64_t out_sb, int same_phase, int io, int lane,
-                                            float* lds_a, float* lds_b, float* lds_c) {
+                                            int64_t out_sb, int same_phase, int lane, float* lds_a,
+                                            float* lds_b, float* lds_c) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
     const RowGeom<DT> g(in + row * in_sb, N);
@@ -210,7 +210,7 @@ __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigne
             const uint4 enc = encode<DT>(y);
             const int c0 = w * E - g.head;
             if (same_phase && c0 >= 0 && c0 + E <= N) {
-                store16(orow + (size_t)c0 * ES, enc, io & kNtStore);
+                store16(orow + (size_t)c0 * ES, enc);
             } else {
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
@@ -232,10 +232,10 @@ struct RowLaunch {
     static_assert(G <= 64 || groups == 1, "multi-wave rows own their workgroup");
 };
 
-template <int DT, int G, int V, bool PF>
+template <int DT, int G, int V, bool PF, bool NT>
 __global__ void __launch_bounds__(RowLaunch<G>::block)
 k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, int64_t in_sb,
-               int64_t out_sb, int same_phase, int io) {
+               int64_t out_sb, int same_phase) {
     constexpr int GPB = RowLaunch<G>::groups;
     constexpr int NW = G > 64 ? G / 64 : 1;
     __shared__ float lds_a[NW], lds_b[NW], lds_c[NW];
@@ -247,20 +247,20 @@ k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, in
     int64_t row = (int64_t)blockIdx.x * GPB + grp;
 
     uint4 cur[V];
-    load_row<DT, G, V>(cur, in, row, M, N, in_sb, lane, io);
+    load_row<DT, G, V, NT>(cur, in, row, M, N, in_sb, lane);
     while (row < M) {
         const int64_t next = row + rstep;
         if constexpr (PF) {
             uint4 nxt[V];
-            load_row<DT, G, V>(nxt, in, next, M, N, in_sb, lane, io);
-            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, io, lane, lds_a,
+            load_row<DT, G, V, NT>(nxt, in, next, M, N, in_sb, lane);
+            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, lane, lds_a,
                                   lds_b, lds_c);
 #pragma unroll
             for (int v = 0; v < V; ++v) cur[v] = nxt[v];
         } else {
-            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, io, lane, lds_a,
+            process_row<DT, G, V>(cur, in, out, row, N, in_sb, out_sb, same_phase, lane, lds_a,
                                   lds_b, lds_c);
-            load_row<DT, G, V>(cur, in, next, M, N, in_sb, lane, io);
+            load_row<DT, G, V, NT>(cur, in, next, M, N, in_sb, lane);
         }
         row = next;
     }
@@ -277,16 +277,16 @@ struct Wide {
     static constexpr int VPL = WPC / 64;  // windows per lane per chunk
 };
 
-template <int DT>
+template <int DT, bool NT>
 __device__ __forceinline__ void load_chunk(uint4 (&raw)[Wide<DT>::VPL], const RowGeom<DT>& g,
-                                           int64_t c, int lane, int io) {
+                                           int64_t c, int lane) {
     constexpr int WPC = Wide<DT>::WPC;
     const uint32_t ni = Elem<DT>::neg_inf_word;
 #pragma unroll
     for (int v = 0; v < Wide<DT>::VPL; ++v) {
         const int64_t w = c * WPC + lane + 64 * v;
         if (w < g.nwin)
-            raw[v] = load16(g.base + 16 * (size_t)w, io & kNtLoad);
+            raw[v] = load16<NT>(g.base + 16 * (size_t)w);
         else
             raw[v] = make_uint4(ni, ni, ni, ni);
     }
@@ -317,10 +317,10 @@ __device__ __forceinline__ void decode_chunk(const uint4 (&raw)[Wide<DT>::VPL],
 
 // Pass 1: per-lane online (max, sum) over the wave's chunks; then the wave's
 // 64 lane states are merged and written as one (max, sum) pair.
-template <int DT>
+template <int DT, bool NT>
 __global__ void __launch_bounds__(256)
 k_wide_stats(const unsigned char* in, float2* stats, int64_t M, int N, int64_t in_sb, int cpw,
-             int64_t wpr, int io) {
+             int64_t wpr) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int VPL = Wide<DT>::VPL;
     constexpr int WPC = Wide<DT>::WPC;
@@ -339,7 +339,7 @@ k_wide_stats(const unsigned char* in, float2* stats, int64_t M, int N, int64_t i
     CSum cs;
     for (int64_t c = c_begin; c < c_end; ++c) {
         uint4 raw[VPL];
-        load_chunk<DT>(raw, g, c, lane, io);
+        load_chunk<DT, NT>(raw, g, c, lane);
         float x[VPL][E];
         decode_chunk<DT>(raw, x, g, N, c, lane);
         float cm = m;
@@ -417,10 +417,10 @@ __device__ __forceinline__ void row_stats(const float2* st, int64_t wpr, int lan
 
 // Pass 2: merge the row's statistics, re-read the wave's chunks, normalise,
 // round once, store.
-template <int DT>
+template <int DT, bool NT>
 __global__ void __launch_bounds__(256)
 k_wide_norm(const unsigned char* in, unsigned char* out, const float2* stats, int64_t M, int N,
-            int64_t in_sb, int64_t out_sb, int cpw, int64_t wpr, int same_phase, int io) {
+            int64_t in_sb, int64_t out_sb, int cpw, int64_t wpr, int same_phase) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
     constexpr int VPL = Wide<DT>::VPL;
@@ -445,7 +445,7 @@ k_wide_norm(const unsigned char* in, unsigned char* out, const float2* stats, in
 
     for (int64_t c = c_begin; c < c_end; ++c) {
         uint4 raw[VPL];
-        load_chunk<DT>(raw, g, c, lane, io);
+        load_chunk<DT, NT>(raw, g, c, lane);
         float x[VPL][E];
 #pragma unroll
         for (int v = 0; v < VPL; ++v) decode<DT>(raw[v], x[v]);
@@ -468,7 +468,7 @@ k_wide_norm(const unsigned char* in, unsigned char* out, const float2* stats, in
                 const uint4 enc = encode<DT>(y);
                 const int64_t c0 = w * E - g.head;
                 if (same_phase && c0 >= 0 && c0 + E <= N) {
-                    store16(orow + (size_t)c0 * ES, enc, io & kNtStore);
+                    store16(orow + (size_t)c0 * ES, enc);
                 } else {
 #pragma unroll
                     for (int k = 0; k < E; ++k) {

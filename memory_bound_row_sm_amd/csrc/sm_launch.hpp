@@ -7,26 +7,25 @@
 namespace smx {
 
 using RowKernelFn = void (*)(const unsigned char*, unsigned char*, int64_t, int, int64_t, int64_t,
-                             int, int);
-using StatsKernelFn = void (*)(const unsigned char*, float2*, int64_t, int, int64_t, int, int64_t,
-                               int);
+                             int);
+using StatsKernelFn = void (*)(const unsigned char*, float2*, int64_t, int, int64_t, int, int64_t);
 using NormKernelFn = void (*)(const unsigned char*, unsigned char*, const float2*, int64_t, int,
-                              int64_t, int64_t, int, int64_t, int, int);
+                              int64_t, int64_t, int, int64_t, int);
 
-// Row-kernel instance for (lanes per row G, vectors per lane V, prefetch), or
-// nullptr when that combination is not built. Defined per dtype in
-// sm_rows_{f32,f16,bf16}.hip.
-RowKernelFn row_kernel_f32(int G, int V, int PF);
-RowKernelFn row_kernel_f16(int G, int V, int PF);
-RowKernelFn row_kernel_bf16(int G, int V, int PF);
-StatsKernelFn wide_stats_kernel(int dtype);
-NormKernelFn wide_norm_kernel(int dtype);
+// Row-kernel instance for (lanes per row G, vectors per lane V, prefetch,
+// streaming loads), or nullptr when that combination is not built. Defined per
+// dtype in sm_rows_{f32,f16,bf16}.hip.
+RowKernelFn row_kernel_f32(int G, int V, int PF, int NT);
+RowKernelFn row_kernel_f16(int G, int V, int PF, int NT);
+RowKernelFn row_kernel_bf16(int G, int V, int PF, int NT);
+StatsKernelFn wide_stats_kernel(int dtype, int NT);
+NormKernelFn wide_norm_kernel(int dtype, int NT);
 
-inline RowKernelFn row_kernel(int dtype, int G, int V, int PF) {
+inline RowKernelFn row_kernel(int dtype, int G, int V, int PF, int NT) {
     switch (dtype) {
-    case 0: return row_kernel_f32(G, V, PF);
-    case 1: return row_kernel_f16(G, V, PF);
-    case 2: return row_kernel_bf16(G, V, PF);
+    case 0: return row_kernel_f32(G, V, PF, NT);
+    case 1: return row_kernel_f16(G, V, PF, NT);
+    case 2: return row_kernel_bf16(G, V, PF, NT);
     default: return nullptr;
     }
 }

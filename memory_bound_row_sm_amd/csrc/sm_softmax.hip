@@ -36,19 +36,19 @@ __global__ void __launch_bounds__(256) k_sweep_read16(const uint4* buf, int64_t 
 }
 
 // ------------------------------------------------------------ wide kernels
-StatsKernelFn wide_stats_kernel(int dtype) {
+StatsKernelFn wide_stats_kernel(int dtype, int NT) {
     switch (dtype) {
-    case kF32: return &k_wide_stats<kF32>;
-    case kF16: return &k_wide_stats<kF16>;
-    case kBF16: return &k_wide_stats<kBF16>;
+    case kF32: return NT ? &k_wide_stats<kF32, true> : &k_wide_stats<kF32, false>;
+    case kF16: return NT ? &k_wide_stats<kF16, true> : &k_wide_stats<kF16, false>;
+    case kBF16: return NT ? &k_wide_stats<kBF16, true> : &k_wide_stats<kBF16, false>;
     default: return nullptr;
     }
 }
-NormKernelFn wide_norm_kernel(int dtype) {
+NormKernelFn wide_norm_kernel(int dtype, int NT) {
     switch (dtype) {
-    case kF32: return &k_wide_norm<kF32>;
-    case kF16: return &k_wide_norm<kF16>;
-    case kBF16: return &k_wide_norm<kBF16>;
+    case kF32: return NT ? &k_wide_norm<kF32, true> : &k_wide_norm<kF32, false>;
+    case kF16: return NT ? &k_wide_norm<kF16, true> : &k_wide_norm<kF16, false>;
+    case kBF16: return NT ? &k_wide_norm<kBF16, true> : &k_wide_norm<kBF16, false>;
     default: return nullptr;
     }
 }
@@ -122,15 +122,42 @@ int validate(const Problem& p) {
 struct RowShape {
     int G, V;
 };
-// Preferred (lanes per row, vectors per lane) by 16-byte windows needed, narrowest
-// first. Measured on MI355X (cold calls, FP16/BF16): rows of up to 64 windows
-// take one vector per lane in a sub-wave or wave; wider rows spread over 2-16
+// Row shapes (lanes per row, vectors per lane) by 16-byte windows needed,
+// narrowest first, measured on MI355X with cold calls. Rows of up to 64 windows
+// take one vector per lane in a sub-wave or wave. Wider rows spread over 2-16
 // waves with 2-4 vectors per lane, which beat 4-8 vectors per lane in one wave
-// (fewer registers, more waves in flight, shorter per-row latency).
-constexpr RowShape kShapes[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {128, 2},
-                                {256, 2}, {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
-// Calls that move at least this many bytes stream their input past the MALL.
-constexpr int64_t kNtLoadBytes = int64_t(256) << 20;
+// (fewer registers, more waves in flight, shorter per-row latency). With many
+// rows (resident plan) 256-lane rows won from 256 windows up (524288 x 2048 BF16:
+// 659 us for 256 x 2 against 685 us for 128 x 2); with few rows (persistent
+// plan) the narrower 128-lane rows did (8192 x 2048 FP16: 11.8 us against 12.7).
+constexpr RowShape kShapesPersistent[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {128, 2},
+                                          {256, 2}, {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+constexpr RowShape kShapesResident[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {256, 2},
+                                        {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+// Calls that move at least this many bytes stream their input past the MALL
+// (524288 x 2048 BF16, 4 GiB: 639 against 659 us; below 1 GiB streaming loads
+// cost 1-3%).
+constexpr int64_t kNtLoadBytes = int64_t(1) << 30;
+
+template <size_t K>
+bool pick_shape(const RowShape (&tab)[K], int64_t nw, int fixG, int fixV, int& G, int& V) {
+    for (const RowShape& s : tab) {
+        if ((fixG && s.G != fixG) || (fixV && s.V != fixV)) continue;
+        if ((int64_t)s.G * s.V >= nw) {
+            G = s.G;
+            V = s.V;
+            return true;
+        }
+    }
+    if (fixG && !fixV) {  // a fixed G outside the table: smallest V that fits
+        for (int v : {1, 2, 4, 8})
+            if ((int64_t)fixG * v >= nw) { G = fixG; V = v; return true; }
+    } else if (fixV && !fixG) {
+        for (int g : {16, 32, 64, 128, 256, 512, 1024})
+            if ((int64_t)g * fixV >= nw) { G = g; V = fixV; return true; }
+    }
+    return false;
+}
 
 bool built_shape(int G, int V, int PF) {
     const bool g_ok = G == 16 || G == 32 || G == 64 || G == 128 || G == 256 || G == 512 || G == 1024;
@@ -160,13 +187,9 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_WIDE) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
     if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_WIDE;
+    if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
     const int64_t model = (plan == SM_PLAN_WIDE ? 3 : 2) * p.M * p.N * es;
-    int io = 0;
-    if (o.nontemporal == 0) io = model >= kNtLoadBytes ? kNtLoad : 0;
-    else if (o.nontemporal == 1) io = kNtLoad;
-    else if (o.nontemporal == 2) io = kNtLoad | kNtStore;
-    else if (o.nontemporal != -1) return SM_ERR_PLAN;
-    pi->io_flags = io;
+    const bool want_nt = o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes);
 
     if (plan == SM_PLAN_WIDE) {
         const int WPC = kChunk / E;
@@ -189,54 +212,58 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
         pi->chunks_per_wave = (int)cpw;
         pi->waves_per_row = wpr;
         pi->launches = 2;
+        pi->nt_loads = want_nt ? 1 : 0;
         pi->workspace_bytes = ((waves * 8 + 255) / 256) * 256;
         pi->model_bytes = model;
         return SM_OK;
     }
 
-    // One-pass plans: pick a row shape that holds the whole row.
-    int G = o.lanes_per_row, V = o.vecs_per_lane;
-    if (G == 0 || V == 0) {
-        bool found = false;
-        for (const RowShape& s : kShapes) {
-            if ((G && s.G != G) || (V && s.V != V)) continue;
-            if ((int64_t)s.G * s.V >= nw_max) {
-                G = s.G;
-                V = s.V;
-                found = true;
-                break;
-            }
+    // One-pass plans: a row shape that holds the whole row.
+    const int fixG = o.lanes_per_row, fixV = o.vecs_per_lane;
+    int G = fixG, V = fixV;
+    const bool auto_shape = !(fixG && fixV);
+    auto prefetch_for = [&](int g, int v) {
+        // Prefetching the next row paid off for rows held inside one wave, not
+        // for rows spread over several waves (measured).
+        int pf = (o.prefetch > 0) ? 1 : (o.prefetch < 0 ? 0 : (g <= 64 ? 1 : 0));
+        return (pf && built_shape(g, v, 1)) ? 1 : 0;
+    };
+    int64_t slots = 0;  // workgroups resident at once
+    if (auto_plan) {
+        // Auto: a grid-stride loop avoids relaunching workgroups when the rows fit
+        // in at most two rounds of resident workgroups; with more rows, one
+        // workgroup per row group kept memory streaming better (524288 x 2048
+        // BF16: 659 against 909 us).
+        int gp = G, vp = V;
+        if (auto_shape && !pick_shape(kShapesPersistent, nw_max, fixG, fixV, gp, vp)) return SM_ERR_PLAN;
+        const int gpb = row_block(gp) / gp;
+        const int occ = std::max(1, dev.occ_row(dev.ctx, p.dtype, gp, vp, prefetch_for(gp, vp)));
+        slots = (int64_t)occ * dev.cus;
+        if ((p.M + gpb - 1) / gpb <= 2 * slots) {
+            plan = SM_PLAN_PERSISTENT;
+            G = gp;
+            V = vp;
+        } else if (auto_shape && !pick_shape(kShapesResident, nw_max, fixG, fixV, G, V)) {
+            return SM_ERR_PLAN;
         }
-        if (!found) {
-            if (G && !V) {  // fixed G: smallest V that fits
-                for (int v : {1, 2, 4, 8})
-                    if ((int64_t)G * v >= nw_max) { V = v; found = true; break; }
-            } else if (V && !G) {
-                for (int g : {16, 32, 64, 128, 256, 512, 1024})
-                    if ((int64_t)g * V >= nw_max) { G = g; found = true; break; }
-            }
-        }
-        if (!found) return SM_ERR_PLAN;
+    } else if (auto_shape) {
+        const bool ok = plan == SM_PLAN_PERSISTENT
+                            ? pick_shape(kShapesPersistent, nw_max, fixG, fixV, G, V)
+                            : pick_shape(kShapesResident, nw_max, fixG, fixV, G, V);
+        if (!ok) return SM_ERR_PLAN;
     }
     if (!built_shape(G, V, 0) || (int64_t)G * V < nw_max) return SM_ERR_PLAN;
     const int block = row_block(G);
     const int gpb = block / G;
     const int64_t groups = (p.M + gpb - 1) / gpb;
     const int64_t cap = kMaxThreadsPerLaunch / block;
-    // Prefetching the next row paid off for rows held inside one wave, not for
-    // rows spread over several waves (measured).
-    int PF = (o.prefetch > 0) ? 1 : (o.prefetch < 0 ? 0 : (G <= 64 ? 1 : 0));
-    if (PF && !built_shape(G, V, 1)) PF = 0;
-    int64_t slots = 0;  // workgroups resident at once
-    if (plan == SM_PLAN_PERSISTENT || auto_plan) {
+    const int PF = plan == SM_PLAN_PERSISTENT ? prefetch_for(G, V) : 0;
+    if (plan == SM_PLAN_PERSISTENT && slots == 0) {
         const int occ = std::max(1, dev.occ_row(dev.ctx, p.dtype, G, V, PF));
         slots = (int64_t)occ * dev.cus;
     }
-    // Auto: a grid-stride loop avoids relaunching workgroups when the rows fit in
-    // at most two rounds of resident workgroups; with more rows, one workgroup per
-    // row group kept memory streaming better (524288 x 2048 BF16: 617 vs 810 us).
-    if (auto_plan && groups <= 2 * slots) plan = SM_PLAN_PERSISTENT;
-    if (plan != SM_PLAN_PERSISTENT) PF = 0;
+    // Streaming loads exist for the resident multi-wave shapes.
+    const int NT = (want_nt && !PF && G >= 128) ? 1 : 0;
     int64_t grid;
     if (o.grid > 0) {
         grid = o.grid;
@@ -250,6 +277,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     pi->lanes_per_row = G;
     pi->vecs_per_lane = V;
     pi->prefetch = PF;
+    pi->nt_loads = NT;
     pi->block = block;
     pi->grid = grid;
     pi->launches = 1;
@@ -279,11 +307,11 @@ int occ_of(const void* fn, int block) {
 }
 
 int occ_row_live(void*, int dtype, int G, int V, int PF) {
-    RowKernelFn fn = row_kernel(dtype, G, V, PF);
+    RowKernelFn fn = row_kernel(dtype, G, V, PF, 0);
     return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
 }
 int occ_wide_live(void*, int dtype) {
-    return occ_of(reinterpret_cast<const void*>(wide_stats_kernel(dtype)), 256);
+    return occ_of(reinterpret_cast<const void*>(wide_stats_kernel(dtype, 0)), 256);
 }
 int occ_row_host(void*, int, int G, int, int) { return std::max(1, 2048 / row_block(G)); }
 int occ_wide_host(void*, int) { return 8; }
@@ -343,20 +371,20 @@ int launch(const Problem& p, const sm_plan_info& pi, void* ws, hipEvent_t ev0, h
         auto* st = reinterpret_cast<float2*>(ws);
         const int cpw = pi.chunks_per_wave;
         const int64_t wpr = pi.waves_per_row;
-        e = launch_k(reinterpret_cast<const void*>(wide_stats_kernel(p.dtype)),
+        e = launch_k(reinterpret_cast<const void*>(wide_stats_kernel(p.dtype, pi.nt_loads)),
                      dim3((unsigned)pi.grid), dim3(256), stream, ev0, nullptr, in, st, p.M, N, isb,
-                     cpw, wpr, (int)pi.io_flags);
+                     cpw, wpr);
         if (e != hipSuccess) return hip_fail(e);
-        e = launch_k(reinterpret_cast<const void*>(wide_norm_kernel(p.dtype)),
+        e = launch_k(reinterpret_cast<const void*>(wide_norm_kernel(p.dtype, pi.nt_loads)),
                      dim3((unsigned)pi.grid), dim3(256), stream, nullptr, ev1, in, out,
-                     (const float2*)st, p.M, N, isb, osb, cpw, wpr, (int)pi.same_phase,
-                     (int)pi.io_flags);
+                     (const float2*)st, p.M, N, isb, osb, cpw, wpr, (int)pi.same_phase);
         return e == hipSuccess ? SM_OK : hip_fail(e);
     }
-    RowKernelFn fn = row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.prefetch);
+    RowKernelFn fn =
+        row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.prefetch, pi.nt_loads);
     if (!fn) return SM_ERR_PLAN;
     e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(pi.block), stream,
-                 ev0, ev1, in, out, p.M, N, isb, osb, (int)pi.same_phase, (int)pi.io_flags);
+                 ev0, ev1, in, out, p.M, N, isb, osb, (int)pi.same_phase);
     return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 

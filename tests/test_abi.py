@@ -103,7 +103,7 @@ def test_plan_rule_one_pass_shapes():
         (4096, 4096, BF16): (256, 2, "persistent"),   # 4096 groups = 2 rounds of 2048
         (8192, 4096, F16): (256, 2, "resident"),      # 8192 groups: 4 rounds
         (8192, 8192, F16): (256, 4, "resident"),
-        (524288, 2048, BF16): (128, 2, "resident"),
+        (524288, 2048, BF16): (256, 2, "resident"),    # many rows: the resident table
         (128, 781, F32): (128, 2, "persistent"),      # 3124-byte rows: 196 windows
         (16, 8192, F32): (512, 4, "persistent"),
     }
@@ -114,8 +114,8 @@ def test_plan_rule_one_pass_shapes():
         es = 4 if dt == F32 else 2
         assert p["model_bytes"] == 2 * M * N * es
         assert p["lanes_per_row"] * p["vecs_per_lane"] * 16 >= N * es
-        # streaming loads from 256 MiB of traffic up
-        assert p["io_flags"] == (1 if 2 * M * N * es >= 256 << 20 else 0)
+        # streaming loads from 1 GiB of traffic up, on 128- to 1024-lane rows
+        assert p["nt_loads"] == (1 if 2 * M * N * es >= 1 << 30 and G >= 128 else 0)
         if name == "persistent":
             assert p["grid"] == min(256 * 2048 // p["block"], -(-M // (p["block"] // G)))
             assert p["prefetch"] == (1 if G <= 64 else 0)
@@ -123,13 +123,18 @@ def test_plan_rule_one_pass_shapes():
 
 def test_nontemporal_option():
     rc, p = plan(4096, 4096, BF16, {"nontemporal": 1})
-    assert p["io_flags"] == 1
-    rc, p = plan(4096, 4096, BF16, {"nontemporal": 2})
-    assert p["io_flags"] == 3
+    assert rc == OK and p["nt_loads"] == 1
+    rc, p = plan(8192, 1000, F16, {"nontemporal": 1})
+    assert rc == OK and p["nt_loads"] == 0          # 64-lane rows have no streaming instance
+    rc, p = plan(524288, 2048, BF16)
+    assert p["nt_loads"] == 1
     rc, p = plan(524288, 2048, BF16, {"nontemporal": -1})
-    assert p["io_flags"] == 0
-    rc, p = plan(524288, 2048, BF16, {"nontemporal": 5})
-    assert rc == PLAN
+    assert p["nt_loads"] == 0
+    rc, p = plan(64, 131072, BF16, {"nontemporal": 1})
+    assert p["plan_name"] == "wide" and p["nt_loads"] == 1
+    for bad in (2, 5, -2):
+        rc, p = plan(524288, 2048, BF16, {"nontemporal": bad})
+        assert rc == PLAN
 
 
 def test_plan_rule_wide():
@@ -155,6 +160,10 @@ def test_plan_forcing_and_limits():
     assert rc == PLAN  # 64 windows hold 512 elements, not 5000
     rc, p = plan(100, 40000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
     assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (1024, 8)
+    rc, p = plan(100, 2000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
+    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 2)   # resident table
+    rc, p = plan(100, 2000, BF16, {"plan": sm.SM_PLAN_PERSISTENT})
+    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (128, 2)   # persistent table
     rc, p = plan(100, 70000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
     assert rc == PLAN
     rc, p = plan(100, 500, BF16, {"plan": 9})

@@ -346,11 +346,16 @@ def test_every_row_kernel_instance(dt):
         for V in (1, 2, 4, 8):
             if G * V * 16 < (N + 16 // es) * es:
                 continue
-            for plan, pf in (("resident", 0), ("persistent", 0), ("persistent", 1)):
-                if pf and G > 256:
+            for plan, pf, nt in (("resident", 0, -1), ("resident", 0, 1), ("persistent", 0, -1),
+                                 ("persistent", 1, -1)):
+                if (pf and G > 256) or (nt == 1 and G < 128):
                     continue
-                g = run(xd, plan, lanes_per_row=G, vecs_per_lane=V, prefetch=1 if pf else -1, grid=7)
-                compare(g, x.contiguous(), what=f"{dt} G={G} V={V} {plan} pf={pf}")
+                g = run(xd, plan, lanes_per_row=G, vecs_per_lane=V, prefetch=1 if pf else -1,
+                        nontemporal=nt, grid=7)
+                compare(g, x.contiguous(), what=f"{dt} G={G} V={V} {plan} pf={pf} nt={nt}")
                 n += 1
+    for nt in (-1, 1):  # both wide-path instances
+        g = run(xd, "wide", nontemporal=nt)
+        compare(g, x.contiguous(), what=f"{dt} wide nt={nt}")
     log(f"[parity] {dt}: {n} row-kernel instances checked")
-    assert n >= 40
+    assert n >= 50

@@ -62,9 +62,11 @@ class Oracle:
         lib.oracle_decode.argtypes = [vp, ctypes.c_int, i64, _DP]
         lib.oracle_encode.argtypes = [_DP, ctypes.c_int, i64, vp]
         lib.oracle_softmax_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, _DP, ctypes.c_int]
+        lib.oracle_softmax_bwd_rows.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, i64, _DP,
+                                                ctypes.c_int]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_softmax_rows,
-                  lib.oracle_max_threads):
+                  lib.oracle_softmax_bwd_rows, lib.oracle_max_threads):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -124,6 +126,44 @@ class Oracle:
         y = self.softmax_f64(x, dtype, rows=rows, threads=threads)
         return y, self.encode(y, dtype)
 
+    def softmax_bwd_f64(self, y: np.ndarray, dy: np.ndarray, dtype, rows=None,
+                        threads: int = 0) -> np.ndarray:
+        """FP64 dx = y * (dy - sum(y * dy)) per row, from stored y and dy (2-D, row-strided
+        views allowed; same shape and dtype)."""
+        a = _as_storage(y, dtype)
+        b = _as_storage(dy, dtype)
+        if a.ndim != 2 or a.shape != b.shape:
+            raise ValueError("y and dy must be 2-D matrices of one shape")
+        es = a.dtype.itemsize
+        M, N = a.shape
+        nrows = M if rows is None else len(rows)
+        if a.size == 0:
+            return np.empty((nrows, N), np.float64)
+        for t in (a, b):
+            if N > 1 and t.strides[1] != es:
+                raise ValueError("column stride must be one element")
+            if t.strides[0] % es or t.strides[0] < 0:
+                raise ValueError("row stride must be a non-negative multiple of the element size")
+        sa = a.strides[0] // es if M > 1 else N
+        sb = b.strides[0] // es if M > 1 else N
+        idx = None
+        if rows is not None:
+            idx = np.ascontiguousarray(rows, dtype=np.int64)
+            if idx.size and (idx.min() < 0 or idx.max() >= M):
+                raise IndexError("row index out of range")
+        out = np.empty((nrows, N), np.float64)
+        rc = self.lib.oracle_softmax_bwd_rows(
+            a.ctypes.data, b.ctypes.data, _code(dtype), N, sa, sb,
+            None if idx is None else idx.ctypes.data, nrows, out.ctypes.data_as(_DP), int(threads))
+        if rc:
+            raise ValueError("oracle_softmax_bwd_rows rejected its arguments")
+        return out
+
+    def reference_bwd(self, y, dy, dtype, rows=None, threads: int = 0):
+        """(dx_f64, dx_rounded)."""
+        dx = self.softmax_bwd_f64(y, dy, dtype, rows=rows, threads=threads)
+        return dx, self.encode(dx, dtype)
+
 
 _default = None
 
@@ -157,3 +197,11 @@ def softmax_f64(x, dtype, rows=None, threads: int = 0):
 
 def reference(x, dtype, rows=None, threads: int = 0):
     return default().reference(x, dtype, rows=rows, threads=threads)
+
+
+def softmax_bwd_f64(y, dy, dtype, rows=None, threads: int = 0):
+    return default().softmax_bwd_f64(y, dy, dtype, rows=rows, threads=threads)
+
+
+def reference_bwd(y, dy, dtype, rows=None, threads: int = 0):
+    return default().reference_bwd(y, dy, dtype, rows=rows, threads=threads)

@@ -27,6 +27,13 @@
  *   4. s = sum of e_j, added left to right in double;
  *   5. y_j = e_j / s in double.
  *
+ * The backward of the same operation ("Measured optimization case studies",
+ * section "Training: backward kernels through autograd": the softmax keeps its
+ * output y and forms y * (dy - sum(y * dy))) is computed from the stored y and
+ * dy, decoded exactly, by the same plain steps in FP64:
+ *   1. d = sum_j y_j * dy_j, added left to right;
+ *   2. dx_j = y_j * (dy_j - d).
+ *
  * Readings where the pages are silent (listed in the design notes too):
  *   - a row whose entries are all -inf (and an empty row) has no finite
  *     maximum; the online-merge guard of "Measured optimization case studies",
@@ -215,6 +222,56 @@ int oracle_softmax_rows(const void *in, int dtype, int64_t cols, int64_t in_stri
             softmax_row(x, cols, y + (size_t)k * (size_t)cols);
         }
         free(x);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Backward of one decoded row: dx = y * (dy - sum(y * dy)). */
+static void softmax_bwd_row(const double *y, const double *dy, int64_t n, double *dx) {
+    double d = 0.0;
+    for (int64_t j = 0; j < n; ++j) d += y[j] * dy[j];
+    for (int64_t j = 0; j < n; ++j) dx[j] = y[j] * (dy[j] - d);
+}
+
+/*
+ * Softmax backward of selected rows.
+ *   y, dy      : stored softmax output and upstream gradient (same dtype), row r of
+ *                each at base + r * stride elements
+ *   rows       : row indices, or NULL for rows 0..nrows-1
+ *   dx         : output, nrows x cols doubles, contiguous
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_softmax_bwd_rows(const void *y, const void *dy, int dtype, int64_t cols,
+                            int64_t y_stride, int64_t dy_stride, const int64_t *rows,
+                            int64_t nrows, double *dx, int threads) {
+    int es = elem_size(dtype);
+    if (!es || cols < 0 || nrows < 0 || y_stride < cols || dy_stride < cols) return -1;
+    if (nrows == 0 || cols == 0) return 0;
+    const unsigned char *yb = (const unsigned char *)y;
+    const unsigned char *db = (const unsigned char *)dy;
+#ifdef _OPENMP
+    if (threads <= 0) threads = omp_get_max_threads();
+#else
+    threads = 1;
+#endif
+    int bad = 0;
+#pragma omp parallel num_threads(threads) reduction(| : bad)
+    {
+        double *a = (double *)malloc(sizeof(double) * 2 * (size_t)cols);
+        if (!a) bad = 1;
+#pragma omp for schedule(static)
+        for (int64_t k = 0; k < nrows; ++k) {
+            if (!a) continue;
+            int64_t r = rows ? rows[k] : k;
+            const unsigned char *yr = yb + (size_t)(r * y_stride) * (size_t)es;
+            const unsigned char *dr = db + (size_t)(r * dy_stride) * (size_t)es;
+            for (int64_t j = 0; j < cols; ++j) {
+                a[j] = load_elem(yr + (size_t)j * es, dtype);
+                a[cols + j] = load_elem(dr + (size_t)j * es, dtype);
+            }
+            softmax_bwd_row(a, a + cols, cols, dx + (size_t)k * (size_t)cols);
+        }
+        free(a);
     }
     return bad ? -1 : 0;
 }

@@ -38,6 +38,11 @@ MUTANTS = [
     ("encode drops carry", "        r = ldexp(1.0, mant);\n        E += 1;", "        r = ldexp(1.0, mant + 1) - 1;"),
     ("all -inf row gives NaN", "y[j] = has_nan ? NAN : 0.0;", "y[j] = NAN;"),
     ("NaN ignored", "y[j] = has_nan ? NAN : 0.0;", "y[j] = 0.0;"),
+    ("bwd wrong sign", "dx[j] = y[j] * (dy[j] - d);", "dx[j] = y[j] * (d - dy[j]);"),
+    ("bwd drops a dot term", "for (int64_t j = 0; j < n; ++j) d += y[j] * dy[j];",
+     "for (int64_t j = 1; j < n; ++j) d += y[j] * dy[j];"),
+    ("bwd scales by dy", "dx[j] = y[j] * (dy[j] - d);", "dx[j] = dy[j] * (dy[j] - d);"),
+    ("bwd dy stride", "db + (size_t)(r * dy_stride)", "db + (size_t)(r * y_stride)"),
 ]
 
 
@@ -132,7 +137,25 @@ def pin_battery(orc: "oracle.Oracle"):
         y = orc.softmax_f64(x, "f32")
         return np.all(y[0] == 0.0) and np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
 
-    for name, fn in [("brute force", brute), ("f16 decode", f16_decode), ("bf16 decode", bf16_decode),
+    def bwd_torch():
+        x = rng.standard_normal((4, 40)) * 2
+        ys = _stored(torch.softmax(torch.from_numpy(x), -1).numpy(), "f32")
+        g = _stored(rng.standard_normal((4, 40)), "f32")
+        dx = orc.softmax_bwd_f64(ys, g, "f32")
+        want = torch._softmax_backward_data(torch.from_numpy(g.astype(np.float64)),
+                                            torch.from_numpy(ys.astype(np.float64)), -1,
+                                            torch.float64).numpy()
+        return np.allclose(dx, want, rtol=1e-12, atol=1e-15)
+
+    def bwd_strided():
+        yb = _stored(rng.random((6, 50)), "f32")
+        gb = _stored(rng.standard_normal((6, 60)), "f32")
+        return np.array_equal(orc.softmax_bwd_f64(yb[:, :40], gb[:, 5:45], "f32"),
+                              orc.softmax_bwd_f64(np.ascontiguousarray(yb[:, :40]),
+                                                  np.ascontiguousarray(gb[:, 5:45]), "f32"))
+
+    for name, fn in [("bwd vs torch", bwd_torch), ("bwd strided", bwd_strided),
+                     ("brute force", brute), ("f16 decode", f16_decode), ("bf16 decode", bf16_decode),
                      ("f16 encode", encode_f16), ("constant rows", constant_rows),
                      ("spikes at the ends", spikes_first_last), ("strided view", strided),
                      ("row sums", row_sums), ("masked rows", masked)]:

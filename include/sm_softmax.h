@@ -122,7 +122,9 @@ typedef struct sm_plan_info {
     int launches;          /* 1, or 2 for WIDE */
     int same_phase;        /* input and output rows share their 16-byte phase */
     int64_t workspace_bytes; /* WIDE scratch: M * waves_per_row * 8 bytes */
-    int64_t model_bytes;   /* algorithmic bytes: 2*M*N*elem one-pass, 3*M*N*elem WIDE */
+    int64_t model_bytes;   /* algorithmic bytes: 2*M*N*elem one-pass, 3*M*N*elem WIDE
+                              (backward: 3*M*N*elem one-pass, 5*M*N*elem WIDE) */
+    int dy_same_phase;     /* backward: dy rows share y's 16-byte phase (vector loads) */
 } sm_plan_info;
 
 /*
@@ -165,6 +167,39 @@ int sm_softmax_fwd_ex(const void *in, void *out, int64_t M, int64_t N, int64_t i
 int sm_softmax_plan_query(const void *in, const void *out, int64_t M, int64_t N,
                           int64_t in_stride, int64_t out_stride, int dtype,
                           const sm_softmax_opts *opts, int num_cus, sm_plan_info *info);
+
+/*
+ * Softmax backward: dx = y * (dy - sum_j y_j * dy_j) per row, where y is the
+ * softmax output saved by the forward call and dy the gradient of the loss with
+ * respect to y ("Measured optimization case studies", section "Training:
+ * backward kernels through autograd"). FP32 dot product (compensated, with exact
+ * products, for FP32 data), one rounding of dx to the storage dtype.
+ *   y, dy, dx   : device pointers of one dtype, element-aligned; dx may be y or
+ *                 dy exactly (same pointer and stride: in place); any other
+ *                 overlap of dx with y or dy -> SM_ERR_OVERLAP (y and dy may
+ *                 overlap each other: both are only read)
+ *   strides     : row strides in elements, >= N when M > 1
+ * Plans as for the forward call: one-pass RESIDENT/PERSISTENT for N <= 8192
+ * (3*M*N*elem bytes); WIDE above, in two passes (a partial dot per wave, then
+ * merge and apply: 5*M*N*elem bytes) with stream-ordered scratch of
+ * M * waves_per_row * 8 bytes, or caller workspace through the _ex form.
+ * Returns SM_OK or a negative sm_status; validation as for sm_softmax_fwd.
+ */
+int sm_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
+                   int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
+                   hipStream_t stream);
+
+/* As sm_softmax_bwd with overrides (plan, lanes_per_row, vecs_per_lane in {1, 2, 4},
+ * grid, chunks_per_wave, timing events) and optional caller workspace. */
+int sm_softmax_bwd_ex(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
+                      int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
+                      const sm_softmax_opts *opts, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* The plan sm_softmax_bwd would launch (num_cus as for sm_softmax_plan_query). */
+int sm_softmax_bwd_plan_query(const void *y, const void *dy, const void *dx, int64_t M, int64_t N,
+                              int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
+                              const sm_softmax_opts *opts, int num_cus, sm_plan_info *info);
 
 /* Static text for a status code. */
 const char *sm_softmax_strerror(int status);

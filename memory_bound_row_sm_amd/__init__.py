@@ -18,7 +18,8 @@ __all__ = [
     "SM_PLAN_WIDE", "SmOpts", "SmPlanInfo", "SoftmaxError", "lib", "lib_path",
     "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_strerror",
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
-    "softmax", "plan_for", "EXPORTED_SYMBOLS",
+    "softmax", "plan_for", "EXPORTED_SYMBOLS", "sm_softmax_bwd", "sm_softmax_bwd_ex",
+    "sm_softmax_bwd_plan_query", "softmax_backward", "plan_for_backward",
 ]
 
 SM_F32, SM_F16, SM_BF16 = 0, 1, 2
@@ -29,7 +30,8 @@ STATUS = {0: "SM_OK", -1: "SM_ERR_INVALID", -2: "SM_ERR_DTYPE", -3: "SM_ERR_OVER
           -4: "SM_ERR_HIP", -5: "SM_ERR_NO_DEVICE", -6: "SM_ERR_WORKSPACE", -7: "SM_ERR_PLAN"}
 
 EXPORTED_SYMBOLS = (
-    "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_strerror",
+    "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_bwd",
+    "sm_softmax_bwd_ex", "sm_softmax_bwd_plan_query", "sm_softmax_strerror",
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
 )
 
@@ -51,7 +53,8 @@ class SmPlanInfo(ctypes.Structure):
                 ("nt_loads", ctypes.c_int), ("block", ctypes.c_int), ("grid", ctypes.c_int64),
                 ("chunks_per_wave", ctypes.c_int), ("waves_per_row", ctypes.c_int64),
                 ("launches", ctypes.c_int), ("same_phase", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_int64), ("model_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("model_bytes", ctypes.c_int64),
+                ("dy_same_phase", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}
@@ -93,6 +96,12 @@ def lib() -> ctypes.CDLL:
                                         vp, ctypes.c_size_t, vp]
         L.sm_softmax_plan_query.argtypes = [vp, vp, i64, i64, i64, i64, ci,
                                             ctypes.POINTER(SmOpts), ci, ctypes.POINTER(SmPlanInfo)]
+        L.sm_softmax_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ci, vp]
+        L.sm_softmax_bwd_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ci,
+                                        ctypes.POINTER(SmOpts), vp, ctypes.c_size_t, vp]
+        L.sm_softmax_bwd_plan_query.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ci,
+                                                ctypes.POINTER(SmOpts), ci,
+                                                ctypes.POINTER(SmPlanInfo)]
         L.sm_softmax_strerror.argtypes = [ci]
         L.sm_softmax_strerror.restype = ctypes.c_char_p
         L.sm_softmax_version.argtypes = []
@@ -100,6 +109,7 @@ def lib() -> ctypes.CDLL:
         L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, vp, vp, vp]
         L.sm_bench_flush.argtypes = [vp, ctypes.c_size_t, vp]
         for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
+                  L.sm_softmax_bwd, L.sm_softmax_bwd_ex, L.sm_softmax_bwd_plan_query,
                   L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_bench_copy,
                   L.sm_bench_flush):
             f.restype = ci
@@ -142,6 +152,34 @@ def sm_softmax_plan_query(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: 
     rc = lib().sm_softmax_plan_query(in_ptr, out_ptr, M, N, in_stride, out_stride, dtype,
                                      ctypes.byref(o) if o is not None else None, num_cus,
                                      ctypes.byref(info))
+    return rc, info
+
+
+def sm_softmax_bwd(y_ptr: int, dy_ptr: int, dx_ptr: int, M: int, N: int, y_stride: int,
+                   dy_stride: int, dx_stride: int, dtype: int, stream: int = 0) -> int:
+    return lib().sm_softmax_bwd(y_ptr, dy_ptr, dx_ptr, M, N, y_stride, dy_stride, dx_stride,
+                                dtype, stream)
+
+
+def sm_softmax_bwd_ex(y_ptr: int, dy_ptr: int, dx_ptr: int, M: int, N: int, y_stride: int,
+                      dy_stride: int, dx_stride: int, dtype: int, opts=None, workspace: int = 0,
+                      workspace_bytes: int = 0, stream: int = 0) -> int:
+    o = _opts(opts)
+    return lib().sm_softmax_bwd_ex(y_ptr, dy_ptr, dx_ptr, M, N, y_stride, dy_stride, dx_stride,
+                                   dtype, ctypes.byref(o) if o is not None else None,
+                                   workspace or None, workspace_bytes, stream)
+
+
+def sm_softmax_bwd_plan_query(y_ptr: int, dy_ptr: int, dx_ptr: int, M: int, N: int,
+                              y_stride: int, dy_stride: int, dx_stride: int, dtype: int,
+                              opts=None, num_cus: int = 0):
+    """(status, SmPlanInfo)."""
+    o = _opts(opts)
+    info = SmPlanInfo()
+    rc = lib().sm_softmax_bwd_plan_query(y_ptr, dy_ptr, dx_ptr, M, N, y_stride, dy_stride,
+                                         dx_stride, dtype,
+                                         ctypes.byref(o) if o is not None else None, num_cus,
+                                         ctypes.byref(info))
     return rc, info
 
 
@@ -232,4 +270,41 @@ def plan_for(x, out=None, opts=None, num_cus: int = 0) -> dict:
                                      _torch_dtype_code(x), opts, num_cus)
     if rc != 0:
         raise SoftmaxError(rc, "sm_softmax_plan_query")
+    return info.as_dict()
+
+
+def softmax_backward(y, dy, dx=None, opts=None, workspace=None, stream=None):
+    """dx = y * (dy - sum(y * dy)) along the last dimension, for device tensors y (the
+    softmax output) and dy (the gradient with respect to y). Returns ``dx``."""
+    import torch
+    if not (y.is_cuda and dy.is_cuda):
+        raise ValueError("softmax_backward expects device tensors")
+    if y.shape != dy.shape or y.dtype != dy.dtype:
+        raise ValueError("y and dy must match in shape and dtype")
+    if dx is None:
+        dx = torch.empty_like(y, memory_format=torch.contiguous_format)
+    M, N, sy = _rows_view(y)
+    _, _, sd = _rows_view(dy)
+    _, _, sx = _rows_view(dx)
+    s = (stream if stream is not None else torch.cuda.current_stream(y.device)).cuda_stream
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(y.device):
+        rc = sm_softmax_bwd_ex(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, sy, sd, sx,
+                               _torch_dtype_code(y), opts, ws_ptr, ws_bytes, s)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_softmax_bwd_ex")
+    return dx
+
+
+def plan_for_backward(y, dy, dx=None, opts=None, num_cus: int = 0) -> dict:
+    dx = y if dx is None else dx
+    M, N, sy = _rows_view(y)
+    _, _, sd = _rows_view(dy)
+    _, _, sx = _rows_view(dx)
+    rc, info = sm_softmax_bwd_plan_query(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, sy, sd,
+                                         sx, _torch_dtype_code(y), opts, num_cus)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_softmax_bwd_plan_query")
     return info.as_dict()

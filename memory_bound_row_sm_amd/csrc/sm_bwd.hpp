@@ -1,0 +1,267 @@
+// sm_bwd.hpp -- gfx950 kernels of the softmax backward, dx = y * (dy - sum(y * dy)).
+//
+// The softmax keeps its output y and forms dx from it and the upstream gradient
+// dy ("Measured optimization case studies", section "Training: backward kernels
+// through autograd"). Per row that is one dot product and one elementwise pass:
+// 3 * N * elem bytes (read y, read dy, write dx).
+//
+//   k_softmax_bwd_rows<DT, G, V>  one-pass: a group of G lanes holds the row of y
+//       and of dy in registers (the window grid of the forward kernels, taken
+//       from y's 16-byte phase), reduces the dot once (DPP, then one LDS step for
+//       multi-wave rows) and writes dx.
+//   k_bwd_wide_dot<DT> / k_bwd_wide_apply<DT>  rows wider than the one-pass
+//       limit: pass 1 writes one compensated FP32 partial dot per wave, pass 2
+//       merges a row's partials in a fixed order, re-reads y and dy, writes dx.
+//
+// dy may sit at another 16-byte phase than y (then its elements are loaded one
+// by one); dx is stored with 16-byte stores when it shares y's phase.
+#pragma once
+
+#include "sm_kernels.hpp"
+
+namespace smx {
+
+// Decoded elements of dy for the windows of y: vector loads when dy shares y's
+// 16-byte phase, element loads otherwise. Columns outside [0, N) read as 0.
+template <int DT, int NV>
+__device__ __forceinline__ void load_dy(float (&f)[NV][Elem<DT>::per_vec], const unsigned char* dyrow,
+                                        int head, int N, int64_t w0, int wstep, int nwin,
+                                        bool dy_phase) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int ES = Elem<DT>::bytes;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int64_t w = w0 + (int64_t)wstep * v;
+        const int64_t c0 = w * E - head;
+        if (dy_phase) {
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (w < nwin) raw = load16<false>(dyrow - (size_t)head * ES + 16 * (size_t)w);
+            decode<DT>(raw, f[v]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int64_t c = c0 + k;
+                float val = 0.f;
+                if (c >= 0 && c < N) {
+                    const unsigned char* p = dyrow + (size_t)c * ES;
+                    if constexpr (DT == kF32) {
+                        val = *reinterpret_cast<const float*>(p);
+                    } else if constexpr (DT == kBF16) {
+                        val = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
+                    } else {
+                        val = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(p));
+                    }
+                }
+                f[v][k] = val;
+            }
+        }
+    }
+}
+
+// Zero the elements of windows that straddle the row ends (they may hold data of
+// neighbouring rows, including NaN or inf).
+template <int DT, int NV>
+__device__ __forceinline__ void zero_outside(float (&f)[NV][Elem<DT>::per_vec], int head, int N,
+                                             int64_t w0, int wstep) {
+    constexpr int E = Elem<DT>::per_vec;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int64_t c0 = (w0 + (int64_t)wstep * v) * E - head;
+        if (c0 < 0 || c0 + E > N) {
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int64_t c = c0 + k;
+                if (c < 0 || c >= N) f[v][k] = 0.f;
+            }
+        }
+    }
+}
+
+// Row dot product of the lane's elements (compensated with exact products for FP32).
+template <int DT, int NV>
+__device__ __forceinline__ void lane_dot(const float (&fy)[NV][Elem<DT>::per_vec],
+                                         const float (&fd)[NV][Elem<DT>::per_vec], float& acc,
+                                         CSum& cs) {
+    constexpr int E = Elem<DT>::per_vec;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            if constexpr (DT == kF32) {
+                const float p = fy[v][k] * fd[v][k];
+                const float pe = __builtin_fmaf(fy[v][k], fd[v][k], -p);  // exact product error
+                cs.add(p);
+                cs.lo += pe;
+            } else {
+                acc = __builtin_fmaf(fy[v][k], fd[v][k], acc);
+            }
+        }
+    }
+}
+
+// dx for the lane's windows: encode and store (16-byte when fully inside the row
+// and dx shares y's phase, element stores otherwise).
+template <int DT, int NV>
+__device__ __forceinline__ void store_dx(const float (&fy)[NV][Elem<DT>::per_vec],
+                                         const float (&fd)[NV][Elem<DT>::per_vec], float dot,
+                                         unsigned char* dxrow, int head, int N, int64_t w0,
+                                         int wstep, int nwin, bool dx_phase) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int ES = Elem<DT>::bytes;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int64_t w = w0 + (int64_t)wstep * v;
+        if (w < nwin) {
+            float o[E];
+#pragma unroll
+            for (int k = 0; k < E; ++k) o[k] = fy[v][k] * (fd[v][k] - dot);
+            const uint4 enc = encode<DT>(o);
+            const int64_t c0 = w * E - head;
+            if (dx_phase && c0 >= 0 && c0 + E <= N) {
+                store16(dxrow + (size_t)c0 * ES, enc);
+            } else {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const int64_t c = c0 + k;
+                    if (c >= 0 && c < N) store_elem<DT>(dxrow + (size_t)c * ES, enc, k);
+                }
+            }
+        }
+    }
+}
+
+template <int DT, int G, int V>
+__global__ void __launch_bounds__(RowLaunch<G>::block)
+k_softmax_bwd_rows(const unsigned char* y, const unsigned char* dy, unsigned char* dx, int64_t M,
+                   int N, int64_t y_sb, int64_t dy_sb, int64_t dx_sb, int dy_phase, int dx_phase) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int GPB = RowLaunch<G>::groups;
+    constexpr int NW = G > 64 ? G / 64 : 1;
+    // Two LDS buffers, alternating by row: with one barrier per row, a wave that
+    // runs ahead to the next row never overwrites values a slower wave still reads.
+    __shared__ float lds_hi[2][NW], lds_lo[2][NW];
+
+    const int tid = threadIdx.x;
+    const int lane = (GPB == 1) ? tid : (tid % G);
+    const int grp = (GPB == 1) ? 0 : (tid / G);
+    const int64_t rstep = (int64_t)gridDim.x * GPB;
+    int parity = 0;
+    for (int64_t row = (int64_t)blockIdx.x * GPB + grp; row < M; row += rstep, parity ^= 1) {
+        const RowGeom<DT> g(y + row * y_sb, N);
+        float fy[V][E], fd[V][E];
+        {
+            uint4 raw[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int w = lane + G * v;
+                raw[v] = make_uint4(0u, 0u, 0u, 0u);
+                if (w < g.nwin) raw[v] = load16<false>(g.base + 16 * (size_t)w);
+            }
+            load_dy<DT, V>(fd, dy + row * dy_sb, g.head, N, lane, G, g.nwin, dy_phase);
+#pragma unroll
+            for (int v = 0; v < V; ++v) decode<DT>(raw[v], fy[v]);
+        }
+        if (g.head != 0 || (N % E) != 0) {
+            zero_outside<DT, V>(fy, g.head, N, lane, G);
+            zero_outside<DT, V>(fd, g.head, N, lane, G);
+        }
+        float acc = 0.f;
+        CSum cs;
+        lane_dot<DT, V>(fy, fd, acc, cs);
+        float dot;
+        if constexpr (DT == kF32) {
+            dot = row_sum_acc<G>(cs, lds_hi[parity], lds_lo[parity]);
+        } else {
+            dot = row_sum<G>(acc, lds_hi[parity]);
+        }
+        store_dx<DT, V>(fy, fd, dot, dx + row * dx_sb, g.head, N, lane, G, g.nwin, dx_phase);
+    }
+}
+
+// ------------------------------------------------------------ wide rows
+template <int DT>
+__global__ void __launch_bounds__(256)
+k_bwd_wide_dot(const unsigned char* y, const unsigned char* dy, float2* part, int64_t M, int N,
+               int64_t y_sb, int64_t dy_sb, int cpw, int64_t wpr, int dy_phase) {
+    constexpr int VPL = Wide<DT>::VPL;
+    constexpr int WPC = Wide<DT>::WPC;
+    constexpr int E = Elem<DT>::per_vec;
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= M * wpr) return;  // whole waves only
+    const int64_t row = gw / wpr;
+    const int64_t wr = gw - row * wpr;
+    const RowGeom<DT> g(y + row * y_sb, N);
+    const int64_t nchunks = ((int64_t)g.nwin + WPC - 1) / WPC;
+    const int64_t c_end = wr * cpw + cpw < nchunks ? wr * cpw + cpw : nchunks;
+    float acc = 0.f;
+    CSum cs;
+    for (int64_t c = wr * cpw; c < c_end; ++c) {
+        const int64_t w0 = c * WPC + lane;
+        float fy[VPL][E], fd[VPL][E];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int64_t w = w0 + 64 * v;
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (w < g.nwin) raw = load16<false>(g.base + 16 * (size_t)w);
+            decode<DT>(raw, fy[v]);
+        }
+        load_dy<DT, VPL>(fd, dy + row * dy_sb, g.head, N, w0, 64, g.nwin, dy_phase);
+        if (g.head != 0 || (N % E) != 0) {
+            zero_outside<DT, VPL>(fy, g.head, N, w0, 64);
+            zero_outside<DT, VPL>(fd, g.head, N, w0, 64);
+        }
+        lane_dot<DT, VPL>(fy, fd, acc, cs);
+    }
+    if constexpr (DT != kF32) {
+        cs.hi = acc;
+        cs.lo = 0.f;
+    }
+    cs = group_allreduce_csum<64>(cs);
+    if (lane == 0) part[gw] = make_float2(cs.hi, cs.lo);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256)
+k_bwd_wide_apply(const unsigned char* y, const unsigned char* dy, unsigned char* dx,
+                 const float2* part, int64_t M, int N, int64_t y_sb, int64_t dy_sb, int64_t dx_sb,
+                 int cpw, int64_t wpr, int dy_phase, int dx_phase) {
+    constexpr int VPL = Wide<DT>::VPL;
+    constexpr int WPC = Wide<DT>::WPC;
+    constexpr int E = Elem<DT>::per_vec;
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= M * wpr) return;
+    const int64_t row = gw / wpr;
+    const int64_t wr = gw - row * wpr;
+    // the row's partial dots in a fixed order: lane-strided, then the wave tree
+    CSum cs;
+    for (int64_t k = lane; k < wpr; k += 64) {
+        const float2 p = part[row * wpr + k];
+        float s, e;
+        two_sum(cs.hi, p.x, s, e);
+        cs.hi = s;
+        cs.lo = (cs.lo + p.y) + e;
+    }
+    cs = group_allreduce_csum<64>(cs);
+    const float dot = cs.hi + cs.lo;
+
+    const RowGeom<DT> g(y + row * y_sb, N);
+    const int64_t nchunks = ((int64_t)g.nwin + WPC - 1) / WPC;
+    const int64_t c_end = wr * cpw + cpw < nchunks ? wr * cpw + cpw : nchunks;
+    for (int64_t c = wr * cpw; c < c_end; ++c) {
+        const int64_t w0 = c * WPC + lane;
+        float fy[VPL][E], fd[VPL][E];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int64_t w = w0 + 64 * v;
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (w < g.nwin) raw = load16<false>(g.base + 16 * (size_t)w);
+            decode<DT>(raw, fy[v]);
+        }
+        load_dy<DT, VPL>(fd, dy + row * dy_sb, g.head, N, w0, 64, g.nwin, dy_phase);
+        store_dx<DT, VPL>(fy, fd, dot, dx + row * dx_sb, g.head, N, w0, 64, g.nwin, dx_phase);
+    }
+}
+
+}  // namespace smx

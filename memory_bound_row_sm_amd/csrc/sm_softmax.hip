@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "sm_bench.h"
+#include "sm_bwd.hpp"
 #include "sm_kernels.hpp"
 #include "sm_launch.hpp"
 #include "sm_softmax.h"
@@ -149,10 +150,16 @@ bool pick_shape(const RowShape (&tab)[K], int64_t nw, int fixG, int fixV, int& G
             return true;
         }
     }
-    if (fixG && !fixV) {  // a fixed G outside the table: smallest V that fits
+    if (fixG && fixV) {  // both fixed: any built shape that covers the row
+        if ((int64_t)fixG * fixV < nw) return false;
+        G = fixG;
+        V = fixV;
+        return true;
+    }
+    if (fixG) {  // a fixed G outside the table: smallest V that fits
         for (int v : {1, 2, 4, 8})
             if ((int64_t)fixG * v >= nw) { G = fixG; V = v; return true; }
-    } else if (fixV && !fixG) {
+    } else if (fixV) {
         for (int g : {16, 32, 64, 128, 256, 512, 1024})
             if ((int64_t)g * fixV >= nw) { G = g; V = fixV; return true; }
     }
@@ -432,6 +439,159 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     return rc;
 }
 
+// ------------------------------------------------------------ backward
+struct BwdProblem {
+    uintptr_t y, dy, dx;
+    int64_t M, N, y_stride, dy_stride, dx_stride;
+    int dtype;
+};
+
+int validate_bwd(const BwdProblem& p) {
+    if (p.dtype != SM_F32 && p.dtype != SM_F16 && p.dtype != SM_BF16) return SM_ERR_DTYPE;
+    if (p.M < 0 || p.N < 0) return SM_ERR_INVALID;
+    if (p.M == 0 || p.N == 0) return SM_OK;
+    if (!p.y || !p.dy || !p.dx) return SM_ERR_INVALID;
+    // each (input, dx) pair obeys the forward rules: sizes, strides, alignment,
+    // spans, and no overlap other than exactly in place
+    int rc = validate(Problem{p.y, p.dx, p.M, p.N, p.y_stride, p.dx_stride, p.dtype});
+    if (rc != SM_OK) return rc;
+    return validate(Problem{p.dy, p.dx, p.M, p.N, p.dy_stride, p.dx_stride, p.dtype});
+}
+
+// Backward row shapes: y and dy both live in registers, so at most 4 vectors per lane.
+constexpr RowShape kShapesBwd[] = {{16, 1},  {32, 1},  {64, 1},  {64, 2},   {128, 2},
+                                   {256, 2}, {256, 4}, {512, 4}, {1024, 4}};
+
+int occ_bwd_live(int dtype, int G, int V) {
+    BwdRowKernelFn fn = bwd_row_kernel(dtype, G, V);
+    return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
+}
+
+int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool live,
+                  sm_plan_info* pi) {
+    *pi = sm_plan_info{};
+    const int es = elem_bytes(p.dtype);
+    const int E = 16 / es;
+    const bool y_aligned = (p.y % 16 == 0) && (p.M == 1 || (p.y_stride * es) % 16 == 0);
+    const int64_t nw_max = ((y_aligned ? 0 : E - 1) + p.N + E - 1) / E;
+    auto phase = [&](uintptr_t a, int64_t sa) {
+        return ((p.y - a) % 16 == 0) && (p.M == 1 || (((p.y_stride - sa) * es) % 16 == 0));
+    };
+    pi->same_phase = phase(p.dx, p.dx_stride);
+    pi->dy_same_phase = phase(p.dy, p.dy_stride);
+    if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
+    int plan = o.plan;
+    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_WIDE) return SM_ERR_PLAN;
+    const bool auto_plan = plan == SM_PLAN_AUTO;
+    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_WIDE;
+    if (plan == SM_PLAN_WIDE) {
+        const int WPC = kChunk / E;
+        const int64_t nchunks = (nw_max + WPC - 1) / WPC;
+        int64_t cpw = o.chunks_per_wave;
+        if (cpw <= 0) {
+            const int64_t target = (int64_t)cus * 32;
+            cpw = std::max<int64_t>(1, (p.M * nchunks + target - 1) / target);
+        }
+        cpw = std::min<int64_t>(cpw, nchunks);
+        if (cpw > INT32_MAX) return SM_ERR_PLAN;
+        const int64_t wpr = (nchunks + cpw - 1) / cpw;
+        if (p.M > INT64_MAX / wpr) return SM_ERR_PLAN;
+        const int64_t waves = p.M * wpr;
+        const int64_t grid = (waves + 3) / 4;
+        if (grid * 256 > kMaxThreadsPerLaunch) return SM_ERR_PLAN;
+        pi->plan = SM_PLAN_WIDE;
+        pi->block = 256;
+        pi->grid = grid;
+        pi->chunks_per_wave = (int)cpw;
+        pi->waves_per_row = wpr;
+        pi->launches = 2;
+        pi->workspace_bytes = ((waves * 8 + 255) / 256) * 256;
+        pi->model_bytes = 5 * p.M * p.N * es;
+        return SM_OK;
+    }
+    int G = 0, V = 0;
+    if (!pick_shape(kShapesBwd, nw_max, o.lanes_per_row, o.vecs_per_lane, G, V)) return SM_ERR_PLAN;
+    if (!bwd_row_kernel(p.dtype, G, V) || (int64_t)G * V < nw_max) return SM_ERR_PLAN;
+    const int block = row_block(G);
+    const int gpb = block / G;
+    const int64_t groups = (p.M + gpb - 1) / gpb;
+    const int occ = live ? std::max(1, occ_bwd_live(p.dtype, G, V)) : std::max(1, 2048 / block);
+    const int64_t slots = (int64_t)occ * cus;
+    if (auto_plan && groups <= 2 * slots) plan = SM_PLAN_PERSISTENT;
+    int64_t grid = o.grid > 0 ? o.grid : (plan == SM_PLAN_PERSISTENT ? slots : groups);
+    grid = std::max<int64_t>(1, std::min<int64_t>(std::min(grid, groups),
+                                                  kMaxThreadsPerLaunch / block));
+    pi->plan = plan;
+    pi->lanes_per_row = G;
+    pi->vecs_per_lane = V;
+    pi->block = block;
+    pi->grid = grid;
+    pi->launches = 1;
+    pi->model_bytes = 3 * p.M * p.N * es;
+    return SM_OK;
+}
+
+int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, hipEvent_t ev0,
+               hipEvent_t ev1, hipStream_t stream) {
+    const int es = elem_bytes(p.dtype);
+    const auto* y = reinterpret_cast<const unsigned char*>(p.y);
+    const auto* dy = reinterpret_cast<const unsigned char*>(p.dy);
+    auto* dx = reinterpret_cast<unsigned char*>(p.dx);
+    const int64_t ysb = p.y_stride * es, dysb = p.dy_stride * es, dxsb = p.dx_stride * es;
+    const int N = (int)p.N;
+    hipError_t e;
+    if (pi.plan == SM_PLAN_WIDE) {
+        auto* part = reinterpret_cast<float2*>(ws);
+        const int cpw = pi.chunks_per_wave;
+        const int64_t wpr = pi.waves_per_row;
+        e = launch_k(reinterpret_cast<const void*>(bwd_dot_kernel(p.dtype)), dim3((unsigned)pi.grid),
+                     dim3(256), stream, ev0, nullptr, y, dy, part, p.M, N, ysb, dysb, cpw, wpr,
+                     (int)pi.dy_same_phase);
+        if (e != hipSuccess) return hip_fail(e);
+        e = launch_k(reinterpret_cast<const void*>(bwd_apply_kernel(p.dtype)),
+                     dim3((unsigned)pi.grid), dim3(256), stream, nullptr, ev1, y, dy, dx,
+                     (const float2*)part, p.M, N, ysb, dysb, dxsb, cpw, wpr, (int)pi.dy_same_phase,
+                     (int)pi.same_phase);
+        return e == hipSuccess ? SM_OK : hip_fail(e);
+    }
+    BwdRowKernelFn fn = bwd_row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane);
+    if (!fn) return SM_ERR_PLAN;
+    e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(pi.block), stream,
+                 ev0, ev1, y, dy, dx, p.M, N, ysb, dysb, dxsb, (int)pi.dy_same_phase,
+                 (int)pi.same_phase);
+    return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+int run_bwd(const BwdProblem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes,
+            hipStream_t stream) {
+    int rc = validate_bwd(p);
+    if (rc != SM_OK || p.M == 0 || p.N == 0) return rc;
+    DeviceView dv;
+    rc = live_device(&dv);
+    if (rc != SM_OK) return rc;
+    const sm_softmax_opts o = opts_or_default(opts);
+    sm_plan_info pi;
+    rc = make_plan_bwd(p, o, dv.cus, true, &pi);
+    if (rc != SM_OK) return rc;
+    if (pi.plan != SM_PLAN_WIDE) return launch_bwd(p, pi, nullptr, o.start_event, o.stop_event, stream);
+    if (ws) {
+        if (ws_bytes < (size_t)pi.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
+            return SM_ERR_WORKSPACE;
+        return launch_bwd(p, pi, ws, o.start_event, o.stop_event, stream);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    keep_pool_memory(dev);
+    void* tmp = nullptr;
+    e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = launch_bwd(p, pi, tmp, o.start_event, o.stop_event, stream);
+    e = hipFreeAsync(tmp, stream);
+    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
+    return rc;
+}
+
 }  // namespace
 }  // namespace smx
 
@@ -477,6 +637,45 @@ int sm_softmax_plan_query(const void* in, const void* out, int64_t M, int64_t N,
         if (rc != SM_OK) return rc;
     }
     return make_plan(p, opts_or_default(opts), dv, info);
+}
+
+int sm_softmax_bwd(const void* y, const void* dy, void* dx, int64_t M, int64_t N,
+                   int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
+                   hipStream_t stream) {
+    const BwdProblem p{reinterpret_cast<uintptr_t>(y), reinterpret_cast<uintptr_t>(dy),
+                       reinterpret_cast<uintptr_t>(dx), M, N, y_stride, dy_stride, dx_stride, dtype};
+    return run_bwd(p, nullptr, nullptr, 0, stream);
+}
+
+int sm_softmax_bwd_ex(const void* y, const void* dy, void* dx, int64_t M, int64_t N,
+                      int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
+                      const sm_softmax_opts* opts, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    const BwdProblem p{reinterpret_cast<uintptr_t>(y), reinterpret_cast<uintptr_t>(dy),
+                       reinterpret_cast<uintptr_t>(dx), M, N, y_stride, dy_stride, dx_stride, dtype};
+    return run_bwd(p, opts, workspace, workspace_bytes, stream);
+}
+
+int sm_softmax_bwd_plan_query(const void* y, const void* dy, const void* dx, int64_t M, int64_t N,
+                              int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
+                              const sm_softmax_opts* opts, int num_cus, sm_plan_info* info) {
+    if (!info) return SM_ERR_INVALID;
+    const BwdProblem p{reinterpret_cast<uintptr_t>(y), reinterpret_cast<uintptr_t>(dy),
+                       reinterpret_cast<uintptr_t>(dx), M, N, y_stride, dy_stride, dx_stride, dtype};
+    int rc = validate_bwd(p);
+    if (rc != SM_OK) return rc;
+    if (M == 0 || N == 0) {
+        *info = sm_plan_info{};
+        return SM_OK;
+    }
+    int cus = num_cus;
+    if (cus <= 0) {
+        DeviceView dv;
+        rc = live_device(&dv);
+        if (rc != SM_OK) return rc;
+        cus = dv.cus;
+    }
+    return make_plan_bwd(p, opts_or_default(opts), cus, num_cus <= 0, info);
 }
 
 const char* sm_softmax_strerror(int status) {

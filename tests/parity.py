@@ -76,3 +76,48 @@ def row_sum_bound(dt: str) -> float:
     tolerance of "Measured optimization case studies", section "CUDA: parallel
     reduction, online statistics and a numerical fix")."""
     return {"bf16": 2.0 ** -8 + 1e-5, "f16": 2.0 ** -11 + 1e-5, "f32": 2e-5}[dt]
+
+
+# ------------------------------------------------------------------ backward
+# dx = y * (dy - d), d = sum_k y_k dy_k. Both sides read the same stored y and dy;
+# the GPU forms d in FP32 and rounds dx once, the oracle works in FP64. The pages
+# give no backward tolerance, so it is derived from that arithmetic. Error scale
+# per element: s_j = |y_j| (|dy_j| + sum_k |y_k dy_k|) >= |dx_j|. An FP32 dot over
+# a lane's V*E elements and a log2(G)-deep tree is off by at most about
+# (V*E + log2 G) * 2^-24 * sum|y dy| (< 3e-6 s_j for every one-pass shape; the
+# compensated FP32 dot far less), so 1e-4 s_j bounds the FP32 error with margin
+# while a wrong sign, index or term (an error of order s_j) still fails.
+#   FP16/BF16: |g - r| <= u |r| + 1e-4 s_j + a
+#       r: the oracle rounded once to the dtype; u = 2^-10 (FP16) / 2^-7 (BF16), one
+#       unit in the last place relative to |r|: the FP32 value may sit on the other
+#       side of a rounding boundary; a: the dtype's subnormal spacing.
+#   FP32:      |g - dx| <= 1e-6 (|dx| + s_j) + 2^-126   (dx: the FP64 result)
+TOL_BWD = {"f32": (1e-6, 1e-6, 2.0 ** -126), "f16": (2.0 ** -10, 1e-4, 2.0 ** -24),
+           "bf16": (2.0 ** -7, 1e-4, 2.0 ** -133)}
+
+
+def compare_bwd(g: torch.Tensor, y: torch.Tensor, dy: torch.Tensor, rows=None,
+                what: str = "") -> dict:
+    dt = workloads.dtype_name(y)
+    ys, ds = workloads.storage_numpy(y), workloads.storage_numpy(dy)
+    dx, dxr = oracle.reference_bwd(ys, ds, dt, rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    yd = oracle.decode(np.ascontiguousarray(ys)[sel], dt)
+    dd = oracle.decode(np.ascontiguousarray(ds)[sel], dt)
+    s = np.abs(yd) * (np.abs(dd) + np.abs(yd * dd).sum(axis=1, keepdims=True))
+    gd = to_f64(g)
+    ref = dx if dt == "f32" else oracle.decode(dxr, dt)
+    rt, sc, at = TOL_BWD[dt]
+    nan_ref, nan_g = np.isnan(ref), np.isnan(gd)
+    assert np.array_equal(nan_ref, nan_g), f"{what}: NaN pattern differs ({nan_ref.sum()} vs {nan_g.sum()})"
+    ok = ~nan_ref
+    err = np.abs(gd[ok] - ref[ok])
+    bound = rt * np.abs(ref[ok]) + sc * s[ok] + at
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(ok)[np.argmax(err - bound)]
+        i, j = int(idx[0]), int(idx[1])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst at "
+                             f"({i},{j}): gpu={gd[i, j]!r} ref={ref[i, j]!r} scale={s[i, j]!r}")
+    return {"max_abs": float(err.max()) if err.size else 0.0,
+            "worst_frac_of_tol": float(np.max(err / bound)) if err.size else 0.0, "n": int(err.size)}

@@ -181,3 +181,42 @@ def test_plan_phase_flag():
     assert p["same_phase"] == 0
     rc, p = plan(4, 60, F16, si=64, so=72)
     assert p["same_phase"] == 1
+
+
+# ------------------------------------------------------------------ backward entry points
+
+@pytest.mark.parametrize("args,want", [
+    ((BASE, BASE * 2, BASE * 3, 4, 8, 8, 8, 8, 9), DTYPE),
+    ((BASE, BASE * 2, 0, 4, 8, 8, 8, 8, F32), INVALID),            # null dx
+    ((BASE, BASE * 2, BASE * 3, 4, 8, 8, 7, 8, F32), INVALID),     # dy stride < N
+    ((BASE, BASE * 2, BASE + 16, 4, 8, 8, 8, 8, F32), OVERLAP),    # dx overlaps y partially
+    ((BASE, BASE * 2, BASE * 2 + 4, 4, 8, 8, 8, 8, F32), OVERLAP), # dx overlaps dy partially
+    ((BASE, BASE, BASE * 3, 0, 8, 8, 8, 8, F32), OK),              # M == 0
+])
+def test_backward_validation(args, want):
+    assert sm.sm_softmax_bwd(*args, 0) == want
+    assert sm.sm_softmax_bwd_ex(*args, None, 0, 0, 0) == want
+
+
+def test_backward_in_place_passes_validation():
+    for y, dy, dx in [(BASE, BASE * 2, BASE), (BASE, BASE * 2, BASE * 2), (BASE, BASE, BASE * 3)]:
+        rc = sm.sm_softmax_bwd(y, dy, dx, 4, 8, 8, 8, 8, F32, 0)
+        assert rc in (OK, NO_DEVICE), rc
+
+
+def test_backward_plan_rule():
+    def q(M, N, dt, opts=None, dy=BASE * 2, sd=None):
+        rc, info = sm.sm_softmax_bwd_plan_query(BASE, dy, BASE * 3, M, N, N, sd or N, N, dt,
+                                                opts, 256)
+        return rc, info.as_dict()
+    rc, p = q(4096, 4096, BF16)
+    assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 2)
+    assert p["model_bytes"] == 3 * 4096 * 4096 * 2 and p["plan_name"] == "persistent"
+    assert p["dy_same_phase"] == 1 and p["same_phase"] == 1
+    rc, p = q(64, 131072, BF16)
+    assert p["plan_name"] == "wide" and p["model_bytes"] == 5 * 64 * 131072 * 2
+    assert p["workspace_bytes"] == 64 * p["waves_per_row"] * 8
+    rc, p = q(8, 1000, F16, dy=BASE * 2 + 2)
+    assert p["dy_same_phase"] == 0
+    rc, p = q(8, 1000, F16, {"vecs_per_lane": 8})
+    assert rc == PLAN  # backward rows hold at most 4 vectors per lane

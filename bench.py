@@ -1,8 +1,8 @@
 """Bench: cold BF16 4096 x 4096 row softmax on one MI355X through the C ABI.
 
 One step is one cold call of ``sm_softmax_fwd`` over the seeded 4096 x 4096 BF16
-matrix (x ~ N(0, 2^2), seed 2026), after a 1 GiB read-modify-write sweep that
-evicts the input from L2 and MALL. The sweep runs outside the timed events.
+matrix (x ~ N(0, 2^2), seed 2026), after a 1 GiB read-only sweep that evicts the
+input from L2 and MALL. The sweep runs outside the timed events.
 
 Protocol (the pages' methodology, restated):
   * a correctness gate before any timing (Warpline README, the correctness
@@ -21,8 +21,12 @@ Protocol (the pages' methodology, restated):
   * the FP64 oracle timed on this host's cores on the same input (a baseline,
     not the target).
 
-Prints ONE JSON line on stdout. ``--sweep`` also times every workload and plan and
-writes those lines to stderr.
+The softmax backward (dx = y * (dy - sum(y * dy)), byte model 3 * M * N * elem, or
+5 * M * N * elem on the two-pass wide path) is timed the same way on the same shape,
+with y the forward's output and a seeded dy, and reported beside the headline.
+
+Prints ONE JSON line on stdout. ``--sweep`` also times every workload and plan,
+forward and backward, and writes those lines to stderr.
 """
 from __future__ import annotations
 
@@ -43,10 +47,11 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
 FLUSH_BYTES = 1 << 30
 WORKLOAD = "normal_bf16_4096x4096"
-KERNEL_SOURCES = ["include/sm_softmax.h", "memory_bound_row_sm_amd/csrc/sm_device.hpp",
+# device code of the one-pass row kernels: a traffic record stays valid while these
+# are unchanged and the plan still launches the recorded instance
+KERNEL_SOURCES = ["memory_bound_row_sm_amd/csrc/sm_device.hpp",
                   "memory_bound_row_sm_amd/csrc/sm_kernels.hpp",
-                  "memory_bound_row_sm_amd/csrc/sm_rows_inst.inl",
-                  "memory_bound_row_sm_amd/csrc/sm_softmax.hip"]
+                  "memory_bound_row_sm_amd/csrc/sm_rows_inst.inl"]
 
 
 def byte_model(M: int, N: int, elem_bytes: int, wide: bool = False) -> int:
@@ -71,15 +76,23 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, launch_bytes: int):
+def row_kernel_name(dt_code: int, info: dict) -> str:
+    """The demangled name (without arguments) of the row-kernel instance a plan launches."""
+    b = lambda v: "true" if v else "false"
+    return (f"smx::k_softmax_rows<{dt_code}, {info['lanes_per_row']}, {info['vecs_per_lane']}, "
+            f"{b(info['prefetch'])}, {b(info['nt_loads'])}>")
+
+
+def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources (else None)."""
+    taken on the current kernel sources and for the instance the plan launches (else
+    None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha() or t.get("kernel") != kernel:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -151,6 +164,10 @@ def main(argv=None) -> int:
                     help="per-kernel mean of each rocprofv3 --pmc counter (per dispatch) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing on the host")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from the two rocprofv3 --pmc "
+                         "CSVs (FETCH_SIZE run, WRITE_SIZE run) of this bench, and exit")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
@@ -158,6 +175,9 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return 0
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic), indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -293,6 +313,11 @@ def main(argv=None) -> int:
         f"{gbps:.0f} GB/s ({100 * gbps / PEAK_GBPS:.1f}% of 8 TB/s); copy ceiling {copy_gbps:.0f} GB/s"
         + (f"; warm median {warm['median_us']:.2f} us" if warm else ""))
 
+    # ---------------------------------------------------------------- backward, same shape, cold
+    bwd = None
+    if not args.no_backward:
+        bwd = bench_backward(torch, sm, workloads, out, flush, s_handle, args.steps, args.warmup, log)
+
     # ---------------------------------------------------------------- sweep (stderr)
     if args.sweep:
         sweep(torch, sm, workloads, flush, s_handle, log, args)
@@ -304,7 +329,7 @@ def main(argv=None) -> int:
         if not parity.get("passed"):
             log(f"[bench] oracle parity FAILED: {parity}")
 
-    traffic = load_traffic(WORKLOAD, model_bytes)
+    traffic = load_traffic(WORKLOAD, row_kernel_name(dt_code, info))
     result = {
         "metric": "achieved HBM GB/s (and % of MI355X peak) for cold BF16 softmax, 4096x4096",
         "value": round(gbps, 1),
@@ -336,6 +361,7 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(result), flush=True)
     return 0 if parity.get("passed") is not False else 1
@@ -344,7 +370,7 @@ def main(argv=None) -> int:
 def summarize_trace(path: str) -> str:
     """Per kernel: dispatch count and mean/median/min duration of the dispatches that
     follow a cache sweep (cold) and of the others (warm), from a rocprofv3
-    kernel-trace CSV."""
+    kernel-trace CSV. Only this library's kernels are listed."""
     import csv
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
     groups = {}
@@ -353,9 +379,11 @@ def summarize_trace(path: str) -> str:
         name = r["Kernel_Name"]
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
         lane = "cold" if "sweep" in prev else "warm"
+        prev = name
+        if "smx::" not in name:  # torch's own set-up kernels
+            continue
         key = (name.split("(")[0].replace("void ", ""), r["Grid_Size_X"], r["Workgroup_Size_X"], lane)
         groups.setdefault(key, []).append(dur)
-        prev = name
     lines = [f"{'kernel':48s} {'grid(items)':>11s} {'wg':>5s} {'lane':5s} {'calls':>6s} "
              f"{'mean_us':>9s} {'median_us':>9s} {'min_us':>8s}"]
     for (k, g, w, lane), v in sorted(groups.items()):
@@ -378,6 +406,48 @@ def summarize_counters(path: str) -> dict:
         out[k] = {c: round(statistics.mean(v), 3) for c, v in d.items()}
         out[k]["dispatches"] = max(len(v) for v in d.values())
     return out
+
+
+def record_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """Build the HBM-traffic record of the headline kernel from the FETCH_SIZE and
+    WRITE_SIZE counter runs of this bench. The 16-byte copy kernel in the same runs
+    moves a known number of bytes; its counts give the scale of each counter."""
+    f, w = summarize_counters(fetch_csv), summarize_counters(write_csv)
+    soft = [k for k in f if "k_softmax_rows" in k]
+    if len(soft) != 1 or "smx::k_copy16" not in f:
+        raise RuntimeError(f"expected one softmax row kernel and the copy kernel, found {sorted(f)}")
+    k = soft[0]
+    M, N, es = 4096, 4096, 2
+    copy_bytes = M * N * es  # the copy moves the model's bytes: half read, half written
+    ff = (copy_bytes / 1024) / f["smx::k_copy16"]["FETCH_SIZE"]
+    wf = (copy_bytes / 1024) / w["smx::k_copy16"]["WRITE_SIZE"]
+    fetch = f[k]["FETCH_SIZE"] * ff * 1024
+    write = w[k]["WRITE_SIZE"] * wf * 1024
+    alg = byte_model(M, N, es)
+    rec = {"workload": WORKLOAD, "kernel": k, "kernel_source_sha": kernel_source_sha(),
+           "algorithmic_bytes_per_launch": alg,
+           "fetch_size_kib_raw": f[k]["FETCH_SIZE"], "write_size_kib_raw": w[k]["WRITE_SIZE"],
+           "dispatches": {"fetch": f[k]["dispatches"], "write": w[k]["dispatches"]},
+           "calibration": {"copy_kernel": f"smx::k_copy16 moving {copy_bytes >> 20} MiB in and "
+                                          f"{copy_bytes >> 20} MiB out",
+                           "copy_fetch_size_kib_raw": f["smx::k_copy16"]["FETCH_SIZE"],
+                           "copy_write_size_kib_raw": w["smx::k_copy16"]["WRITE_SIZE"],
+                           "fetch_factor": round(ff, 5), "write_factor": round(wf, 5)},
+           "hbm_fetch_bytes_per_launch": int(round(fetch)),
+           "hbm_write_bytes_per_launch": int(round(write)),
+           "hbm_bytes_per_launch": int(round(fetch + write)),
+           "traffic_over_algorithmic": round((fetch + write) / alg, 5),
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+               "python3 -u bench.py --steps 20 --warmup 2 --no-warm --no-cpu-baseline --no-backward",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+               "python3 -u bench.py --steps 20 --warmup 2 --no-warm --no-cpu-baseline --no-backward",
+               "python bench.py --record-traffic gpurun_out/pmc_fetch/fetch_counter_collection.csv "
+               "gpurun_out/pmc_write/write_counter_collection.csv"]}
+    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
 
 
 def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
@@ -461,8 +531,69 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
                     "median_us": round(st["median_us"], 3), "GBps": round(gb, 1),
                     "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
             log("[sweep] " + json.dumps(line))
-        del x, out
+        sm.softmax(x, out)
+        dy = workloads.upstream_grad(x.shape, workloads.dtype_name(x), device="cuda")
+        for pname, p in plans.items():
+            if p in (1, 2) and N > 8192:
+                continue
+            st, info = time_backward(torch, sm, out, dy, p, flush, s_handle, steps, 5)
+            gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
+            line = {"workload": name, "op": "backward", "plan": pname, "resolved": info["plan_name"],
+                    "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
+                    "cpw": info["chunks_per_wave"], "grid": info["grid"],
+                    "model_bytes": info["model_bytes"], "mean_us": round(st["mean_us"], 3),
+                    "median_us": round(st["median_us"], 3), "GBps": round(gb, 1),
+                    "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
+            log("[sweep] " + json.dumps(line))
+        del x, out, dy
         torch.cuda.empty_cache()
+
+
+def time_backward(torch, sm, y, dy, plan, flush, s_handle, steps, warmup):
+    """Cold timing of sm_softmax_bwd_ex (dx in a buffer of its own) under ``plan``."""
+    dx = torch.empty_like(y)
+    M, N = y.shape
+    o = sm.SmOpts()
+    o.plan = plan
+    info = sm.plan_for_backward(y, dy, dx, {"plan": plan})
+    dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[y.dtype]
+
+    def call(events=(None, None)):
+        o.start_event, o.stop_event = events
+        rc = sm.sm_softmax_bwd_ex(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, y.stride(0),
+                                  dy.stride(0), dx.stride(0), dt, o, 0, 0, s_handle)
+        if rc != 0:
+            raise sm.SoftmaxError(rc, "sm_softmax_bwd_ex")
+
+    for _ in range(warmup):
+        flush()
+        call()
+    t = DispatchEvents(steps)
+    for _ in range(steps):
+        flush()
+        call(t.next_pair())
+    st = stats_us(t.samples_ms(torch))
+    t.close()
+    # property of every correct dx: each row sums to d * (1 - sum(y)), about 0
+    rs = dx.float().sum(dim=1).abs().max().item()
+    info["max_abs_row_sum"] = rs
+    return st, info
+
+
+def bench_backward(torch, sm, workloads, y, flush, s_handle, steps, warmup, log):
+    dy = workloads.upstream_grad(y.shape, workloads.dtype_name(y), device="cuda")
+    st, info = time_backward(torch, sm, y, dy, 0, flush, s_handle, steps, warmup)
+    gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
+    res = {"op": "softmax backward dx = y*(dy - sum(y*dy))", "plan": info["plan_name"],
+           "lanes_per_row": info["lanes_per_row"], "vecs_per_lane": info["vecs_per_lane"],
+           "grid": info["grid"], "model_bytes": info["model_bytes"],
+           "cold_mean_us": round(st["mean_us"], 3), "cold_median_us": round(st["median_us"], 3),
+           "GBps": round(gb, 1), "pct_of_peak": round(100 * gb / PEAK_GBPS, 2),
+           "max_abs_row_sum": info["max_abs_row_sum"]}
+    log(f"[bench] backward: {res}")
+    if not info["max_abs_row_sum"] < 0.05:
+        raise RuntimeError(f"backward rows do not sum to about 0: {info['max_abs_row_sum']}")
+    return res
 
 
 if __name__ == "__main__":

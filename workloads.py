@@ -140,6 +140,14 @@ def generate(name: str) -> torch.Tensor:
     raise KeyError(name)
 
 
+def upstream_grad(shape, dtype: str, seed: int = 7, device="cpu") -> torch.Tensor:
+    """A seeded upstream gradient dy ~ N(0, 1) of ``shape``, rounded to ``dtype``, drawn
+    by torch's generator on ``device`` (the backward's second input; a GPU generator
+    makes the multi-GiB shapes without a host round trip)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(_TORCH[dtype])
+
+
 def storage_numpy(t: torch.Tensor) -> np.ndarray:
     """A CPU tensor's stored elements as numpy: float32, or the raw uint16 patterns of
     FP16/BF16 (a view, no conversion). Row-strided views stay views."""

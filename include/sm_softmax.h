@@ -190,7 +190,9 @@ int sm_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N
                    hipStream_t stream);
 
 /* As sm_softmax_bwd with overrides (plan, lanes_per_row, vecs_per_lane in {1, 2, 4},
- * grid, chunks_per_wave, timing events) and optional caller workspace. */
+ * grid, chunks_per_wave, nontemporal (one-pass rows of 128 to 1024 lanes), timing
+ * events) and optional caller workspace. Automatic one-pass plans launch one
+ * workgroup per row group (RESIDENT); PERSISTENT is available when forced. */
 int sm_softmax_bwd_ex(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
                       int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
                       const sm_softmax_opts *opts, void *workspace, size_t workspace_bytes,

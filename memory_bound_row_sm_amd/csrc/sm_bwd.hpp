@@ -130,7 +130,80 @@ __device__ __forceinline__ void store_dx(const float (&fy)[NV][Elem<DT>::per_vec
     }
 }
 
-template <int DT, int G, int V>
+// Raw (still encoded) windows of dy for the windows of y: 16-byte loads when dy
+// shares y's 16-byte phase, element loads packed into words otherwise. Columns
+// outside [0, N) read as 0.
+template <int DT, int NV, bool NT>
+__device__ __forceinline__ void load_dy_raw(uint32_t (&r)[NV][4], const unsigned char* dyrow,
+                                            int head, int N, int64_t w0, int wstep, int nwin,
+                                            bool dy_phase) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int ES = Elem<DT>::bytes;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int64_t w = w0 + (int64_t)wstep * v;
+        if (dy_phase) {
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (w < nwin) raw = load16<NT>(dyrow - (size_t)head * ES + 16 * (size_t)w);
+            r[v][0] = raw.x;
+            r[v][1] = raw.y;
+            r[v][2] = raw.z;
+            r[v][3] = raw.w;
+        } else {
+            const int64_t c0 = w * E - head;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[v][i] = 0u;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int64_t c = c0 + k;
+                if (c >= 0 && c < N) {
+                    const unsigned char* p = dyrow + (size_t)c * ES;
+                    if constexpr (DT == kF32) {
+                        r[v][k] = *reinterpret_cast<const uint32_t*>(p);
+                    } else {
+                        const uint32_t h = *reinterpret_cast<const uint16_t*>(p);
+                        r[v][k >> 1] |= (k & 1) ? (h << 16) : h;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Zero the encoded elements of windows that straddle the row ends (they may hold
+// data of neighbouring rows, including NaN or inf); +0 is the all-zero pattern.
+template <int DT, int NV>
+__device__ __forceinline__ void zero_raw_outside(uint32_t (&r)[NV][4], int head, int N, int64_t w0,
+                                                 int wstep) {
+    constexpr int E = Elem<DT>::per_vec;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int64_t c0 = (w0 + (int64_t)wstep * v) * E - head;
+        if (c0 < 0 || c0 + E > N) {
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int64_t c = c0 + k;
+                if (c < 0 || c >= N) {
+                    if constexpr (DT == kF32) {
+                        r[v][k] = 0u;
+                    } else {
+                        r[v][k >> 1] &= (k & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void decode_words(const uint32_t (&w)[4], float (&f)[Elem<DT>::per_vec]) {
+    decode<DT>(make_uint4(w[0], w[1], w[2], w[3]), f);
+}
+
+// One-pass backward. y and dy stay in registers in their stored encoding (half
+// the registers of decoded FP32 for 16-bit types, so wide rows keep full
+// occupancy) and are decoded twice: for the dot and for dx.
+template <int DT, int G, int V, bool NT>
 __global__ void __launch_bounds__(RowLaunch<G>::block)
 k_softmax_bwd_rows(const unsigned char* y, const unsigned char* dy, unsigned char* dx, int64_t M,
                    int N, int64_t y_sb, int64_t dy_sb, int64_t dx_sb, int dy_phase, int dx_phase) {
@@ -148,33 +221,54 @@ k_softmax_bwd_rows(const unsigned char* y, const unsigned char* dy, unsigned cha
     int parity = 0;
     for (int64_t row = (int64_t)blockIdx.x * GPB + grp; row < M; row += rstep, parity ^= 1) {
         const RowGeom<DT> g(y + row * y_sb, N);
-        float fy[V][E], fd[V][E];
-        {
-            uint4 raw[V];
+        uint32_t ry[V][4], rd[V][4];
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int w = lane + G * v;
-                raw[v] = make_uint4(0u, 0u, 0u, 0u);
-                if (w < g.nwin) raw[v] = load16<false>(g.base + 16 * (size_t)w);
-            }
-            load_dy<DT, V>(fd, dy + row * dy_sb, g.head, N, lane, G, g.nwin, dy_phase);
-#pragma unroll
-            for (int v = 0; v < V; ++v) decode<DT>(raw[v], fy[v]);
+        for (int v = 0; v < V; ++v) {
+            const int w = lane + G * v;
+            uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+            if (w < g.nwin) raw = load16<NT>(g.base + 16 * (size_t)w);
+            ry[v][0] = raw.x;
+            ry[v][1] = raw.y;
+            ry[v][2] = raw.z;
+            ry[v][3] = raw.w;
         }
+        load_dy_raw<DT, V, NT>(rd, dy + row * dy_sb, g.head, N, lane, G, g.nwin, dy_phase);
         if (g.head != 0 || (N % E) != 0) {
-            zero_outside<DT, V>(fy, g.head, N, lane, G);
-            zero_outside<DT, V>(fd, g.head, N, lane, G);
+            zero_raw_outside<DT, V>(ry, g.head, N, lane, G);
+            zero_raw_outside<DT, V>(rd, g.head, N, lane, G);
         }
         float acc = 0.f;
         CSum cs;
-        lane_dot<DT, V>(fy, fd, acc, cs);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float fy[1][E], fd[1][E];
+            decode_words<DT>(ry[v], fy[0]);
+            decode_words<DT>(rd[v], fd[0]);
+            lane_dot<DT, 1>(fy, fd, acc, cs);
+        }
         float dot;
         if constexpr (DT == kF32) {
             dot = row_sum_acc<G>(cs, lds_hi[parity], lds_lo[parity]);
         } else {
             dot = row_sum<G>(acc, lds_hi[parity]);
         }
-        store_dx<DT, V>(fy, fd, dot, dx + row * dx_sb, g.head, N, lane, G, g.nwin, dx_phase);
+        unsigned char* dxrow = dx + row * dx_sb;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int64_t w = lane + (int64_t)G * v;
+            if (w < g.nwin) {
+                if constexpr (DT != kF32) {
+                    // decode again rather than keep the decoded values live across
+                    // the reduction (the empty asm hides that the words are unchanged)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ry[v][i]), "+v"(rd[v][i]));
+                }
+                float fy[1][E], fd[1][E];
+                decode_words<DT>(ry[v], fy[0]);
+                decode_words<DT>(rd[v], fd[0]);
+                store_dx<DT, 1>(fy, fd, dot, dxrow, g.head, N, w, 0, g.nwin, dx_phase);
+            }
+        }
     }
 }
 

@@ -39,7 +39,7 @@ using BwdDotKernelFn = void (*)(const unsigned char*, const unsigned char*, floa
 using BwdApplyKernelFn = void (*)(const unsigned char*, const unsigned char*, unsigned char*,
                                   const float2*, int64_t, int, int64_t, int64_t, int64_t, int,
                                   int64_t, int, int);
-BwdRowKernelFn bwd_row_kernel(int dtype, int G, int V);
+BwdRowKernelFn bwd_row_kernel(int dtype, int G, int V, int NT);
 BwdDotKernelFn bwd_dot_kernel(int dtype);
 BwdApplyKernelFn bwd_apply_kernel(int dtype);
 

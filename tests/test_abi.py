@@ -211,8 +211,13 @@ def test_backward_plan_rule():
         return rc, info.as_dict()
     rc, p = q(4096, 4096, BF16)
     assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 2)
-    assert p["model_bytes"] == 3 * 4096 * 4096 * 2 and p["plan_name"] == "persistent"
+    assert p["model_bytes"] == 3 * 4096 * 4096 * 2 and p["plan_name"] == "resident"
+    assert p["grid"] == 4096 and p["nt_loads"] == 0
     assert p["dy_same_phase"] == 1 and p["same_phase"] == 1
+    rc, p = q(524288, 2048, BF16)  # 6 GiB moved: streaming loads
+    assert rc == OK and p["plan_name"] == "resident" and p["nt_loads"] == 1
+    rc, p = q(4096, 4096, BF16, {"plan": 2})
+    assert p["plan_name"] == "persistent" and p["grid"] < 4096
     rc, p = q(64, 131072, BF16)
     assert p["plan_name"] == "wide" and p["model_bytes"] == 5 * 64 * 131072 * 2
     assert p["workspace_bytes"] == 64 * p["waves_per_row"] * 8

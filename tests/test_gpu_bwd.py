@@ -113,11 +113,16 @@ def test_every_instance(dt):
             if G * V < 126:
                 continue
             for plan in ("resident", "persistent"):
-                g = run_bwd(yd, dyd, plan, lanes_per_row=G, vecs_per_lane=V, grid=5)
-                compare_bwd(g, yv.contiguous(), dv.contiguous(), what=f"bwd {dt} G={G} V={V} {plan}")
-                n += 1
+                for nt in ((-1, 1) if G >= 128 else (-1,)):
+                    info = sm.plan_for_backward(yd, dyd, opts={"plan": PLANS[plan], "lanes_per_row": G,
+                                                               "vecs_per_lane": V, "nontemporal": nt})
+                    assert info["nt_loads"] == (1 if nt == 1 else 0)
+                    g = run_bwd(yd, dyd, plan, lanes_per_row=G, vecs_per_lane=V, grid=5, nontemporal=nt)
+                    compare_bwd(g, yv.contiguous(), dv.contiguous(),
+                                what=f"bwd {dt} G={G} V={V} {plan} nt={nt}")
+                    n += 1
     log(f"[bwd] {dt}: {n} instances")
-    assert n >= 30
+    assert n >= 50
 
 
 def test_forward_backward_chain_on_device():

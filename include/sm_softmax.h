@@ -76,7 +76,21 @@ typedef enum sm_status {
  *                 optimization case studies", section "Wide rows: loop in one
  *                 program, or split across programs"; Warpline README, the
  *                 description of its online path).
- * AUTO takes WIDE for N > 8192. Otherwise it holds the row in the narrowest
+ *   SPLIT      -- rows too wide to hold in one workgroup, in one launch: a row
+ *                 is cut into P slices of 256 * V 16-byte windows, one 256-lane
+ *                 workgroup holds a slice in registers, publishes its slice's
+ *                 (max, sum) pair, waits (bounded) for the row's other slices,
+ *                 merges the P pairs in a fixed order and writes its slice.
+ *                 Each element is read once and written once. The grid is a
+ *                 multiple of P and at most half of the resident capacity
+ *                 (further rows are taken in rounds), so a row's slices are
+ *                 resident together unless the device is filled by other
+ *                 work; more than two SPLIT calls running at once on different
+ *                 streams of one device can exceed it. A wait that exceeds
+ *                 spin_limit polls writes NaN over its slice and is counted
+ *                 (sm_softmax_sync_failures), so every call ends.
+ * AUTO takes SPLIT for N > 8192 when a row's slices fit the resident capacity
+ * (WIDE otherwise). For N <= 8192 it holds the row in the narrowest
  * measured-best group (16 to 1024 lanes, 1 to 8 vectors per lane), and takes
  * PERSISTENT when the row groups fit in at most two rounds of resident
  * workgroups, RESIDENT when there are more. */
@@ -84,21 +98,26 @@ typedef enum sm_plan {
     SM_PLAN_AUTO = 0,
     SM_PLAN_RESIDENT = 1,
     SM_PLAN_PERSISTENT = 2,
-    SM_PLAN_WIDE = 3
+    SM_PLAN_WIDE = 3,
+    SM_PLAN_SPLIT = 4
 } sm_plan;
 
 /* Optional launch overrides (zero-initialise for "automatic"). */
 typedef struct sm_softmax_opts {
     int plan;            /* sm_plan */
     int lanes_per_row;   /* RESIDENT/PERSISTENT: 16, 32, 64, 128, 256, 512 or 1024; 0 = auto */
-    int vecs_per_lane;   /* RESIDENT/PERSISTENT: 16-byte vectors per lane, 1, 2, 4 or 8; 0 = auto */
-    int grid;            /* workgroups to launch; 0 = auto */
+    int vecs_per_lane;   /* RESIDENT/PERSISTENT/SPLIT: 16-byte vectors per lane, 1, 2, 4 or 8
+                            (backward: at most 4); 0 = auto */
+    int grid;            /* workgroups to launch; 0 = auto (SPLIT: a multiple of the
+                            slices per row, at most half the resident capacity) */
     int chunks_per_wave; /* WIDE: 1024-element chunks per wave; 0 = auto */
     int prefetch;        /* PERSISTENT: 1 = load the next row early, -1 = no; 0 = auto */
     int nontemporal;     /* streaming (nontemporal) loads of the input: 1 = yes, -1 = no,
                             0 = auto (yes when the call moves at least 1 GiB, four times the
                             MI355X MALL); one-pass plans have them on 128- to 1024-lane
                             rows without prefetch, the WIDE plan on both passes */
+    int spin_limit;      /* SPLIT: polls a workgroup may spend waiting for the other
+                            slices of a row; 0 = default (2^20, about a second) */
     /* Optional timing events (created by the caller with hipEventCreate), or NULL.
      * They are attached to the kernel dispatches themselves (hipExtLaunchKernel):
      * start_event takes the start time of the call's first kernel and stop_event
@@ -118,12 +137,15 @@ typedef struct sm_plan_info {
     int block;             /* threads per workgroup */
     int64_t grid;          /* workgroups per launch */
     int chunks_per_wave;   /* WIDE only */
-    int64_t waves_per_row; /* WIDE only */
+    int64_t waves_per_row; /* WIDE: waves per row; SPLIT: slices (workgroups) per row */
     int launches;          /* 1, or 2 for WIDE */
     int same_phase;        /* input and output rows share their 16-byte phase */
-    int64_t workspace_bytes; /* WIDE scratch: M * waves_per_row * 8 bytes */
-    int64_t model_bytes;   /* algorithmic bytes: 2*M*N*elem one-pass, 3*M*N*elem WIDE
-                              (backward: 3*M*N*elem one-pass, 5*M*N*elem WIDE) */
+    int64_t workspace_bytes; /* WIDE scratch: M * waves_per_row * 8 bytes;
+                                SPLIT: M * slices per row * 32 bytes (both rounded up
+                                to 256) */
+    int64_t model_bytes;   /* algorithmic bytes: 2*M*N*elem one-pass and SPLIT, 3*M*N*elem
+                              WIDE (backward: 3*M*N*elem one-pass and SPLIT, 5*M*N*elem
+                              WIDE) */
     int dy_same_phase;     /* backward: dy rows share y's 16-byte phase (vector loads) */
 } sm_plan_info;
 
@@ -136,9 +158,11 @@ typedef struct sm_plan_info {
  *   in_stride,
  *   out_stride  : row strides in elements, >= N when M > 1
  *   dtype       : sm_dtype of both tensors
- * The WIDE plan takes its scratch stream-ordered from the device's default
- * memory pool (hipMallocAsync / hipFreeAsync on `stream`), so concurrent calls
- * on different streams never share scratch.
+ * The WIDE and SPLIT plans take their scratch stream-ordered from the device's
+ * default memory pool (hipMallocAsync / hipFreeAsync on `stream`), so
+ * concurrent calls on different streams never share scratch. The first SPLIT
+ * call on a stream also allocates that stream's failure counter (hipMalloc +
+ * hipMemset of 256 bytes, kept until the process ends).
  * Returns SM_OK or a negative sm_status.
  */
 int sm_softmax_fwd(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,
@@ -148,7 +172,7 @@ int sm_softmax_fwd(const void *in, void *out, int64_t M, int64_t N, int64_t in_s
  * As sm_softmax_fwd, with launch overrides and optional caller scratch.
  *   opts        : NULL = automatic
  *   workspace   : device memory of at least plan_info.workspace_bytes, 16-byte
- *                 aligned, used only by the WIDE plan; NULL = allocate
+ *                 aligned, used only by the WIDE and SPLIT plans; NULL = allocate
  *                 stream-ordered as sm_softmax_fwd does. The caller must not
  *                 reuse it until the call's work on `stream` has finished.
  */
@@ -211,6 +235,14 @@ int sm_softmax_version(void);
 
 /* The hipError_t of the most recent SM_ERR_HIP on the calling thread (0 if none). */
 int sm_softmax_last_hip_error(void);
+
+/*
+ * SPLIT-plan waits that ran out of polls on `stream` since its counter was
+ * created (each wrote NaN over one row slice). Synchronises `stream`, then
+ * reads the count into *count (0 if no SPLIT call ran on that stream).
+ * Returns SM_OK, SM_ERR_INVALID for a NULL count, or SM_ERR_HIP.
+ */
+int sm_softmax_sync_failures(hipStream_t stream, unsigned int *count);
 
 #ifdef __cplusplus
 }

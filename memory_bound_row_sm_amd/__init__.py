@@ -15,24 +15,26 @@ import os
 
 __all__ = [
     "SM_F32", "SM_F16", "SM_BF16", "SM_PLAN_AUTO", "SM_PLAN_RESIDENT", "SM_PLAN_PERSISTENT",
-    "SM_PLAN_WIDE", "SmOpts", "SmPlanInfo", "SoftmaxError", "lib", "lib_path",
+    "SM_PLAN_WIDE", "SM_PLAN_SPLIT", "SmOpts", "SmPlanInfo", "SoftmaxError", "lib", "lib_path",
     "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_strerror",
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
     "softmax", "plan_for", "EXPORTED_SYMBOLS", "sm_softmax_bwd", "sm_softmax_bwd_ex",
     "sm_softmax_bwd_plan_query", "softmax_backward", "plan_for_backward",
+    "sm_softmax_sync_failures", "sync_failures",
 ]
 
 SM_F32, SM_F16, SM_BF16 = 0, 1, 2
-SM_PLAN_AUTO, SM_PLAN_RESIDENT, SM_PLAN_PERSISTENT, SM_PLAN_WIDE = 0, 1, 2, 3
+SM_PLAN_AUTO, SM_PLAN_RESIDENT, SM_PLAN_PERSISTENT, SM_PLAN_WIDE, SM_PLAN_SPLIT = 0, 1, 2, 3, 4
 PLAN_NAMES = {SM_PLAN_AUTO: "auto", SM_PLAN_RESIDENT: "resident",
-              SM_PLAN_PERSISTENT: "persistent", SM_PLAN_WIDE: "wide"}
+              SM_PLAN_PERSISTENT: "persistent", SM_PLAN_WIDE: "wide", SM_PLAN_SPLIT: "split"}
 STATUS = {0: "SM_OK", -1: "SM_ERR_INVALID", -2: "SM_ERR_DTYPE", -3: "SM_ERR_OVERLAP",
           -4: "SM_ERR_HIP", -5: "SM_ERR_NO_DEVICE", -6: "SM_ERR_WORKSPACE", -7: "SM_ERR_PLAN"}
 
 EXPORTED_SYMBOLS = (
     "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_bwd",
     "sm_softmax_bwd_ex", "sm_softmax_bwd_plan_query", "sm_softmax_strerror",
-    "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
+    "sm_softmax_version", "sm_softmax_last_hip_error", "sm_softmax_sync_failures",
+    "sm_bench_copy", "sm_bench_flush",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +45,7 @@ class SmOpts(ctypes.Structure):
     _fields_ = [("plan", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
                 ("vecs_per_lane", ctypes.c_int), ("grid", ctypes.c_int),
                 ("chunks_per_wave", ctypes.c_int), ("prefetch", ctypes.c_int),
-                ("nontemporal", ctypes.c_int),
+                ("nontemporal", ctypes.c_int), ("spin_limit", ctypes.c_int),
                 ("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p)]
 
 
@@ -106,12 +108,13 @@ def lib() -> ctypes.CDLL:
         L.sm_softmax_strerror.restype = ctypes.c_char_p
         L.sm_softmax_version.argtypes = []
         L.sm_softmax_last_hip_error.argtypes = []
+        L.sm_softmax_sync_failures.argtypes = [vp, ctypes.POINTER(ctypes.c_uint)]
         L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, vp, vp, vp]
         L.sm_bench_flush.argtypes = [vp, ctypes.c_size_t, vp]
         for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
                   L.sm_softmax_bwd, L.sm_softmax_bwd_ex, L.sm_softmax_bwd_plan_query,
-                  L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_bench_copy,
-                  L.sm_bench_flush):
+                  L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_softmax_sync_failures,
+                  L.sm_bench_copy, L.sm_bench_flush):
             f.restype = ci
         _lib = L
     return _lib
@@ -193,6 +196,13 @@ def sm_softmax_version() -> int:
 
 def sm_softmax_last_hip_error() -> int:
     return lib().sm_softmax_last_hip_error()
+
+
+def sm_softmax_sync_failures(stream: int = 0) -> tuple[int, int]:
+    """(status, count): SPLIT waits that ran out of polls on ``stream``."""
+    c = ctypes.c_uint(0)
+    rc = lib().sm_softmax_sync_failures(stream, ctypes.byref(c))
+    return rc, c.value
 
 
 def sm_bench_copy(src: int, dst: int, nbytes: int, grid: int = 0, stream: int = 0,
@@ -308,3 +318,14 @@ def plan_for_backward(y, dy, dx=None, opts=None, num_cus: int = 0) -> dict:
     if rc != 0:
         raise SoftmaxError(rc, "sm_softmax_bwd_plan_query")
     return info.as_dict()
+
+
+def sync_failures(stream=None) -> int:
+    """SPLIT-plan waits that ran out of polls on ``stream`` (torch's current stream
+    by default); synchronises that stream."""
+    import torch
+    s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+    rc, n = sm_softmax_sync_failures(s)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_softmax_sync_failures")
+    return n

@@ -92,7 +92,7 @@ __device__ __forceinline__ float row_sum(float s, float* lds) {
 }
 
 template <int G>
-__device__ __forceinline__ float row_sum_acc(CSum c, float* lds_hi, float* lds_lo) {
+__device__ __forceinline__ CSum row_csum(CSum c, float* lds_hi, float* lds_lo) {
     if constexpr (G <= 64) {
         c = group_allreduce_csum<G>(c);
     } else {
@@ -115,6 +115,12 @@ __device__ __forceinline__ float row_sum_acc(CSum c, float* lds_hi, float* lds_l
         }
         c = r;
     }
+    return c;
+}
+
+template <int G>
+__device__ __forceinline__ float row_sum_acc(CSum c, float* lds_hi, float* lds_lo) {
+    c = row_csum<G>(c, lds_hi, lds_lo);
     return c.hi + c.lo;
 }
 

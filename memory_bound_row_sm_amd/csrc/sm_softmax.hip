@@ -7,6 +7,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <map>
 #include <mutex>
 
@@ -139,6 +141,9 @@ constexpr RowShape kShapesResident[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2}, 
 // (524288 x 2048 BF16, 4 GiB: 639 against 659 us; below 1 GiB streaming loads
 // cost 1-3%).
 constexpr int64_t kNtLoadBytes = int64_t(1) << 30;
+// SPLIT workgroup width (lanes per slice) and default wait budget (polls).
+constexpr int kSplitLanes = 256;
+constexpr int kSplitSpinDefault = 1 << 20;
 
 template <size_t K>
 bool pick_shape(const RowShape (&tab)[K], int64_t nw, int fixG, int fixV, int& G, int& V) {
@@ -177,8 +182,60 @@ struct DeviceView {
     // workgroups per CU for a row-kernel instance / for the wide kernels
     int (*occ_row)(void* ctx, int dtype, int G, int V, int PF);
     int (*occ_wide)(void* ctx, int dtype);
+    // workgroups per CU for a split-kernel instance (bwd: the backward one)
+    int (*occ_split)(void* ctx, int dtype, int V, int bwd);
     void* ctx;
 };
+
+// ------------------------------------------------------------ SPLIT geometry
+// Slices per row P for V vectors per lane, and the grid: at most half of the
+// resident capacity, a multiple of P, so that every row's slices can be resident
+// together (with room to spare for other work on the device). Returns false when
+// even one row's slices exceed that budget, or a forced grid breaks the rules.
+bool split_geometry(int64_t M, int64_t nw, int V, int64_t cap_slots, int64_t fixed_grid,
+                    int64_t& P, int64_t& grid) {
+    const int64_t S = (int64_t)kSplitLanes * V;
+    P = std::max<int64_t>(1, (nw + S - 1) / S);
+    if (P > INT32_MAX || M > INT64_MAX / P) return false;
+    const int64_t cap = (cap_slots / 2) / P * P;
+    if (cap < P) return false;
+    const int64_t items = M * P;
+    if (fixed_grid > 0) {
+        if (fixed_grid % P != 0 || fixed_grid > cap) return false;
+        grid = std::min(fixed_grid, items);
+    } else {
+        grid = std::min(items, cap);
+    }
+    return true;
+}
+
+// Automatic SPLIT shape: the smallest V >= 2 whose rows need at most
+// kSplitMaxAutoSlices slices and whose slices of all rows fit in one round; else
+// the largest V that fits at all (fewest rounds). Returns 0 when no V fits.
+// Measured on MI355X, cold BF16 (us, V = 1 / 2 / 4 / 8): 1 x 1048576: 7.6 / 6.2 /
+// 5.7 / 6.6; 8 x 262144: 5.8 / 5.4 / 5.6 / 6.9; 16 x 65536: 4.6 / 4.5 / 5.1 / 6.4;
+// 64 x 131072: - / 13.8 / 11.3 / 11.1. Very wide slices leave few workgroups in
+// flight; very narrow ones make each workgroup wait on many slots.
+constexpr int64_t kSplitMaxAutoSlices = 128;
+
+int split_auto_v(int64_t M, int64_t nw, int vmax, int64_t cus, void* ctx, int dtype, int bwd,
+                 int (*occ)(void*, int, int, int), int64_t& P, int64_t& grid) {
+    int best = 0;
+    for (int v = 2; v <= vmax; v *= 2) {
+        const int64_t slots = (int64_t)std::max(1, occ(ctx, dtype, v, bwd)) * cus;
+        int64_t p = 0, g = 0;
+        if (!split_geometry(M, nw, v, slots, 0, p, g)) continue;
+        if (M * p <= g && p <= kSplitMaxAutoSlices) {
+            P = p;
+            grid = g;
+            return v;
+        }
+        best = v;
+        P = p;
+        grid = g;
+    }
+    return best;
+}
 
 int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev, sm_plan_info* pi) {
     *pi = sm_plan_info{};
@@ -191,10 +248,43 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
                      (p.M == 1 || (((p.in_stride - p.out_stride) * es) % 16 == 0));
 
     int plan = o.plan;
-    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_WIDE) return SM_ERR_PLAN;
+    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
-    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_WIDE;
+    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
     if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
+
+    if (plan == SM_PLAN_SPLIT) {
+        int64_t P = 0, grid = 0;
+        int V = o.vecs_per_lane;
+        if (V) {
+            if (V != 1 && V != 2 && V != 4 && V != 8) return SM_ERR_PLAN;
+            const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
+            if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
+        } else {
+            V = split_auto_v(p.M, nw_max, 8, dev.cus, dev.ctx, p.dtype, 0, dev.occ_split, P, grid);
+            if (V && o.grid > 0) {
+                const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
+                if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
+            }
+        }
+        if (V) {
+            const int64_t model = 2 * p.M * p.N * es;
+            const bool nt = o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes);
+            pi->plan = SM_PLAN_SPLIT;
+            pi->lanes_per_row = kSplitLanes;
+            pi->vecs_per_lane = V;
+            pi->block = kSplitLanes;
+            pi->grid = grid;
+            pi->waves_per_row = P;
+            pi->launches = 1;
+            pi->nt_loads = nt ? 1 : 0;
+            pi->workspace_bytes = ((p.M * P * 32 + 255) / 256) * 256;
+            pi->model_bytes = model;
+            return SM_OK;
+        }
+        if (!auto_plan) return SM_ERR_PLAN;
+        plan = SM_PLAN_WIDE;  // a row's slices cannot all be resident: two passes
+    }
     const int64_t model = (plan == SM_PLAN_WIDE ? 3 : 2) * p.M * p.N * es;
     const bool want_nt = o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes);
 
@@ -320,8 +410,14 @@ int occ_row_live(void*, int dtype, int G, int V, int PF) {
 int occ_wide_live(void*, int dtype) {
     return occ_of(reinterpret_cast<const void*>(wide_stats_kernel(dtype, 0)), 256);
 }
+int occ_split_live(void*, int dtype, int V, int bwd) {
+    const void* fn = bwd ? reinterpret_cast<const void*>(bwd_split_kernel(dtype, V, 0))
+                         : reinterpret_cast<const void*>(split_kernel(dtype, V, 0));
+    return fn ? occ_of(fn, kSplitLanes) : 1;
+}
 int occ_row_host(void*, int, int G, int, int) { return std::max(1, 2048 / row_block(G)); }
 int occ_wide_host(void*, int) { return 8; }
+int occ_split_host(void*, int, int, int) { return 8; }
 
 int live_device(DeviceView* v) {
     int dev = 0;
@@ -346,6 +442,7 @@ int live_device(DeviceView* v) {
     }
     v->occ_row = occ_row_live;
     v->occ_wide = occ_wide_live;
+    v->occ_split = occ_split_live;
     v->ctx = nullptr;
     return SM_OK;
 }
@@ -353,6 +450,41 @@ int live_device(DeviceView* v) {
 sm_softmax_opts opts_or_default(const sm_softmax_opts* o) {
     sm_softmax_opts d{};
     return o ? *o : d;
+}
+
+// ------------------------------------------------------------ SPLIT synchronisation
+// Per (device, stream) count of timed-out SPLIT waits: device memory zeroed once
+// at creation and kept until the process ends.
+std::mutex g_sync_mu;
+std::map<std::pair<int, uintptr_t>, void*> g_sync;
+
+void* split_sync(hipStream_t stream, bool create, hipError_t* err) {
+    *err = hipSuccess;
+    int dev = 0;
+    if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lk(g_sync_mu);
+    const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(stream));
+    auto it = g_sync.find(key);
+    if (it != g_sync.end()) return it->second;
+    if (!create) return nullptr;
+    void* ptr = nullptr;
+    if ((*err = hipMalloc(&ptr, 256)) != hipSuccess) return nullptr;
+    if ((*err = hipMemset(ptr, 0, 256)) != hipSuccess) {
+        (void)hipFree(ptr);
+        return nullptr;
+    }
+    g_sync[key] = ptr;
+    return ptr;
+}
+
+// Call ids that tag SPLIT slots: never 0, different for every call of the
+// process, starting from a value that differs between processes.
+uint32_t next_tag() {
+    static std::atomic<uint32_t> tag{static_cast<uint32_t>(
+        std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u) | 1u};
+    uint32_t t = tag.fetch_add(1);
+    while (t == 0) t = tag.fetch_add(1);
+    return t;
 }
 
 // ------------------------------------------------------------ launches
@@ -366,14 +498,26 @@ hipError_t launch_k(const void* fn, dim3 grid, dim3 block, hipStream_t s, hipEve
     return hipLaunchKernel(fn, grid, block, argv, 0, s);
 }
 
-int launch(const Problem& p, const sm_plan_info& pi, void* ws, hipEvent_t ev0, hipEvent_t ev1,
+int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_opts& o,
            hipStream_t stream) {
+    const hipEvent_t ev0 = o.start_event, ev1 = o.stop_event;
     const int es = elem_bytes(p.dtype);
     const auto* in = reinterpret_cast<const unsigned char*>(p.in);
     auto* out = reinterpret_cast<unsigned char*>(p.out);
     const int64_t isb = p.in_stride * es, osb = p.out_stride * es;
     const int N = (int)p.N;
     hipError_t e;
+    if (pi.plan == SM_PLAN_SPLIT) {
+        void* sync = split_sync(stream, true, &e);
+        if (!sync) return hip_fail(e);
+        SplitKernelFn fn = split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
+        if (!fn) return SM_ERR_PLAN;
+        const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
+        e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
+                     stream, ev0, ev1, in, out, ws, sync, p.M, N, isb, osb, (int)pi.waves_per_row,
+                     next_tag(), spin, (int)pi.same_phase);
+        return e == hipSuccess ? SM_OK : hip_fail(e);
+    }
     if (pi.plan == SM_PLAN_WIDE) {
         auto* st = reinterpret_cast<float2*>(ws);
         const int cpw = pi.chunks_per_wave;
@@ -419,12 +563,12 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     const sm_softmax_opts o = opts_or_default(opts);
     rc = make_plan(p, o, dv, &pi);
     if (rc != SM_OK) return rc;
-    if (pi.plan != SM_PLAN_WIDE) return launch(p, pi, nullptr, o.start_event, o.stop_event, stream);
+    if (pi.workspace_bytes == 0) return launch(p, pi, nullptr, o, stream);
 
     if (ws) {
         if (ws_bytes < (size_t)pi.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
             return SM_ERR_WORKSPACE;
-        return launch(p, pi, ws, o.start_event, o.stop_event, stream);
+        return launch(p, pi, ws, o, stream);
     }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -433,7 +577,7 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     void* tmp = nullptr;
     e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
     if (e != hipSuccess) return hip_fail(e);
-    rc = launch(p, pi, tmp, o.start_event, o.stop_event, stream);
+    rc = launch(p, pi, tmp, o, stream);
     e = hipFreeAsync(tmp, stream);
     if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
     return rc;
@@ -487,9 +631,42 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
     pi->dy_same_phase = phase(p.dy, p.dy_stride);
     if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
     int plan = o.plan;
-    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_WIDE) return SM_ERR_PLAN;
+    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
-    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_WIDE;
+    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
+    if (plan == SM_PLAN_SPLIT) {
+        auto occ_fn = live ? occ_split_live : occ_split_host;
+        int64_t P = 0, grid = 0;
+        int V = o.vecs_per_lane;
+        if (V) {
+            if (V != 1 && V != 2 && V != 4) return SM_ERR_PLAN;
+            const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 1)) * cus;
+            if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
+        } else {
+            V = split_auto_v(p.M, nw_max, 4, cus, nullptr, p.dtype, 1, occ_fn, P, grid);
+            if (V && o.grid > 0) {
+                const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 1)) * cus;
+                if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
+            }
+        }
+        if (V) {
+            const int64_t model = 3 * p.M * p.N * es;
+            const bool nt = o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes);
+            pi->plan = SM_PLAN_SPLIT;
+            pi->lanes_per_row = kSplitLanes;
+            pi->vecs_per_lane = V;
+            pi->block = kSplitLanes;
+            pi->grid = grid;
+            pi->waves_per_row = P;
+            pi->launches = 1;
+            pi->nt_loads = nt ? 1 : 0;
+            pi->workspace_bytes = ((p.M * P * 32 + 255) / 256) * 256;
+            pi->model_bytes = model;
+            return SM_OK;
+        }
+        if (!auto_plan) return SM_ERR_PLAN;
+        plan = SM_PLAN_WIDE;
+    }
     if (plan == SM_PLAN_WIDE) {
         const int WPC = kChunk / E;
         const int64_t nchunks = (nw_max + WPC - 1) / WPC;
@@ -539,8 +716,9 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
     return SM_OK;
 }
 
-int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, hipEvent_t ev0,
-               hipEvent_t ev1, hipStream_t stream) {
+int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, const sm_softmax_opts& o,
+               hipStream_t stream) {
+    const hipEvent_t ev0 = o.start_event, ev1 = o.stop_event;
     const int es = elem_bytes(p.dtype);
     const auto* y = reinterpret_cast<const unsigned char*>(p.y);
     const auto* dy = reinterpret_cast<const unsigned char*>(p.dy);
@@ -548,6 +726,18 @@ int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, hipEvent_t
     const int64_t ysb = p.y_stride * es, dysb = p.dy_stride * es, dxsb = p.dx_stride * es;
     const int N = (int)p.N;
     hipError_t e;
+    if (pi.plan == SM_PLAN_SPLIT) {
+        void* sync = split_sync(stream, true, &e);
+        if (!sync) return hip_fail(e);
+        BwdSplitKernelFn fn = bwd_split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
+        if (!fn) return SM_ERR_PLAN;
+        const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
+        e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
+                     stream, ev0, ev1, y, dy, dx, ws, sync, p.M, N, ysb, dysb, dxsb,
+                     (int)pi.waves_per_row, next_tag(), spin, (int)pi.dy_same_phase,
+                     (int)pi.same_phase);
+        return e == hipSuccess ? SM_OK : hip_fail(e);
+    }
     if (pi.plan == SM_PLAN_WIDE) {
         auto* part = reinterpret_cast<float2*>(ws);
         const int cpw = pi.chunks_per_wave;
@@ -581,11 +771,11 @@ int run_bwd(const BwdProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
     sm_plan_info pi;
     rc = make_plan_bwd(p, o, dv.cus, true, &pi);
     if (rc != SM_OK) return rc;
-    if (pi.plan != SM_PLAN_WIDE) return launch_bwd(p, pi, nullptr, o.start_event, o.stop_event, stream);
+    if (pi.workspace_bytes == 0) return launch_bwd(p, pi, nullptr, o, stream);
     if (ws) {
         if (ws_bytes < (size_t)pi.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
             return SM_ERR_WORKSPACE;
-        return launch_bwd(p, pi, ws, o.start_event, o.stop_event, stream);
+        return launch_bwd(p, pi, ws, o, stream);
     }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -594,7 +784,7 @@ int run_bwd(const BwdProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
     void* tmp = nullptr;
     e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
     if (e != hipSuccess) return hip_fail(e);
-    rc = launch_bwd(p, pi, tmp, o.start_event, o.stop_event, stream);
+    rc = launch_bwd(p, pi, tmp, o, stream);
     e = hipFreeAsync(tmp, stream);
     if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
     return rc;
@@ -639,6 +829,7 @@ int sm_softmax_plan_query(const void* in, const void* out, int64_t M, int64_t N,
         dv.cus = num_cus;
         dv.occ_row = occ_row_host;
         dv.occ_wide = occ_wide_host;
+        dv.occ_split = occ_split_host;
         dv.ctx = nullptr;
     } else {
         rc = live_device(&dv);
@@ -703,6 +894,21 @@ const char* sm_softmax_strerror(int status) {
 int sm_softmax_version(void) { return SM_SOFTMAX_VERSION; }
 
 int sm_softmax_last_hip_error(void) { return t_last_hip_error; }
+
+int sm_softmax_sync_failures(hipStream_t stream, unsigned int* count) {
+    if (!count) return SM_ERR_INVALID;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    void* sync = split_sync(stream, false, &e);
+    if (e != hipSuccess) return hip_fail(e);
+    *count = 0;
+    if (!sync) return SM_OK;
+    uint32_t v = 0;
+    e = hipMemcpy(&v, sync, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    *count = v;
+    return SM_OK;
+}
 
 int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream,
                   hipEvent_t start_event, hipEvent_t stop_event) {

@@ -131,6 +131,8 @@ def test_nontemporal_option():
     rc, p = plan(524288, 2048, BF16, {"nontemporal": -1})
     assert p["nt_loads"] == 0
     rc, p = plan(64, 131072, BF16, {"nontemporal": 1})
+    assert p["plan_name"] == "split" and p["nt_loads"] == 1
+    rc, p = plan(64, 131072, BF16, {"nontemporal": 1, "plan": sm.SM_PLAN_WIDE})
     assert p["plan_name"] == "wide" and p["nt_loads"] == 1
     for bad in (2, 5, -2):
         rc, p = plan(524288, 2048, BF16, {"nontemporal": bad})
@@ -138,16 +140,51 @@ def test_nontemporal_option():
 
 
 def test_plan_rule_wide():
-    rc, p = plan(64, 131072, BF16)
+    W = {"plan": sm.SM_PLAN_WIDE}
+    rc, p = plan(64, 131072, BF16, W)
     assert rc == OK and p["plan_name"] == "wide"
     assert p["chunks_per_wave"] == 1 and p["waves_per_row"] == 128
     assert p["workspace_bytes"] == 64 * 128 * 8
     assert p["model_bytes"] == 3 * 64 * 131072 * 2
     assert p["launches"] == 2 and p["grid"] == 64 * 128 // 4
-    rc, p = plan(1024, 16384, BF16)  # 16384 chunks over 8192 wave slots -> 2 per wave
+    rc, p = plan(1024, 16384, BF16, W)  # 16384 chunks over 8192 wave slots -> 2 per wave
     assert p["chunks_per_wave"] == 2 and p["waves_per_row"] == 8
-    rc, p = plan(4, 8193, F32)  # just past the resident limit
+    rc, p = plan(4, 8193, F32, W)
     assert p["plan_name"] == "wide" and p["waves_per_row"] == 9
+
+
+def test_plan_rule_split():
+    # host path: 256 CUs x 8 workgroups = 2048 slots, half of them usable (1024)
+    rc, p = plan(64, 131072, BF16)  # 16384 windows; V=4 -> 16 slices, 1024 items: one round
+    assert rc == OK and p["plan_name"] == "split" and p["launches"] == 1
+    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (4, 16, 1024)
+    assert p["workspace_bytes"] == 64 * 16 * 32 and p["model_bytes"] == 2 * 64 * 131072 * 2
+    rc, p = plan(4, 8193, F32)  # just past the one-pass limit: 2049 windows -> 5 slices of 512
+    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 5)
+    assert p["grid"] == 20
+    rc, p = plan(1, 1 << 20, BF16)  # V=2 would need 256 slices per row: V=4, 128 slices
+    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (4, 128, 128)
+    rc, p = plan(8, 1 << 18, BF16)  # V=2: 64 slices, 512 workgroups in one round
+    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (2, 64, 512)
+    rc, p = plan(1024, 16384, BF16)  # V=8 -> one slice per row, 1024 rows: one round
+    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (8, 1, 1024)
+    rc, p = plan(8192, 16384, BF16)  # more rows than slots: V=8, rounds of 1024 rows
+    assert (p["vecs_per_lane"], p["grid"]) == (8, 1024)
+    rc, p = plan(1, 1 << 25, BF16)  # 2^22 windows: even V=8 needs 2048 slices > 1024
+    assert rc == OK and p["plan_name"] == "wide"
+    S = {"plan": sm.SM_PLAN_SPLIT}
+    rc, p = plan(1, 1 << 25, BF16, S)
+    assert rc == PLAN
+    rc, p = plan(64, 131072, BF16, {**S, "vecs_per_lane": 2, "grid": 64})
+    assert rc == OK and (p["waves_per_row"], p["grid"]) == (32, 64)   # 2 rows per round
+    rc, p = plan(64, 131072, BF16, {**S, "vecs_per_lane": 2, "grid": 48})
+    assert rc == PLAN  # not a multiple of the 32 slices per row
+    rc, p = plan(64, 131072, BF16, {**S, "vecs_per_lane": 3})
+    assert rc == PLAN
+    rc, p = plan(100, 3000, BF16, S)  # forced on a narrow row: 375 windows, V=2 -> 1 slice
+    assert rc == OK and p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 1)
+    rc, p = plan(100, 3000, BF16, {**S, "vecs_per_lane": 1})
+    assert rc == OK and p["waves_per_row"] == 2
 
 
 def test_plan_forcing_and_limits():
@@ -219,8 +256,13 @@ def test_backward_plan_rule():
     rc, p = q(4096, 4096, BF16, {"plan": 2})
     assert p["plan_name"] == "persistent" and p["grid"] < 4096
     rc, p = q(64, 131072, BF16)
+    assert p["plan_name"] == "split" and p["model_bytes"] == 3 * 64 * 131072 * 2
+    assert p["workspace_bytes"] == 64 * p["waves_per_row"] * 32 and p["vecs_per_lane"] == 4
+    rc, p = q(64, 131072, BF16, {"plan": sm.SM_PLAN_WIDE})
     assert p["plan_name"] == "wide" and p["model_bytes"] == 5 * 64 * 131072 * 2
     assert p["workspace_bytes"] == 64 * p["waves_per_row"] * 8
+    rc, p = q(64, 131072, BF16, {"plan": sm.SM_PLAN_SPLIT, "vecs_per_lane": 8})
+    assert rc == PLAN  # backward slices hold at most 4 vectors per lane
     rc, p = q(8, 1000, F16, dy=BASE * 2 + 2)
     assert p["dy_same_phase"] == 0
     rc, p = q(8, 1000, F16, {"vecs_per_lane": 8})

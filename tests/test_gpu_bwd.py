@@ -14,7 +14,7 @@ from parity import compare, compare_bwd, log
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-PLANS = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3}
+PLANS = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -47,19 +47,19 @@ def test_widths_all_plans(dt, N):
     M = 21 if N <= 8192 else 4
     y, dy = inputs(M, N, dt, seed=N)
     yd, dyd = y.to(DEV), dy.to(DEV)
-    for plan in ["auto", "resident", "persistent", "wide"]:
-        if plan != "wide" and N > 8192:
+    for plan in ["auto", "resident", "persistent", "wide", "split"]:
+        if plan in ("resident", "persistent") and N > 8192:
             continue
         g = run_bwd(yd, dyd, plan)
         compare_bwd(g, y, dy, what=f"bwd {dt} {M}x{N} {plan}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_phase_shifted_and_strided(dt, plan):
     for N, sy, sd, sx, oy, od, ox in [(100, 103, 100, 100, 1, 0, 3), (1000, 1001, 1003, 1000, 0, 1, 1),
                                       (4097, 4099, 4097, 4101, 3, 0, 0), (9001, 9001, 9005, 9011, 1, 1, 2)]:
-        if plan != "wide" and N > 8192:
+        if plan in ("resident", "persistent") and N > 8192:
             continue
         M = 13
         y, dy = inputs(M, N, dt, seed=N + 1)
@@ -77,10 +77,10 @@ def test_phase_shifted_and_strided(dt, plan):
         assert torch.isnan(bx[ox + M * sx:].float()).all()
 
 
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_in_place(plan):
     for M, N in [(33, 4096), (5, 20000)]:
-        if plan != "wide" and N > 8192:
+        if plan in ("resident", "persistent") and N > 8192:
             continue
         y, dy = inputs(M, N, "bf16", seed=M)
         yd, dyd = y.to(DEV), dy.to(DEV)
@@ -92,7 +92,7 @@ def test_in_place(plan):
 
 
 def test_nan_rows():
-    for plan in ["resident", "wide"]:
+    for plan in ["resident", "wide", "split"]:
         y, dy = inputs(3, 3000, "f32", seed=5)
         dy[1, 17] = math.nan
         g = run_bwd(y.to(DEV), dy.to(DEV), plan).cpu()
@@ -139,16 +139,19 @@ def test_forward_backward_chain_on_device():
     assert float((g.float().cpu() - xt.grad).abs().max()) < 2e-2
 
 
-def test_caller_workspace_and_errors():
+@pytest.mark.parametrize("plan", ["wide", "split"])
+def test_caller_workspace_and_errors(plan):
     y, dy = inputs(6, 30000, "bf16", seed=9)
     yd, dyd = y.to(DEV), dy.to(DEV)
-    info = sm.plan_for_backward(yd, dyd)
-    assert info["plan_name"] == "wide"
+    opts = {"plan": PLANS[plan]}
+    info = sm.plan_for_backward(yd, dyd, opts=opts)
+    assert info["plan_name"] == plan
     ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device=DEV)
-    dx = torch.full_like(yd, float("nan"))
-    sm.softmax_backward(yd, dyd, dx=dx, workspace=ws)
-    torch.cuda.synchronize()
-    compare_bwd(dx, y, dy, what="bwd caller workspace")
+    for _ in range(2):
+        dx = torch.full_like(yd, float("nan"))
+        sm.softmax_backward(yd, dyd, dx=dx, opts=opts, workspace=ws)
+        torch.cuda.synchronize()
+        compare_bwd(dx, y, dy, what=f"bwd caller workspace {plan}")
     with pytest.raises(sm.SoftmaxError) as e:
-        sm.softmax_backward(yd, dyd, dx=dx, workspace=ws[:-16])
+        sm.softmax_backward(yd, dyd, dx=dx, opts=opts, workspace=ws[:-16])
     assert e.value.status == -6

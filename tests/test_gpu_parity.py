@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 PLANS = {"auto": sm.SM_PLAN_AUTO, "resident": sm.SM_PLAN_RESIDENT,
-         "persistent": sm.SM_PLAN_PERSISTENT, "wide": sm.SM_PLAN_WIDE}
+         "persistent": sm.SM_PLAN_PERSISTENT, "wide": sm.SM_PLAN_WIDE, "split": sm.SM_PLAN_SPLIT}
 
 
 def run(x_dev, plan="auto", out=None, **kw):
@@ -65,13 +65,13 @@ def test_workload_full_auto_plan(name):
     assert np.max(np.abs(sums - 1)) <= row_sum_bound(workloads.dtype_name(x))
 
 
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 @pytest.mark.parametrize("name", ["normal_f32_128x781", "normal_bf16_4096x4096",
                                   "spiky_f16_8192x127", "spiky_f16_8192x1000",
                                   "spiky_f16_8192x8192", "offset_bf16_64x131072"])
 def test_workload_forced_plans(name, plan):
     x = workloads.generate(name)
-    if plan != "wide" and x.shape[1] > 8192:
+    if plan in ("resident", "persistent") and x.shape[1] > 8192:
         x = x[:, :32768].contiguous()  # one-pass plans hold at most 1024 x 8 windows per row
     log(f"[parity] {name} plan={plan} shape {tuple(x.shape)}")
     g = run(x.to(DEV), plan)
@@ -128,7 +128,7 @@ def test_width_grid_all_plans(dt, N):
     M = 37 if N <= 8192 else 5
     x = _rand(M, N, dt, seed=N)
     xd = x.to(DEV)
-    for plan in ["auto", "resident", "persistent", "wide"]:
+    for plan in ["auto", "resident", "persistent", "wide", "split"]:
         if plan in ("resident", "persistent") and N > 8192 and dt == "f32" and N > 16384:
             continue
         g = run(xd, plan)
@@ -136,7 +136,7 @@ def test_width_grid_all_plans(dt, N):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_misaligned_strided_and_phase_shifted(dt, plan):
     """Base pointers off by one element, row strides that break 16-byte alignment,
     and an output whose 16-byte phase differs from the input's."""
@@ -149,7 +149,7 @@ def test_misaligned_strided_and_phase_shifted(dt, plan):
         ob = torch.full((M * stride_out + off_out + 8,), float("nan"), dtype=TDT[dt], device=DEV)
         out = ob[off_out:off_out + M * stride_out].view(M, stride_out)[:, :N]
         xd = base.to(DEV)[off_in:off_in + M * stride_in].view(M, stride_in)[:, :N]
-        if plan != "wide" and N > 8192 and dt == "f32":
+        if plan in ("resident", "persistent") and N > 8192 and dt == "f32":
             continue
         run(xd, plan, out=out)
         compare(out, xin.contiguous(), what=f"{dt} {N} si={stride_in} so={stride_out} "
@@ -162,10 +162,10 @@ def test_misaligned_strided_and_phase_shifted(dt, plan):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_in_place(dt, plan):
     for M, N in [(64, 781), (33, 4096), (5, 20000)]:
-        if plan != "wide" and N > 8192:
+        if plan in ("resident", "persistent") and N > 8192:
             continue
         x = _rand(M, N, dt, seed=M)
         xd = x.to(DEV)
@@ -174,7 +174,7 @@ def test_in_place(dt, plan):
 
 
 def test_canaries_around_output():
-    for plan in ["resident", "persistent", "wide"]:
+    for plan in ["resident", "persistent", "wide", "split"]:
         M, N = 19, 3000
         x = _rand(M, N, "bf16", seed=3)
         buf = torch.full((M * N + 256,), -7.0, dtype=torch.bfloat16, device=DEV)
@@ -187,13 +187,13 @@ def test_canaries_around_output():
 # ------------------------------------------------------------------ special values
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_masked_rows_every_plan(dt, plan):
     """-inf entries give exactly 0, fully masked rows give zeros, and masked prefixes
     wider than a chunk stay NaN-free ("Measured optimization case studies", section
     "Wide rows: loop in one program, or split across programs": masked rows on every
     plan)."""
-    N = 12000 if plan == "wide" else 3000
+    N = 12000 if plan in ("wide", "split") else 3000
     x = _rand(6, N, dt, seed=11).float()
     x[0, :] = -math.inf                    # fully masked row
     x[1, : N - 5] = -math.inf              # masked prefix, 5 live entries at the end
@@ -209,7 +209,7 @@ def test_masked_rows_every_plan(dt, plan):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_nan_and_inf_rows(dt, plan):
     x = _rand(4, 2000, dt, seed=12).float()
     x[0, 17] = math.nan
@@ -222,7 +222,7 @@ def test_nan_and_inf_rows(dt, plan):
     compare(g[3:4], x[3:4], what=f"row after NaN rows {dt} {plan}")
 
 
-@pytest.mark.parametrize("plan", ["resident", "persistent", "wide"])
+@pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_extreme_magnitudes(plan):
     # BF16 logits near the top of the FP32 range, and FP16 +/-1e4 spikes
     x = torch.zeros(4, 3000)
@@ -257,7 +257,7 @@ def test_bitwise_repeatable_and_plans_agree():
     a = run(x)
     b = run(x)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    for plan in ["resident", "persistent", "wide"]:
+    for plan in ["resident", "persistent", "wide", "split"]:
         c = run(x, plan)
         d = run(x, plan)
         assert torch.equal(c.view(torch.int16), d.view(torch.int16))
@@ -268,12 +268,14 @@ def test_shift_invariance():
     rng = np.random.default_rng(5)
     xi = rng.integers(-8, 9, size=(64, 1500)).astype(np.float32)
     for dt in ["f32", "bf16"]:
-        a = run(torch.from_numpy(xi).to(TDT[dt]).to(DEV))
-        b = run(torch.from_numpy(xi + 64).to(TDT[dt]).to(DEV))
-        if dt == "f32":  # x - max is exact on this grid: bitwise equal
-            assert torch.equal(a, b)
-        else:
-            assert float((a.float() - b.float()).abs().max()) <= 2.0 ** -8
+        for plan in ["auto", "split"]:  # SPLIT: slice and row maxima shift alike
+            a = run(torch.from_numpy(xi).to(TDT[dt]).to(DEV), plan, vecs_per_lane=1 if plan == "split" else 0)
+            b = run(torch.from_numpy(xi + 64).to(TDT[dt]).to(DEV), plan,
+                    vecs_per_lane=1 if plan == "split" else 0)
+            if dt == "f32":  # x - max is exact on this grid: bitwise equal
+                assert torch.equal(a, b), plan
+            else:
+                assert float((a.float() - b.float()).abs().max()) <= 2.0 ** -8
 
 
 def test_permutation_equivariance():
@@ -296,19 +298,22 @@ def test_zero_sized_and_rejected_calls_launch_nothing():
     assert rc == -7  # 16 lanes x 1 vector cannot hold 100 FP32 elements
 
 
-def test_caller_workspace_for_wide_plan():
+@pytest.mark.parametrize("plan", ["wide", "split"])
+def test_caller_workspace(plan):
     x = _rand(8, 20000, "bf16", seed=4)
     xd = x.to(DEV)
-    info = sm.plan_for(xd)
-    assert info["plan_name"] == "wide"
+    opts = {"plan": PLANS[plan]}
+    info = sm.plan_for(xd, opts=opts)
+    assert info["plan_name"] == plan
     ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device=DEV)
-    out = torch.full_like(xd, float("nan"))
-    sm.softmax(xd, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    compare(out, x, what="caller workspace")
+    for _ in range(3):  # SPLIT reuses the same slots call after call (new tags each time)
+        out = torch.full_like(xd, float("nan"))
+        sm.softmax(xd, out=out, opts=opts, workspace=ws)
+        torch.cuda.synchronize()
+        compare(out, x, what=f"caller workspace {plan}")
     small = torch.empty(info["workspace_bytes"] - 8, dtype=torch.uint8, device=DEV)
     with pytest.raises(sm.SoftmaxError) as e:
-        sm.softmax(xd, out=out, workspace=small)
+        sm.softmax(xd, out=out, opts=opts, workspace=small)
     assert e.value.status == -6
 
 

@@ -1,0 +1,223 @@
+"""GPU tests of the one-launch SPLIT plan (forward and backward): every slice shape,
+rounds (more row slices than the grid), rows whose slices are fully masked, the
+wait budget and its failure count, caller workspace, two streams at once, and the
+bench's wide-row workload at full size. Each result is checked against the FP64
+oracle element by element."""
+import math
+
+import pytest
+import torch
+
+import memory_bound_row_sm_amd as sm
+import workloads
+from parity import compare, compare_bwd, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+SPLIT = sm.SM_PLAN_SPLIT
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    sm.lib()
+
+
+def _rand(M, N, dt, seed, scale=3.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(M, N, generator=g) * scale).to(TDT[dt])
+
+
+def fwd(xd, out=None, **kw):
+    if out is None:
+        out = torch.full_like(xd, float("nan"))
+    sm.softmax(xd, out=out, opts={"plan": SPLIT, **kw})
+    torch.cuda.synchronize()
+    return out
+
+
+def bwd(yd, dyd, dx=None, **kw):
+    if dx is None:
+        dx = torch.full_like(yd, float("nan"))
+    sm.softmax_backward(yd, dyd, dx=dx, opts={"plan": SPLIT, **kw})
+    torch.cuda.synchronize()
+    return dx
+
+
+def test_wide_row_workload_full_size_auto():
+    """64 x 131072 BF16 (per-row offsets U(-50, 50)): the automatic plan is SPLIT."""
+    x = workloads.generate("offset_bf16_64x131072")
+    xd = x.to(DEV)
+    info = sm.plan_for(xd)
+    assert info["plan_name"] == "split" and info["launches"] == 1
+    before = sm.sync_failures()
+    g = torch.full_like(xd, float("nan"))
+    sm.softmax(xd, out=g)
+    st = compare(g, x, what="offset_bf16_64x131072 split")
+    log(f"[split] wide-row workload: plan {info}, {st}")
+    assert sm.sync_failures() == before
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 4, 8])
+def test_every_slice_shape(dt, V):
+    for M, N in [(3, 1), (5, 7), (9, 1000), (4, 8193), (3, 20000), (2, 70001)]:
+        x = _rand(M, N, dt, seed=N + V)
+        for nt in (-1, 1):
+            info = sm.plan_for(x.to(DEV), opts={"plan": SPLIT, "vecs_per_lane": V, "nontemporal": nt})
+            assert info["vecs_per_lane"] == V and info["nt_loads"] == (nt == 1)
+            g = fwd(x.to(DEV), vecs_per_lane=V, nontemporal=nt)
+            compare(g, x, what=f"split {dt} V={V} nt={nt} {M}x{N} P={info['waves_per_row']}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rounds(dt):
+    """A grid of one row's slices: every further row is another round."""
+    M, N = 13, 20000
+    x = _rand(M, N, dt, seed=5)
+    xd = x.to(DEV)
+    for V in (1, 2):
+        P = sm.plan_for(xd, opts={"plan": SPLIT, "vecs_per_lane": V})["waves_per_row"]
+        for grid in (P, 2 * P, 3 * P):
+            info = sm.plan_for(xd, opts={"plan": SPLIT, "vecs_per_lane": V, "grid": grid})
+            assert info["grid"] == grid
+            g = fwd(xd, vecs_per_lane=V, grid=grid)
+            compare(g, x, what=f"rounds {dt} V={V} grid={grid}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_masked_slices(dt):
+    """Slices that are entirely -inf (shift 0, sum 0), a fully masked row, a row whose
+    only live entry sits in the last slice, NaN and +inf confined to one slice."""
+    M, N = 7, 9000
+    x = _rand(M, N, dt, seed=8).float()
+    x[0, :] = -math.inf
+    x[1, : N - 1] = -math.inf
+    x[2, 2048:6144] = -math.inf
+    x[3, 4000] = math.nan
+    x[4, 8999] = math.inf
+    x[5, 1:] = -math.inf
+    x = x.to(TDT[dt])
+    for V in (1, 2):
+        g = fwd(x.to(DEV), vecs_per_lane=V)
+        compare(g, x, what=f"masked slices {dt} V={V}")
+        gc = g.float().cpu()
+        assert (gc[0] == 0).all() and gc[1, -1] == 1 and (gc[1, :-1] == 0).all()
+        assert torch.isnan(gc[3]).all() and torch.isnan(gc[4]).all()
+        assert gc[5, 0] == 1 and (gc[5, 1:] == 0).all()
+
+
+def test_repeatable_and_misaligned():
+    M, N = 11, 30001
+    base = _rand(1, M * (N + 3) + 1, "bf16", seed=2).view(-1)
+    x = base[1:1 + M * (N + 3)].view(M, N + 3)[:, :N]
+    xd = base.to(DEV)[1:1 + M * (N + 3)].view(M, N + 3)[:, :N]
+    ob = torch.full((M * (N + 5) + 2,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = ob[2:2 + M * (N + 5)].view(M, N + 5)[:, :N]
+    fwd(xd, out=out)
+    compare(out, x.contiguous(), what="split misaligned phase-shifted")
+    assert torch.isnan(ob[2:2 + M * (N + 5)].view(M, N + 5)[:, N:].float()).all()
+    a = fwd(xd)
+    b = fwd(xd)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_wait_budget_failures_are_counted():
+    """A wait budget of one poll: slices whose peers are not yet published give up.
+    Each slice is then either correct or all NaN, and the failure count grows by the
+    number of NaN slices. Every kernel drains either way."""
+    M, N = 32, 131072
+    x = _rand(M, N, "bf16", seed=3)
+    xd = x.to(DEV)
+    info = sm.plan_for(xd, opts={"plan": SPLIT, "vecs_per_lane": 1})
+    P, S = info["waves_per_row"], 256 * 8
+    before = sm.sync_failures()
+    g = fwd(xd, vecs_per_lane=1, spin_limit=1)
+    after = sm.sync_failures()
+    gc = g.float().cpu().view(M, P, S)
+    nan_slices = torch.isnan(gc).all(dim=2)
+    partly = torch.isnan(gc).any(dim=2) & ~nan_slices
+    assert not partly.any()
+    assert after - before == int(nan_slices.sum())
+    ok_rows = [i for i in range(M) if not nan_slices[i].any()]
+    if ok_rows:
+        compare(g[ok_rows], x[ok_rows], what="rows without timeouts")
+    log(f"[split] one-poll budget: {int(nan_slices.sum())} of {M * P} slices timed out")
+    # the default budget then works again on the same stream and slots
+    g = fwd(xd, vecs_per_lane=1)
+    compare(g, x, what="after timeouts")
+    assert sm.sync_failures() == after
+
+
+def test_two_streams_at_once():
+    x1 = _rand(64, 65536, "bf16", seed=21)
+    x2 = _rand(48, 40000, "f16", seed=22)
+    d1, d2 = x1.to(DEV), x2.to(DEV)
+    o1, o2 = torch.full_like(d1, float("nan")), torch.full_like(d2, float("nan"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            sm.softmax(d1, out=o1, opts={"plan": SPLIT})
+        with torch.cuda.stream(s2):
+            sm.softmax(d2, out=o2, opts={"plan": SPLIT})
+    torch.cuda.synchronize()
+    compare(o1, x1, what="stream 1")
+    compare(o2, x2, what="stream 2")
+    assert sm.sync_failures(s1) == 0 and sm.sync_failures(s2) == 0
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd_inputs(M, N, dt, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, N, generator=g, dtype=torch.float64) * 3
+    y = torch.softmax(x, -1).to(TDT[dt])
+    dy = torch.randn(M, N, generator=g, dtype=torch.float64).to(TDT[dt])
+    return y, dy
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 4])
+def test_backward_every_slice_shape(dt, V):
+    for M, N in [(3, 1), (9, 1000), (4, 8193), (3, 20000), (2, 70001)]:
+        y, dy = _bwd_inputs(M, N, dt, seed=N + V)
+        for nt in (-1, 1):
+            g = bwd(y.to(DEV), dy.to(DEV), vecs_per_lane=V, nontemporal=nt)
+            compare_bwd(g, y, dy, what=f"bwd split {dt} V={V} nt={nt} {M}x{N}")
+
+
+def test_backward_rounds_phase_and_in_place():
+    M, N = 13, 20000
+    y, dy = _bwd_inputs(M, N, "bf16", seed=4)
+    yd, dyd = y.to(DEV), dy.to(DEV)
+    P = sm.plan_for_backward(yd, dyd, opts={"plan": SPLIT, "vecs_per_lane": 1})["waves_per_row"]
+    g = bwd(yd, dyd, vecs_per_lane=1, grid=P)
+    compare_bwd(g, y, dy, what="bwd split rounds")
+    # dy at another 16-byte phase (element loads), dx at another phase (element stores)
+    db = torch.zeros(M * N + 3, dtype=torch.bfloat16, device=DEV)
+    dv = db[3:].view(M, N)
+    dv.copy_(dyd)
+    xb = torch.full((M * N + 1,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xv = xb[1:].view(M, N)
+    bwd(yd, dv, dx=xv)
+    compare_bwd(xv, y, dy, what="bwd split phases")
+    bwd(yd, dyd, dx=dyd)
+    compare_bwd(dyd, y, dy, what="bwd split in place over dy")
+
+
+def test_backward_wide_row_shape_auto():
+    y = sm.softmax(workloads.generate("offset_bf16_64x131072").to(DEV))
+    dy = workloads.upstream_grad(y.shape, "bf16")
+    info = sm.plan_for_backward(y, dy.to(DEV))
+    assert info["plan_name"] == "split"
+    before = sm.sync_failures()  # cumulative per stream
+    dx = torch.full_like(y, float("nan"))
+    sm.softmax_backward(y, dy.to(DEV), dx=dx)
+    torch.cuda.synchronize()
+    st = compare_bwd(dx, y.cpu(), dy, what="bwd 64x131072 split")
+    log(f"[split] backward wide rows: {st}")
+    assert sm.sync_failures() == before

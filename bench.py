@@ -165,6 +165,15 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing on the host")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--plan-grid", metavar="OUT_JSON",
+                    help="time every plan on the row-plan grid (18 row counts x 10 widths, "
+                         "BF16 forward), write the cell times to OUT_JSON, print the regret "
+                         "summary as one JSON line, and exit")
+    ap.add_argument("--grid-runs", type=int, default=2, help="repeat runs of the plan grid")
+    ap.add_argument("--grid-steps", type=int, default=10, help="timed cold calls per plan and cell")
+    ap.add_argument("--grid-op", default="fwd", choices=["fwd", "bwd"])
+    ap.add_argument("--score-grid", metavar="GRID_JSON",
+                    help="print the regret summary of a plan-grid file and exit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from the two rocprofv3 --pmc "
                          "CSVs (FETCH_SIZE run, WRITE_SIZE run) of this bench, and exit")
@@ -178,6 +187,10 @@ def main(argv=None) -> int:
         return 0
     if args.record_traffic:
         print(json.dumps(record_traffic(*args.record_traffic), indent=1))
+        return 0
+    if args.score_grid:
+        with open(args.score_grid) as f:
+            print(json.dumps(score_grid(json.load(f))))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -199,6 +212,9 @@ def main(argv=None) -> int:
 
     def log(*a):
         print(*a, file=sys.stderr, flush=True)
+
+    if args.plan_grid:
+        return plan_grid(torch, sm, s_handle, log, args)
 
     # ---------------------------------------------------------------- input
     x_cpu = workloads.generate(WORKLOAD)
@@ -484,6 +500,143 @@ def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
         parity = {"passed": False, "error": str(e)[:500]}
     log(f"[bench] oracle parity: {parity}")
     return res, parity
+
+
+# ------------------------------------------------------------------ row-plan grid
+# The grid of "Measured optimization case studies", section "Choosing the plans from
+# a grid": every plan timed at 18 row counts and 10 widths from 12288 to 1,048,576,
+# and a rule scored by its regret, the rule's time over the best plan's time in the
+# same cell, minus 1 (mean, 90th percentile, cells more than 10% off). The page
+# names some of its row counts and widths; the others are filled in here.
+GRID_ROWS = (1, 2, 4, 8, 16, 24, 32, 48, 64, 80, 96, 128, 192, 256, 384, 512, 768, 1024)
+GRID_WIDTHS = (12288, 16384, 32768, 32769, 50257, 65536, 131072, 262144, 524288, 1048576)
+GRID_PLANS = {  # forced plans; "auto" is the library's own rule
+    "auto": {}, "split": {"plan": 4}, "wide": {"plan": 3}, "resident": {"plan": 1},
+    "persistent": {"plan": 2},
+    **{f"split_v{v}": {"plan": 4, "vecs_per_lane": v} for v in (1, 2, 4, 8)},
+    **{f"wide_c{c}": {"plan": 3, "chunks_per_wave": c} for c in (1, 2, 4, 8)},
+}
+
+
+def _signature(info) -> str:
+    d = info.as_dict()
+    return (f"{d['plan_name']}:G{d['lanes_per_row']}:V{d['vecs_per_lane']}:c{d['chunks_per_wave']}"
+            f":p{d['waves_per_row']}:g{d['grid']}:pf{d['prefetch']}:nt{d['nt_loads']}")
+
+
+def plan_grid(torch, sm, s_handle, log, args) -> int:
+    """Time every plan of every grid cell (cold calls, dispatch events), write the cell
+    times, print the regret summary."""
+    dev = torch.device("cuda")
+    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def flush():
+        if sm.sm_bench_flush(flush_buf.data_ptr(), FLUSH_BYTES, s_handle) != 0:
+            raise RuntimeError("sm_bench_flush failed")
+
+    bwd = args.grid_op == "bwd"
+    runs = []
+    for run in range(args.grid_runs):
+        cells = []
+        gen = torch.Generator(device="cuda").manual_seed(2026)
+        for N in GRID_WIDTHS:
+            for M in GRID_ROWS:
+                x = (torch.randn(M, N, device=dev, generator=gen) * 3).to(torch.bfloat16)
+                out = torch.empty_like(x)
+                dy = None
+                if bwd:
+                    sm.softmax(x, out=x)  # y
+                    dy = torch.randn(M, N, device=dev, generator=gen).to(torch.bfloat16)
+                keys, times, model = {}, {}, {}
+                for key, o in GRID_PLANS.items():
+                    opts = sm._opts(o)
+                    if bwd:
+                        rc, info = sm.sm_softmax_bwd_plan_query(
+                            x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N, N, N, N, sm.SM_BF16,
+                            opts, 0)
+                    else:
+                        rc, info = sm.sm_softmax_plan_query(x.data_ptr(), out.data_ptr(), M, N, N, N,
+                                                            sm.SM_BF16, opts, 0)
+                    if rc != 0:
+                        continue
+                    sig = _signature(info)
+                    keys[key] = sig
+                    if sig in times:
+                        continue
+
+                    def call(events=(None, None), opts=opts):
+                        opts.start_event, opts.stop_event = events
+                        if bwd:
+                            r = sm.sm_softmax_bwd_ex(x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N,
+                                                     N, N, N, sm.SM_BF16, opts, 0, 0, s_handle)
+                        else:
+                            r = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N,
+                                                     sm.SM_BF16, opts, 0, 0, s_handle)
+                        if r != 0:
+                            raise sm.SoftmaxError(r)
+
+                    for _ in range(2):
+                        flush()
+                        call()
+                    ev = DispatchEvents(args.grid_steps)
+                    for _ in range(args.grid_steps):
+                        flush()
+                        call(ev.next_pair())
+                    times[sig] = round(float(np.mean(ev.samples_ms(torch))) * 1e3, 3)
+                    ev.close()
+                    model[sig] = int(info.model_bytes)
+                cells.append({"M": M, "N": N, "keys": keys, "us": times})
+                del x, out, dy
+            torch.cuda.empty_cache()
+            log(f"[grid] run {run + 1}: width {N} done ({len(cells)} cells)")
+        runs.append(cells)
+    if sm.sync_failures() != 0:
+        raise RuntimeError("SPLIT waits timed out during the grid")
+    data = {"op": args.grid_op, "dtype": "bf16", "rows": GRID_ROWS, "widths": GRID_WIDTHS,
+            "steps": args.grid_steps, "runs": runs}
+    with open(args.plan_grid, "w") as f:
+        json.dump(data, f, separators=(",", ":"))
+    print(json.dumps(score_grid(data)), flush=True)
+    return 0
+
+
+def score_grid(data: dict) -> dict:
+    """Regret of the library's rule and of simple alternatives on a plan grid:
+    per cell, (time of the rule's plan) / (best forced plan's time) - 1."""
+    def rules(c):
+        k = c["keys"]
+        r = {"library": k.get("auto"), "always_split": k.get("split") or k.get("wide"),
+             "always_wide": k.get("wide")}
+        r["one_pass_when_it_fits"] = k.get("resident") or k.get("auto")
+        return r
+
+    out = {"op": data["op"], "cells": None, "rules": {}}
+    per_run = []
+    for cells in data["runs"]:
+        regrets = {}
+        for c in cells:
+            best = min(c["us"][sig] for key, sig in c["keys"].items() if key != "auto")
+            for name, sig in rules(c).items():
+                if sig is None or sig not in c["us"]:
+                    continue
+                regrets.setdefault(name, []).append(c["us"][sig] / best - 1.0)
+        per_run.append(regrets)
+        out["cells"] = len(cells)
+    for name in per_run[0]:
+        rs = [np.asarray(r[name]) for r in per_run]
+        out["rules"][name] = {
+            "mean_regret_pct": [round(100 * float(a.mean()), 2) for a in rs],
+            "p90_regret_pct": round(100 * float(np.percentile(rs[0], 90)), 2),
+            "cells_over_10pct": int((rs[0] > 0.10).sum()), "cells": int(rs[0].size)}
+    if len(data["runs"]) > 1:  # run-to-run noise of the same plan in the same cell
+        d = []
+        for c1, c2 in zip(data["runs"][0], data["runs"][1]):
+            for sig, t in c1["us"].items():
+                if sig in c2["us"]:
+                    d.append(abs(c2["us"][sig] / t - 1.0))
+        out["repeat_diff_pct"] = {"median": round(100 * float(np.median(d)), 2),
+                                  "p90": round(100 * float(np.percentile(d, 90)), 2)}
+    return out
 
 
 def sweep(torch, sm, workloads, flush, s_handle, log, args):

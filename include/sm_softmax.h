@@ -147,6 +147,8 @@ typedef struct sm_plan_info {
                               WIDE (backward: 3*M*N*elem one-pass and SPLIT, 5*M*N*elem
                               WIDE) */
     int dy_same_phase;     /* backward: dy rows share y's 16-byte phase (vector loads) */
+    int slice_windows;     /* SPLIT: 16-byte windows per slice (a row's windows spread
+                              evenly over its slices; at most 256 * vecs_per_lane) */
 } sm_plan_info;
 
 /*

@@ -56,7 +56,7 @@ class SmPlanInfo(ctypes.Structure):
                 ("chunks_per_wave", ctypes.c_int), ("waves_per_row", ctypes.c_int64),
                 ("launches", ctypes.c_int), ("same_phase", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_int64), ("model_bytes", ctypes.c_int64),
-                ("dy_same_phase", ctypes.c_int)]
+                ("dy_same_phase", ctypes.c_int), ("slice_windows", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}

@@ -131,8 +131,8 @@ __device__ __forceinline__ void store_dx(const float (&fy)[NV][Elem<DT>::per_vec
 }
 
 // Raw (still encoded) windows of dy for the windows of y: 16-byte loads when dy
-// shares y's 16-byte phase, element loads packed into words otherwise. Columns
-// outside [0, N) read as 0.
+// shares y's 16-byte phase, element loads packed into words otherwise. Windows
+// from nwin on and columns outside [0, N) read as 0.
 template <int DT, int NV, bool NT>
 __device__ __forceinline__ void load_dy_raw(uint32_t (&r)[NV][4], const unsigned char* dyrow,
                                             int head, int N, int64_t w0, int wstep, int nwin,
@@ -156,7 +156,7 @@ __device__ __forceinline__ void load_dy_raw(uint32_t (&r)[NV][4], const unsigned
 #pragma unroll
             for (int k = 0; k < E; ++k) {
                 const int64_t c = c0 + k;
-                if (c >= 0 && c < N) {
+                if (w < nwin && c >= 0 && c < N) {
                     const unsigned char* p = dyrow + (size_t)c * ES;
                     if constexpr (DT == kF32) {
                         r[v][k] = *reinterpret_cast<const uint32_t*>(p);

@@ -177,6 +177,20 @@ bool built_shape(int G, int V, int PF) {
     return g_ok && v_ok && (!PF || G <= 256);
 }
 
+// Automatic choice between one-pass rows and SPLIT: rows of up to 8192 elements
+// always run one-pass (the resident limit of the Warpline README's online-softmax
+// description); wider rows run one-pass when they fit in kOnePassWideWindows
+// 16-byte windows and there are at least kOnePassWideRows of them, else SPLIT.
+// On the row-plan grid (BF16, forward) one-pass rows won from 128 rows up at
+// widths to 32768 (SPLIT lost 10 to 47% there) and lost to SPLIT below; rows of
+// 8192 windows (65536 BF16) did better split at every row count.
+constexpr int64_t kOnePassWideWindows = 4096;
+constexpr int64_t kOnePassWideRows = 128;
+
+bool one_pass_rule(int64_t M, int64_t N, int64_t nw) {
+    return N <= kResidentMaxCols || (nw <= kOnePassWideWindows && M >= kOnePassWideRows);
+}
+
 struct DeviceView {
     int cus;
     // workgroups per CU for a row-kernel instance / for the wide kernels
@@ -209,32 +223,53 @@ bool split_geometry(int64_t M, int64_t nw, int V, int64_t cap_slots, int64_t fix
     return true;
 }
 
-// Automatic SPLIT shape: the smallest V >= 2 whose rows need at most
-// kSplitMaxAutoSlices slices and whose slices of all rows fit in one round; else
-// the largest V that fits at all (fewest rounds). Returns 0 when no V fits.
-// Measured on MI355X, cold BF16 (us, V = 1 / 2 / 4 / 8): 1 x 1048576: 7.6 / 6.2 /
-// 5.7 / 6.6; 8 x 262144: 5.8 / 5.4 / 5.6 / 6.9; 16 x 65536: 4.6 / 4.5 / 5.1 / 6.4;
-// 64 x 131072: - / 13.8 / 11.3 / 11.1. Very wide slices leave few workgroups in
-// flight; very narrow ones make each workgroup wait on many slots.
+// Automatic SPLIT shape, in order of preference:
+//   1. the smallest V >= 2 whose rows need at most kSplitMaxAutoSlices slices and
+//      whose slices of all rows fit in one round (most workgroups in flight);
+//   2. with rounds unavoidable, V = 4 when rows need at most kSplitRoundSlices
+//      slices of 1024 windows (shorter rounds than V = 8 at the same traffic);
+//   3. the largest V that fits at all (fewest slices per row).
+// Returns 0 when no V fits. Measured on MI355X, cold BF16 (us, V = 1 / 2 / 4 / 8):
+// 1 x 1048576: 7.6 / 6.2 / 5.7 / 6.6; 8 x 262144: 5.8 / 5.4 / 5.6 / 6.9; 16 x 65536:
+// 4.6 / 4.5 / 5.1 / 6.4; 64 x 131072: - / 13.8 / 11.3 / 11.1. On the row-plan grid
+// (18 row counts x 10 widths) rule 2 took the width-32769 column from 9.4% to 3.1%
+// mean regret, while V = 4 at 32 or more slices per row cost 4 to 21% at widths
+// from 262144 up.
 constexpr int64_t kSplitMaxAutoSlices = 128;
+constexpr int64_t kSplitRoundSlices = 16;
 
 int split_auto_v(int64_t M, int64_t nw, int vmax, int64_t cus, void* ctx, int dtype, int bwd,
                  int (*occ)(void*, int, int, int), int64_t& P, int64_t& grid) {
-    int best = 0;
-    for (int v = 2; v <= vmax; v *= 2) {
+    int64_t cp[4] = {0, 0, 0, 0}, cg[4] = {0, 0, 0, 0};
+    bool ok[4] = {false, false, false, false};
+    int vs[4] = {0, 0, 0, 0}, n = 0;
+    for (int v = 2; v <= vmax; v *= 2, ++n) {
         const int64_t slots = (int64_t)std::max(1, occ(ctx, dtype, v, bwd)) * cus;
-        int64_t p = 0, g = 0;
-        if (!split_geometry(M, nw, v, slots, 0, p, g)) continue;
-        if (M * p <= g && p <= kSplitMaxAutoSlices) {
-            P = p;
-            grid = g;
-            return v;
-        }
-        best = v;
-        P = p;
-        grid = g;
+        vs[n] = v;
+        ok[n] = split_geometry(M, nw, v, slots, 0, cp[n], cg[n]);
     }
-    return best;
+    for (int i = 0; i < n; ++i) {  // 1
+        if (ok[i] && M * cp[i] <= cg[i] && cp[i] <= kSplitMaxAutoSlices) {
+            P = cp[i];
+            grid = cg[i];
+            return vs[i];
+        }
+    }
+    for (int i = 0; i < n; ++i) {  // 2
+        if (ok[i] && vs[i] == 4 && cp[i] <= kSplitRoundSlices) {
+            P = cp[i];
+            grid = cg[i];
+            return 4;
+        }
+    }
+    for (int i = n - 1; i >= 0; --i) {  // 3
+        if (ok[i]) {
+            P = cp[i];
+            grid = cg[i];
+            return vs[i];
+        }
+    }
+    return 0;
 }
 
 int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev, sm_plan_info* pi) {
@@ -250,7 +285,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     int plan = o.plan;
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
-    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
+    if (auto_plan) plan = one_pass_rule(p.M, p.N, nw_max) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
     if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
 
     if (plan == SM_PLAN_SPLIT) {
@@ -276,6 +311,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
             pi->block = kSplitLanes;
             pi->grid = grid;
             pi->waves_per_row = P;
+            pi->slice_windows = (int)((nw_max + P - 1) / P);
             pi->launches = 1;
             pi->nt_loads = nt ? 1 : 0;
             pi->workspace_bytes = ((p.M * P * 32 + 255) / 256) * 256;
@@ -515,7 +551,7 @@ int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_
         const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
         e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
                      stream, ev0, ev1, in, out, ws, sync, p.M, N, isb, osb, (int)pi.waves_per_row,
-                     next_tag(), spin, (int)pi.same_phase);
+                     pi.slice_windows, next_tag(), spin, (int)pi.same_phase);
         return e == hipSuccess ? SM_OK : hip_fail(e);
     }
     if (pi.plan == SM_PLAN_WIDE) {
@@ -633,7 +669,7 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
     int plan = o.plan;
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
-    if (auto_plan) plan = (p.N <= kResidentMaxCols) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
+    if (auto_plan) plan = one_pass_rule(p.M, p.N, nw_max) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
     if (plan == SM_PLAN_SPLIT) {
         auto occ_fn = live ? occ_split_live : occ_split_host;
         int64_t P = 0, grid = 0;
@@ -658,6 +694,7 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
             pi->block = kSplitLanes;
             pi->grid = grid;
             pi->waves_per_row = P;
+            pi->slice_windows = (int)((nw_max + P - 1) / P);
             pi->launches = 1;
             pi->nt_loads = nt ? 1 : 0;
             pi->workspace_bytes = ((p.M * P * 32 + 255) / 256) * 256;
@@ -734,8 +771,8 @@ int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, const sm_s
         const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
         e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
                      stream, ev0, ev1, y, dy, dx, ws, sync, p.M, N, ysb, dysb, dxsb,
-                     (int)pi.waves_per_row, next_tag(), spin, (int)pi.dy_same_phase,
-                     (int)pi.same_phase);
+                     (int)pi.waves_per_row, pi.slice_windows, next_tag(), spin,
+                     (int)pi.dy_same_phase, (int)pi.same_phase);
         return e == hipSuccess ? SM_OK : hip_fail(e);
     }
     if (pi.plan == SM_PLAN_WIDE) {

@@ -1,7 +1,8 @@
 // sm_split.hpp -- one-launch softmax of wide rows split across workgroups.
 //
-// A row of N elements is cut into P slices of S = 256 * V 16-byte windows; one
-// workgroup of 256 lanes (4 waves) holds a slice in registers. Each workgroup
+// A row of N elements is cut into P slices of at most 256 * V 16-byte windows
+// (spread evenly: S = ceil(windows / P) each); one workgroup of 256 lanes (4
+// waves) holds a slice in registers. Each workgroup
 // computes its slice's (max, sum of exp(x - max)), publishes the pair, waits
 // until the row's other P - 1 slices have published theirs, merges the P pairs
 // in a fixed order (so every slice of the row derives bitwise the same row
@@ -127,12 +128,12 @@ __device__ __forceinline__ void split_gather(const SplitSlot* row_slots, int P, 
 template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
 k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, SplitSync* sync,
-                int64_t M, int N, int64_t in_sb, int64_t out_sb, int P, uint32_t tag,
+                int64_t M, int N, int64_t in_sb, int64_t out_sb, int P, int S, uint32_t tag,
                 int spin_limit, int same_phase) {
+    // S: windows per slice (<= B * V; the host spreads a row evenly over its P slices)
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
     constexpr int B = kSplitBlock;
-    constexpr int S = B * V;  // windows per slice
     __shared__ float lds_a[B / 64], lds_b[B / 64], lds_c[B / 64];
     __shared__ float lds_stat[4];
 
@@ -143,6 +144,7 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
         const int p = (int)(item - row * P);
         const RowGeom<DT> g(in + row * in_sb, N);
         const int64_t w0 = (int64_t)p * S + lane;  // this lane's first window
+        const int64_t wend = ((int64_t)p * S + S < g.nwin) ? (int64_t)p * S + S : g.nwin;
 
         float x[V][E];
 #pragma unroll
@@ -150,7 +152,7 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
             const int64_t w = w0 + (int64_t)B * v;
             const uint32_t ni = Elem<DT>::neg_inf_word;
             uint4 raw = make_uint4(ni, ni, ni, ni);
-            if (w < g.nwin) raw = load16<NT>(g.base + 16 * (size_t)w);
+            if (w < wend) raw = load16<NT>(g.base + 16 * (size_t)w);
             decode<DT>(raw, x[v]);
         }
         // -inf outside [0, N) in windows that straddle the row's ends
@@ -230,7 +232,7 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int64_t w = w0 + (int64_t)B * v;
-            if (w < g.nwin) {
+            if (w < wend) {
                 float y[E];
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
@@ -297,11 +299,10 @@ template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
 k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned char* dx,
                     SplitSlot* slots, SplitSync* sync, int64_t M, int N, int64_t y_sb,
-                    int64_t dy_sb, int64_t dx_sb, int P, uint32_t tag, int spin_limit,
+                    int64_t dy_sb, int64_t dx_sb, int P, int S, uint32_t tag, int spin_limit,
                     int dy_phase, int dx_phase) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int B = kSplitBlock;
-    constexpr int S = B * V;
     __shared__ float lds_hi[B / 64], lds_lo[B / 64];
     __shared__ float lds_stat[4];
 
@@ -312,19 +313,20 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
         const int p = (int)(item - row * P);
         const RowGeom<DT> g(y + row * y_sb, N);
         const int64_t w0 = (int64_t)p * S + lane;
+        const int64_t wend = ((int64_t)p * S + S < g.nwin) ? (int64_t)p * S + S : g.nwin;
 
         uint32_t ry[V][4], rd[V][4];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int64_t w = w0 + (int64_t)B * v;
             uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-            if (w < g.nwin) raw = load16<NT>(g.base + 16 * (size_t)w);
+            if (w < wend) raw = load16<NT>(g.base + 16 * (size_t)w);
             ry[v][0] = raw.x;
             ry[v][1] = raw.y;
             ry[v][2] = raw.z;
             ry[v][3] = raw.w;
         }
-        load_dy_raw<DT, V, NT>(rd, dy + row * dy_sb, g.head, N, w0, B, g.nwin, dy_phase);
+        load_dy_raw<DT, V, NT>(rd, dy + row * dy_sb, g.head, N, w0, B, wend, dy_phase);
         if (g.head != 0 || (N % E) != 0) {
             zero_raw_outside<DT, V>(ry, g.head, N, w0, B);
             zero_raw_outside<DT, V>(rd, g.head, N, w0, B);
@@ -360,7 +362,7 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int64_t w = w0 + (int64_t)B * v;
-            if (w < g.nwin) {
+            if (w < wend) {
                 if constexpr (DT != kF32) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ry[v][i]), "+v"(rd[v][i]));

@@ -161,15 +161,26 @@ def test_plan_rule_split():
     assert p["workspace_bytes"] == 64 * 16 * 32 and p["model_bytes"] == 2 * 64 * 131072 * 2
     rc, p = plan(4, 8193, F32)  # just past the one-pass limit: 2049 windows -> 5 slices of 512
     assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 5)
-    assert p["grid"] == 20
+    assert p["grid"] == 20 and p["slice_windows"] == 410  # 2049 windows spread over 5 slices
+    rc, p = plan(1024, 32769, BF16, {"plan": sm.SM_PLAN_SPLIT, "vecs_per_lane": 8})
+    assert (p["waves_per_row"], p["slice_windows"]) == (3, 1366)  # not 2048 + 2048 + 1
     rc, p = plan(1, 1 << 20, BF16)  # V=2 would need 256 slices per row: V=4, 128 slices
     assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (4, 128, 128)
     rc, p = plan(8, 1 << 18, BF16)  # V=2: 64 slices, 512 workgroups in one round
     assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (2, 64, 512)
-    rc, p = plan(1024, 16384, BF16)  # V=8 -> one slice per row, 1024 rows: one round
-    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (8, 1, 1024)
-    rc, p = plan(8192, 16384, BF16)  # more rows than slots: V=8, rounds of 1024 rows
-    assert (p["vecs_per_lane"], p["grid"]) == (8, 1024)
+    # 2048 windows and at least 128 rows: one-pass rows (the grid's finding)
+    rc, p = plan(1024, 16384, BF16)
+    assert p["plan_name"] == "persistent" and (p["lanes_per_row"], p["vecs_per_lane"]) == (512, 4)
+    rc, p = plan(8192, 16384, BF16)
+    assert p["plan_name"] == "resident" and (p["lanes_per_row"], p["vecs_per_lane"]) == (512, 4)
+    rc, p = plan(127, 16384, BF16)  # fewer rows: SPLIT
+    assert p["plan_name"] == "split"
+    rc, p = plan(1024, 65536, BF16)  # 8192 windows: SPLIT at any row count
+    assert p["plan_name"] == "split"
+    rc, p = plan(1024, 131072, BF16)  # rounds unavoidable: V=4 while rows need <= 16 slices
+    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (4, 16, 1024)
+    rc, p = plan(1024, 524288, BF16)  # V=4 would need 64 slices: the largest V, 32 slices
+    assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (8, 32, 1024)
     rc, p = plan(1, 1 << 25, BF16)  # 2^22 windows: even V=8 needs 2048 slices > 1024
     assert rc == OK and p["plan_name"] == "wide"
     S = {"plan": sm.SM_PLAN_SPLIT}

@@ -644,10 +644,16 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
     names = ["normal_f32_128x781", "normal_bf16_4096x4096",
              *[f"spiky_f16_8192x{n}" for n in workloads.SPIKE_WIDTHS],
              "offset_bf16_64x131072", "causal_bf16_524288x2048"]
-    plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3}
+    plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
     steps = max(20, args.steps // 4)
     for name in names:
         x = workloads.generate(name).to("cuda")
+        # the GPU idled while the input was built on the host: bring the clocks back up
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                flush()
+            torch.cuda.synchronize()
         out = torch.empty_like(x)
         M, N = x.shape
         dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[x.dtype]

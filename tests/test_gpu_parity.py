@@ -16,7 +16,7 @@ import torch
 import memory_bound_row_sm_amd as sm
 import oracle
 import workloads
-from parity import compare, log, row_sum_bound, to_f64
+from parity import compare, compare_bwd, log, row_sum_bound, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +109,22 @@ def test_causal_logits_full_size_sampled():
     assert (gv[:, 0, 0] == 1).all()
     sums = gv.sum(dim=-1, dtype=torch.float64)
     assert float((sums - 1).abs().max()) <= row_sum_bound("bf16")
+
+    # the backward of the same tensor in its automatic launch configuration
+    dy = workloads.upstream_grad(g.shape, "bf16", device=DEV)
+    binfo = sm.plan_for_backward(g, dy)
+    log(f"[parity] causal backward plan {binfo['plan_name']} G={binfo['lanes_per_row']} "
+        f"V={binfo['vecs_per_lane']} nt={binfo['nt_loads']}")
+    dx = torch.full_like(g, float("nan"))
+    sm.softmax_backward(g, dy, dx=dx)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(rows).to(DEV)
+    st = compare_bwd(dx[sel].cpu(), g[sel].cpu(), dy[sel].cpu(), what="causal backward sampled rows")
+    log(f"[parity] causal backward sampled {rows.size} rows: {st}")
+    dv = dx.view(heads, Q, Q)
+    assert not torch.isnan(dv).any()
+    assert (dv.masked_select(masked.expand_as(dv)) == 0).all()  # y = 0 there
+    assert float(dv.sum(dim=-1, dtype=torch.float64).abs().max()) < 0.05  # d (1 - sum y)
 
 
 # ------------------------------------------------------------------ shapes and layouts

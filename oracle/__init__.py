@@ -1,4 +1,5 @@
-"""FP64 row-softmax oracle: a ctypes wrapper over ``liboracle_softmax.so``.
+"""FP64 row-softmax oracle (forward, backward, fused residual RMSNorm): a ctypes
+wrapper over ``liboracle_softmax.so``.
 
 TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
 bench's CPU-baseline leg may import this package. The GPU library and its
@@ -64,9 +65,11 @@ class Oracle:
         lib.oracle_softmax_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, _DP, ctypes.c_int]
         lib.oracle_softmax_bwd_rows.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, i64, _DP,
                                                 ctypes.c_int]
+        lib.oracle_rmsnorm_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, vp, i64,
+                                            ctypes.c_double, _DP, _DP, ctypes.c_int]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_softmax_rows,
-                  lib.oracle_softmax_bwd_rows, lib.oracle_max_threads):
+                  lib.oracle_softmax_bwd_rows, lib.oracle_rmsnorm_rows, lib.oracle_max_threads):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -164,6 +167,53 @@ class Oracle:
         dx = self.softmax_bwd_f64(y, dy, dtype, rows=rows, threads=threads)
         return dx, self.encode(dx, dtype)
 
+    def rmsnorm_f64(self, x: np.ndarray, residual, weight: np.ndarray, dtype, eps: float,
+                    rows=None, threads: int = 0):
+        """(y_f64, s_f64): residual RMSNorm of the rows of stored x (2-D, row-strided views
+        allowed) with an optional stored residual of the same shape and a stored weight of
+        N elements; s is the sum rounded once to the dtype (x itself without residual)."""
+        a = _as_storage(x, dtype)
+        if a.ndim != 2:
+            raise ValueError("expected a 2-D matrix")
+        M, N = a.shape
+        es = a.dtype.itemsize
+        b = None if residual is None else _as_storage(residual, dtype)
+        if b is not None and b.shape != a.shape:
+            raise ValueError("residual must match x")
+        w = np.ascontiguousarray(_as_storage(weight, dtype)).reshape(-1)
+        if w.size != N:
+            raise ValueError("weight must hold N elements")
+        nrows = M if rows is None else len(rows)
+        y = np.empty((nrows, N), np.float64)
+        s = np.empty((nrows, N), np.float64)
+        if a.size == 0:
+            return y, s
+        for t in (a, b) if b is not None else (a,):
+            if N > 1 and t.strides[1] != es:
+                raise ValueError("column stride must be one element")
+            if t.strides[0] % es or t.strides[0] < 0:
+                raise ValueError("row stride must be a non-negative multiple of the element size")
+        sa = a.strides[0] // es if M > 1 else N
+        sb = (b.strides[0] // es if M > 1 else N) if b is not None else 0
+        idx = None
+        if rows is not None:
+            idx = np.ascontiguousarray(rows, dtype=np.int64)
+            if idx.size and (idx.min() < 0 or idx.max() >= M):
+                raise IndexError("row index out of range")
+        rc = self.lib.oracle_rmsnorm_rows(
+            a.ctypes.data, None if b is None else b.ctypes.data, w.ctypes.data, _code(dtype), N,
+            sa, sb, None if idx is None else idx.ctypes.data, nrows, float(eps),
+            y.ctypes.data_as(_DP), s.ctypes.data_as(_DP), int(threads))
+        if rc:
+            raise ValueError("oracle_rmsnorm_rows rejected its arguments")
+        return y, s
+
+    def reference_rmsnorm(self, x, residual, weight, dtype, eps: float, rows=None, threads: int = 0):
+        """(y_f64, y_rounded, s_rounded): the FP64 result, its one RNE cast, and the
+        rounded residual sums in the storage encoding."""
+        y, s = self.rmsnorm_f64(x, residual, weight, dtype, eps, rows=rows, threads=threads)
+        return y, self.encode(y, dtype), self.encode(s, dtype)
+
 
 _default = None
 
@@ -205,3 +255,11 @@ def softmax_bwd_f64(y, dy, dtype, rows=None, threads: int = 0):
 
 def reference_bwd(y, dy, dtype, rows=None, threads: int = 0):
     return default().reference_bwd(y, dy, dtype, rows=rows, threads=threads)
+
+
+def rmsnorm_f64(x, residual, weight, dtype, eps, rows=None, threads: int = 0):
+    return default().rmsnorm_f64(x, residual, weight, dtype, eps, rows=rows, threads=threads)
+
+
+def reference_rmsnorm(x, residual, weight, dtype, eps, rows=None, threads: int = 0):
+    return default().reference_rmsnorm(x, residual, weight, dtype, eps, rows=rows, threads=threads)

@@ -1,5 +1,6 @@
 /*
- * oracle_softmax.c -- plain FP64 row-softmax oracle (C99 + OpenMP over rows).
+ * oracle_softmax.c -- plain FP64 row-softmax oracle (C99 + OpenMP over rows), with
+ * the softmax backward and the fused residual RMSNorm on the same row layout.
  *
  * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the bench's
  * CPU-baseline leg load this library. The GPU product path never calls it, and
@@ -33,6 +34,21 @@
  * dy, decoded exactly, by the same plain steps in FP64:
  *   1. d = sum_j y_j * dy_j, added left to right;
  *   2. dx_j = y_j * (dy_j - d).
+ *
+ * The fused residual RMSNorm (Warpline README, the description of its K1 kernel:
+ * the input and the residual are added in FP32, that sum is rounded once to the
+ * input dtype, the RMS reduction runs in FP32, the weight is applied and the result
+ * is written in the input dtype), per row, from the stored x, residual r and
+ * weight w:
+ *   1. s_j = x_j + r_j rounded once to the dtype. The pages add in FP32 and then
+ *      round; for FP16 and BF16 that equals the correctly rounded sum, because FP32
+ *      carries at least 2p + 1 bits for p-bit formats (Figueroa's theorem on
+ *      innocuous double rounding), and for FP32 data the double sum rounded to FP32
+ *      is the FP32 sum for the same reason (53 >= 2 * 24 + 1). So the oracle adds in
+ *      double and rounds once with its own encoder. No residual: s = x.
+ *   2. q = sum_j s_j^2 in double, left to right;
+ *   3. y_j = s_j * w_j / sqrt(q / N + eps) in double (eps is the caller's; the
+ *      pages give no value).
  *
  * Readings where the pages are silent (listed in the design notes too):
  *   - a row whose entries are all -inf (and an empty row) has no finite
@@ -270,6 +286,76 @@ int oracle_softmax_bwd_rows(const void *y, const void *dy, int dtype, int64_t co
                 a[cols + j] = load_elem(dr + (size_t)j * es, dtype);
             }
             softmax_bwd_row(a, a + cols, cols, dx + (size_t)k * (size_t)cols);
+        }
+        free(a);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Residual RMSNorm of one decoded row: s (already rounded), w, n -> y. */
+static void rmsnorm_row(const double *sv, const double *w, int64_t n, double eps, double *y) {
+    double q = 0.0;
+    for (int64_t j = 0; j < n; ++j) q += sv[j] * sv[j];
+    const double den = sqrt(q / (double)n + eps);
+    for (int64_t j = 0; j < n; ++j) y[j] = sv[j] * w[j] / den;
+}
+
+/*
+ * Residual RMSNorm of selected rows.
+ *   x, r      : stored input and residual (same dtype), row k at base + k * stride
+ *               elements; r may be NULL (s = x)
+ *   w         : stored weight, cols elements
+ *   rows      : row indices, or NULL for rows 0..nrows-1
+ *   y         : output, nrows x cols doubles
+ *   s_out     : optional (NULL), nrows x cols doubles: the rounded sums s
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_rmsnorm_rows(const void *x, const void *r, const void *w, int dtype, int64_t cols,
+                        int64_t x_stride, int64_t r_stride, const int64_t *rows, int64_t nrows,
+                        double eps, double *y, double *s_out, int threads) {
+    int es = elem_size(dtype);
+    if (!es || cols < 0 || nrows < 0 || x_stride < cols || (r && r_stride < cols) || !w) return -1;
+    if (nrows == 0 || cols == 0) return 0;
+    const int mant = dtype == ORC_F32 ? 23 : (dtype == ORC_F16 ? 10 : 7);
+    const int ebits = dtype == ORC_F16 ? 5 : 8;
+    const unsigned char *xb = (const unsigned char *)x;
+    const unsigned char *rb = (const unsigned char *)r;
+    const unsigned char *wb = (const unsigned char *)w;
+#ifdef _OPENMP
+    if (threads <= 0) threads = omp_get_max_threads();
+#else
+    threads = 1;
+#endif
+    int bad = 0;
+#pragma omp parallel num_threads(threads) reduction(| : bad)
+    {
+        double *a = (double *)malloc(sizeof(double) * 2 * (size_t)cols);
+        if (!a) bad = 1;
+#pragma omp for schedule(static)
+        for (int64_t k = 0; k < nrows; ++k) {
+            if (!a) continue;
+            int64_t row = rows ? rows[k] : k;
+            const unsigned char *xr = xb + (size_t)(row * x_stride) * (size_t)es;
+            const unsigned char *rr = rb ? rb + (size_t)(row * r_stride) * (size_t)es : NULL;
+            for (int64_t j = 0; j < cols; ++j) {
+                double v = load_elem(xr + (size_t)j * es, dtype);
+                if (rr) {
+                    const uint32_t bits = encode_binary(v + load_elem(rr + (size_t)j * es, dtype),
+                                                        mant, ebits);
+                    unsigned char buf[4];
+                    if (es == 4) {
+                        memcpy(buf, &bits, 4);
+                    } else {
+                        const uint16_t h = (uint16_t)bits;
+                        memcpy(buf, &h, 2);
+                    }
+                    v = load_elem(buf, dtype);
+                }
+                a[j] = v;
+                a[cols + j] = load_elem(wb + (size_t)j * es, dtype);
+            }
+            rmsnorm_row(a, a + cols, cols, eps, y + (size_t)k * (size_t)cols);
+            if (s_out) memcpy(s_out + (size_t)k * (size_t)cols, a, sizeof(double) * (size_t)cols);
         }
         free(a);
     }

@@ -1,7 +1,7 @@
 """Planted mistakes: each one, compiled into a scratch copy of the oracle on the CPU,
 must fail at least one pin. This shows that the pins constrain every step of the
 oracle (decode, max, exp, sum, divide, row indexing, the all--inf reading, the
-one-step RNE encode), not just its happy path.
+one-step RNE encode, the backward, the residual RMSNorm), not just its happy path.
 
 The mutants are built from the committed C source with plain text edits and gcc;
 nothing here touches the GPU or the GPU library.
@@ -43,6 +43,17 @@ MUTANTS = [
      "for (int64_t j = 1; j < n; ++j) d += y[j] * dy[j];"),
     ("bwd scales by dy", "dx[j] = y[j] * (dy[j] - d);", "dx[j] = dy[j] * (dy[j] - d);"),
     ("bwd dy stride", "db + (size_t)(r * dy_stride)", "db + (size_t)(r * y_stride)"),
+    ("rms ignores residual", "encode_binary(v + load_elem(rr + (size_t)j * es, dtype),",
+     "encode_binary(v,"),
+    ("rms sum not rounded", "v = load_elem(buf, dtype);",
+     "v = v + load_elem(rr + (size_t)j * es, dtype);"),
+    ("rms drops eps", "sqrt(q / (double)n + eps)", "sqrt(q / (double)n)"),
+    ("rms mean over n - 1", "sqrt(q / (double)n + eps)", "sqrt(q / (double)(n - 1) + eps)"),
+    ("rms ignores weight", "y[j] = sv[j] * w[j] / den;", "y[j] = sv[j] / den;"),
+    ("rms no square root", "sqrt(q / (double)n + eps)", "(q / (double)n + eps)"),
+    ("rms weight index", "a[cols + j] = load_elem(wb + (size_t)j * es, dtype);",
+     "a[cols + j] = load_elem(wb, dtype);"),
+    ("rms residual stride", "(size_t)(row * r_stride)", "(size_t)(row * x_stride)"),
 ]
 
 
@@ -154,7 +165,32 @@ def pin_battery(orc: "oracle.Oracle"):
                               orc.softmax_bwd_f64(np.ascontiguousarray(yb[:, :40]),
                                                   np.ascontiguousarray(gb[:, 5:45]), "f32"))
 
-    for name, fn in [("bwd vs torch", bwd_torch), ("bwd strided", bwd_strided),
+    def rms_torch():
+        import torch.nn.functional as F
+        for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+            g = torch.Generator().manual_seed(5)
+            x = (torch.randn(4, 33, generator=g) * 3).to(tdt)
+            r = (torch.randn(4, 33, generator=g) * torch.exp2(torch.randint(-10, 2, (4, 33), generator=g))).to(tdt)
+            w = torch.randn(33, generator=g).to(tdt)
+            st = lambda t: t.numpy() if dt == "f32" else t.view(torch.int16).numpy().view(np.uint16)
+            y, _ = orc.rmsnorm_f64(st(x), st(r), st(w), dt, 1e-2)
+            want = F.rms_norm((x.float() + r.float()).to(tdt).double(), (33,), weight=w.double(),
+                              eps=1e-2).numpy()
+            if not np.allclose(y, want, rtol=1e-13, atol=0):
+                return False
+        return True
+
+    def rms_strided():
+        g = torch.Generator().manual_seed(6)
+        xb, rb = torch.randn(5, 40, generator=g), torch.randn(5, 60, generator=g)
+        w = torch.randn(30, generator=g)
+        a, _ = orc.rmsnorm_f64(xb.numpy()[:, :30], rb.numpy()[:, 7:37], w.numpy(), "f32", 1e-6)
+        b, _ = orc.rmsnorm_f64(np.ascontiguousarray(xb.numpy()[:, :30]),
+                               np.ascontiguousarray(rb.numpy()[:, 7:37]), w.numpy(), "f32", 1e-6)
+        return np.array_equal(a, b)
+
+    for name, fn in [("rms vs torch", rms_torch), ("rms strided", rms_strided),
+                     ("bwd vs torch", bwd_torch), ("bwd strided", bwd_strided),
                      ("brute force", brute), ("f16 decode", f16_decode), ("bf16 decode", bf16_decode),
                      ("f16 encode", encode_f16), ("constant rows", constant_rows),
                      ("spikes at the ends", spikes_first_last), ("strided view", strided),

@@ -1,5 +1,6 @@
 /*
- * sm_softmax.h -- C ABI of the MI355X (gfx950) fused row-softmax library.
+ * sm_softmax.h -- C ABI of the MI355X (gfx950) fused row-softmax library (forward,
+ * backward) and the fused residual RMSNorm on the same row layout.
  *
  * Operation (every entry point below computes exactly this):
  *
@@ -228,6 +229,54 @@ int sm_softmax_bwd_ex(const void *y, const void *dy, void *dx, int64_t M, int64_
 int sm_softmax_bwd_plan_query(const void *y, const void *dy, const void *dx, int64_t M, int64_t N,
                               int64_t y_stride, int64_t dy_stride, int64_t dx_stride, int dtype,
                               const sm_softmax_opts *opts, int num_cus, sm_plan_info *info);
+
+/*
+ * Fused residual RMSNorm on the same row layout (Warpline README, the description
+ * of its K1 kernel: the input and residual are added in FP32 and that sum is
+ * rounded once to the input dtype; the RMS reduction runs in FP32; the weight is
+ * applied and the result rounded once to the input dtype). Per row i:
+ *
+ *     s_j = rn_dtype(x_ij + r_ij)             (s_j = x_ij without a residual)
+ *     y_ij = rn_dtype(s_j * w_j / sqrt(sum_k s_k^2 / N + eps))
+ *
+ *   x, residual  : device pointers of one dtype; residual may be NULL
+ *   weight       : N elements of the same dtype, shared by every row (must not
+ *                  overlap y or residual_out)
+ *   y            : output; may be x or residual exactly (same pointer and stride)
+ *   residual_out : optional (NULL): receives s, the rounded sum (the residual
+ *                  stream of the next layer); may be x or residual exactly, must
+ *                  not overlap y
+ *   strides      : row strides in elements, >= N when M > 1
+ *   eps          : finite, >= 0 (the pages give no value; 0 lets a zero row give NaN)
+ * Reduction state is FP32: rows whose sum of squares exceeds the FP32 range give
+ * zeros (or NaN where s is infinite). Plans as for the softmax backward: one-pass
+ * RESIDENT/PERSISTENT rows (up to 4 vectors per lane), SPLIT for wide rows (one
+ * launch, partial sums of squares exchanged between the row's workgroups), and
+ * WIDE as two launches of the split kernel (publish, then gather and apply) when
+ * a row's slices cannot be resident together. model_bytes counts x, w, y and, when
+ * present, the residual and residual_out once per element (w per row, as the
+ * pages' byte model does); WIDE reads x and the residual twice.
+ * Returns SM_OK or a negative sm_status; validation as for sm_softmax_fwd.
+ */
+int sm_rmsnorm_fwd(const void *x, const void *residual, const void *weight, void *y,
+                   void *residual_out, int64_t M, int64_t N, int64_t x_stride, int64_t res_stride,
+                   int64_t y_stride, int64_t res_out_stride, float eps, int dtype,
+                   hipStream_t stream);
+
+/* As sm_rmsnorm_fwd with overrides (plan, lanes_per_row, vecs_per_lane in {1, 2, 4},
+ * grid, nontemporal, spin_limit, timing events) and optional caller workspace. */
+int sm_rmsnorm_fwd_ex(const void *x, const void *residual, const void *weight, void *y,
+                      void *residual_out, int64_t M, int64_t N, int64_t x_stride,
+                      int64_t res_stride, int64_t y_stride, int64_t res_out_stride, float eps,
+                      int dtype, const sm_softmax_opts *opts, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* The plan sm_rmsnorm_fwd would launch (num_cus as for sm_softmax_plan_query). */
+int sm_rmsnorm_plan_query(const void *x, const void *residual, const void *weight, const void *y,
+                          const void *residual_out, int64_t M, int64_t N, int64_t x_stride,
+                          int64_t res_stride, int64_t y_stride, int64_t res_out_stride, float eps,
+                          int dtype, const sm_softmax_opts *opts, int num_cus,
+                          sm_plan_info *info);
 
 /* Static text for a status code. */
 const char *sm_softmax_strerror(int status);

@@ -20,7 +20,8 @@ __all__ = [
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_bench_copy", "sm_bench_flush",
     "softmax", "plan_for", "EXPORTED_SYMBOLS", "sm_softmax_bwd", "sm_softmax_bwd_ex",
     "sm_softmax_bwd_plan_query", "softmax_backward", "plan_for_backward",
-    "sm_softmax_sync_failures", "sync_failures",
+    "sm_softmax_sync_failures", "sync_failures", "sm_rmsnorm_fwd", "sm_rmsnorm_fwd_ex",
+    "sm_rmsnorm_plan_query", "rmsnorm", "plan_for_rmsnorm",
 ]
 
 SM_F32, SM_F16, SM_BF16 = 0, 1, 2
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "sm_softmax_fwd", "sm_softmax_fwd_ex", "sm_softmax_plan_query", "sm_softmax_bwd",
     "sm_softmax_bwd_ex", "sm_softmax_bwd_plan_query", "sm_softmax_strerror",
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_softmax_sync_failures",
+    "sm_rmsnorm_fwd", "sm_rmsnorm_fwd_ex", "sm_rmsnorm_plan_query",
     "sm_bench_copy", "sm_bench_flush",
 )
 
@@ -104,6 +106,13 @@ def lib() -> ctypes.CDLL:
         L.sm_softmax_bwd_plan_query.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ci,
                                                 ctypes.POINTER(SmOpts), ci,
                                                 ctypes.POINTER(SmPlanInfo)]
+        cf = ctypes.c_float
+        L.sm_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, cf, ci, vp]
+        L.sm_rmsnorm_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, cf, ci,
+                                        ctypes.POINTER(SmOpts), vp, ctypes.c_size_t, vp]
+        L.sm_rmsnorm_plan_query.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, cf,
+                                            ci, ctypes.POINTER(SmOpts), ci,
+                                            ctypes.POINTER(SmPlanInfo)]
         L.sm_softmax_strerror.argtypes = [ci]
         L.sm_softmax_strerror.restype = ctypes.c_char_p
         L.sm_softmax_version.argtypes = []
@@ -114,6 +123,7 @@ def lib() -> ctypes.CDLL:
         for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
                   L.sm_softmax_bwd, L.sm_softmax_bwd_ex, L.sm_softmax_bwd_plan_query,
                   L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_softmax_sync_failures,
+                  L.sm_rmsnorm_fwd, L.sm_rmsnorm_fwd_ex, L.sm_rmsnorm_plan_query,
                   L.sm_bench_copy, L.sm_bench_flush):
             f.restype = ci
         _lib = L
@@ -183,6 +193,36 @@ def sm_softmax_bwd_plan_query(y_ptr: int, dy_ptr: int, dx_ptr: int, M: int, N: i
                                          dx_stride, dtype,
                                          ctypes.byref(o) if o is not None else None, num_cus,
                                          ctypes.byref(info))
+    return rc, info
+
+
+def sm_rmsnorm_fwd(x_ptr: int, r_ptr: int, w_ptr: int, y_ptr: int, s_ptr: int, M: int, N: int,
+                   x_stride: int, r_stride: int, y_stride: int, s_stride: int, eps: float,
+                   dtype: int, stream: int = 0) -> int:
+    return lib().sm_rmsnorm_fwd(x_ptr, r_ptr or None, w_ptr, y_ptr, s_ptr or None, M, N, x_stride,
+                                r_stride, y_stride, s_stride, eps, dtype, stream)
+
+
+def sm_rmsnorm_fwd_ex(x_ptr: int, r_ptr: int, w_ptr: int, y_ptr: int, s_ptr: int, M: int, N: int,
+                      x_stride: int, r_stride: int, y_stride: int, s_stride: int, eps: float,
+                      dtype: int, opts=None, workspace: int = 0, workspace_bytes: int = 0,
+                      stream: int = 0) -> int:
+    o = _opts(opts)
+    return lib().sm_rmsnorm_fwd_ex(x_ptr, r_ptr or None, w_ptr, y_ptr, s_ptr or None, M, N,
+                                   x_stride, r_stride, y_stride, s_stride, eps, dtype,
+                                   ctypes.byref(o) if o is not None else None,
+                                   workspace or None, workspace_bytes, stream)
+
+
+def sm_rmsnorm_plan_query(x_ptr: int, r_ptr: int, w_ptr: int, y_ptr: int, s_ptr: int, M: int,
+                          N: int, x_stride: int, r_stride: int, y_stride: int, s_stride: int,
+                          eps: float, dtype: int, opts=None, num_cus: int = 0):
+    o = _opts(opts)
+    info = SmPlanInfo()
+    rc = lib().sm_rmsnorm_plan_query(x_ptr, r_ptr or None, w_ptr, y_ptr, s_ptr or None, M, N,
+                                     x_stride, r_stride, y_stride, s_stride, eps, dtype,
+                                     ctypes.byref(o) if o is not None else None, num_cus,
+                                     ctypes.byref(info))
     return rc, info
 
 
@@ -329,3 +369,52 @@ def sync_failures(stream=None) -> int:
     if rc != 0:
         raise SoftmaxError(rc, "sm_softmax_sync_failures")
     return n
+
+
+def _rms_args(x, weight, residual, out, residual_out):
+    import torch
+    if not (x.is_cuda and weight.is_cuda):
+        raise ValueError("rmsnorm expects device tensors")
+    if weight.dim() != 1 or weight.numel() != x.size(-1) or weight.dtype != x.dtype:
+        raise ValueError("weight must be a 1-D tensor of N elements of x's dtype")
+    if weight.numel() > 1 and weight.stride(0) != 1:
+        raise ValueError("weight must be contiguous")
+    for t in (residual, out, residual_out):
+        if t is not None and (t.shape != x.shape or t.dtype != x.dtype or t.device != x.device):
+            raise ValueError("residual, out and residual_out must match x")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    M, N, sx = _rows_view(x)
+    sr = _rows_view(residual)[2] if residual is not None else 0
+    sy = _rows_view(out)[2]
+    ss = _rows_view(residual_out)[2] if residual_out is not None else 0
+    ptr = lambda t: t.data_ptr() if t is not None else 0
+    return (x.data_ptr(), ptr(residual), weight.data_ptr(), out.data_ptr(), ptr(residual_out), M, N,
+            sx, sr, sy, ss), out
+
+
+def rmsnorm(x, weight, residual=None, eps: float = 1e-6, out=None, residual_out=None, opts=None,
+            workspace=None, stream=None):
+    """Fused residual RMSNorm along the last dimension of device tensors:
+    s = x + residual (FP32 add, rounded to x's dtype), out = s * weight / rms(s).
+    Writes s to ``residual_out`` when given. Returns ``out``."""
+    import torch
+    args, out = _rms_args(x, weight, residual, out, residual_out)
+    s = (stream if stream is not None else torch.cuda.current_stream(x.device)).cuda_stream
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        rc = sm_rmsnorm_fwd_ex(*args, float(eps), _torch_dtype_code(x), opts, ws_ptr, ws_bytes, s)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_rmsnorm_fwd_ex")
+    return out
+
+
+def plan_for_rmsnorm(x, weight, residual=None, eps: float = 1e-6, out=None, residual_out=None,
+                     opts=None, num_cus: int = 0) -> dict:
+    args, out = _rms_args(x, weight, residual, out, residual_out)
+    rc, info = sm_rmsnorm_plan_query(*args, float(eps), _torch_dtype_code(x), opts, num_cus)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_rmsnorm_plan_query")
+    return info.as_dict()

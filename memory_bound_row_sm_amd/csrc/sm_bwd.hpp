@@ -21,6 +21,12 @@
 
 namespace smx {
 
+// Value of a compensated pair. An infinite partial makes TwoSum's error term NaN
+// (inf - inf); the pair's value is then the infinite part itself.
+__device__ __forceinline__ float csum_value(float hi, float lo) {
+    return __builtin_isfinite(hi) ? hi + lo : hi;
+}
+
 // Decoded elements of dy for the windows of y: vector loads when dy shares y's
 // 16-byte phase, element loads otherwise. Columns outside [0, N) read as 0.
 template <int DT, int NV>
@@ -248,7 +254,8 @@ k_softmax_bwd_rows(const unsigned char* y, const unsigned char* dy, unsigned cha
         }
         float dot;
         if constexpr (DT == kF32) {
-            dot = row_sum_acc<G>(cs, lds_hi[parity], lds_lo[parity]);
+            const CSum c = row_csum<G>(cs, lds_hi[parity], lds_lo[parity]);
+            dot = csum_value(c.hi, c.lo);
         } else {
             dot = row_sum<G>(acc, lds_hi[parity]);
         }
@@ -338,7 +345,7 @@ k_bwd_wide_apply(const unsigned char* y, const unsigned char* dy, unsigned char*
         cs.lo = (cs.lo + p.y) + e;
     }
     cs = group_allreduce_csum<64>(cs);
-    const float dot = cs.hi + cs.lo;
+    const float dot = csum_value(cs.hi, cs.lo);
 
     const RowGeom<DT> g(y + row * y_sb, N);
     const int64_t nchunks = ((int64_t)g.nwin + WPC - 1) / WPC;

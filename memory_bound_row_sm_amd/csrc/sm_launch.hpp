@@ -50,6 +50,18 @@ using BwdSplitKernelFn = void (*)(const unsigned char*, const unsigned char*, un
                                   uint32_t, int, int, int);
 SplitKernelFn split_kernel(int dtype, int V, int NT);
 BwdSplitKernelFn bwd_split_kernel(int dtype, int V, int NT);
+
+// Residual RMSNorm (sm_rmsnorm.hip): one-pass rows (G in {16 ... 1024}, V in {1, 2, 4})
+// and split slices (V in {1, 2, 4}); slot and sync pointers as for the split kernels.
+using RmsRowKernelFn = void (*)(const unsigned char*, const unsigned char*, const unsigned char*,
+                                unsigned char*, unsigned char*, int64_t, int, int64_t, int64_t,
+                                int64_t, int64_t, float, int);
+using RmsSplitKernelFn = void (*)(const unsigned char*, const unsigned char*, const unsigned char*,
+                                  unsigned char*, unsigned char*, void*, void*, int64_t, int,
+                                  int64_t, int64_t, int64_t, int64_t, int, int, uint32_t, int,
+                                  float, int, int);
+RmsRowKernelFn rms_row_kernel(int dtype, int G, int V, int NT);
+RmsSplitKernelFn rms_split_kernel(int dtype, int V, int NT);
 BwdDotKernelFn bwd_dot_kernel(int dtype);
 BwdApplyKernelFn bwd_apply_kernel(int dtype);
 

@@ -16,6 +16,7 @@
 #include "sm_bwd.hpp"
 #include "sm_kernels.hpp"
 #include "sm_launch.hpp"
+#include "sm_rmsnorm.hpp"
 #include "sm_softmax.h"
 
 namespace smx {
@@ -446,9 +447,11 @@ int occ_row_live(void*, int dtype, int G, int V, int PF) {
 int occ_wide_live(void*, int dtype) {
     return occ_of(reinterpret_cast<const void*>(wide_stats_kernel(dtype, 0)), 256);
 }
-int occ_split_live(void*, int dtype, int V, int bwd) {
-    const void* fn = bwd ? reinterpret_cast<const void*>(bwd_split_kernel(dtype, V, 0))
-                         : reinterpret_cast<const void*>(split_kernel(dtype, V, 0));
+// kind: 0 softmax forward, 1 softmax backward, 2 residual RMSNorm
+int occ_split_live(void*, int dtype, int V, int kind) {
+    const void* fn = kind == 1   ? reinterpret_cast<const void*>(bwd_split_kernel(dtype, V, 0))
+                     : kind == 2 ? reinterpret_cast<const void*>(rms_split_kernel(dtype, V, 0))
+                                 : reinterpret_cast<const void*>(split_kernel(dtype, V, 0));
     return fn ? occ_of(fn, kSplitLanes) : 1;
 }
 int occ_row_host(void*, int, int G, int, int) { return std::max(1, 2048 / row_block(G)); }
@@ -827,12 +830,278 @@ int run_bwd(const BwdProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
     return rc;
 }
 
+// ------------------------------------------------------------ residual RMSNorm
+struct RmsProblem {
+    uintptr_t x, r, w, y, s;  // r and s may be 0
+    int64_t M, N, x_stride, r_stride, y_stride, s_stride;
+    float eps;
+    int dtype;
+};
+
+bool spans_meet(uintptr_t a, int64_t sa, uintptr_t b, int64_t sb) {
+    return !(a + (uint64_t)sa <= b || b + (uint64_t)sb <= a);
+}
+
+int validate_rms(const RmsProblem& p) {
+    if (p.dtype != SM_F32 && p.dtype != SM_F16 && p.dtype != SM_BF16) return SM_ERR_DTYPE;
+    if (p.M < 0 || p.N < 0) return SM_ERR_INVALID;
+    if (p.M == 0 || p.N == 0) return SM_OK;
+    if (!p.x || !p.w || !p.y) return SM_ERR_INVALID;
+    if (!(p.eps >= 0.f) || p.eps == __builtin_huge_valf()) return SM_ERR_INVALID;
+    const int es = elem_bytes(p.dtype);
+    if (p.w % es) return SM_ERR_INVALID;
+    // every (input, output) pair obeys the softmax rules: sizes, strides, alignment,
+    // spans, and no overlap other than exactly in place
+    int rc = validate(Problem{p.x, p.y, p.M, p.N, p.x_stride, p.y_stride, p.dtype});
+    if (rc != SM_OK) return rc;
+    if (p.r) {
+        rc = validate(Problem{p.r, p.y, p.M, p.N, p.r_stride, p.y_stride, p.dtype});
+        if (rc != SM_OK) return rc;
+    }
+    const int64_t wspan = p.N * es;
+    const int64_t yspan = span_bytes(p.M, p.N, p.y_stride, es);
+    if (p.w > UINTPTR_MAX - (uint64_t)wspan) return SM_ERR_INVALID;
+    if (spans_meet(p.w, wspan, p.y, yspan)) return SM_ERR_OVERLAP;  // every row reads w
+    if (p.s) {
+        rc = validate(Problem{p.x, p.s, p.M, p.N, p.x_stride, p.s_stride, p.dtype});
+        if (rc != SM_OK) return rc;
+        if (p.r) {
+            rc = validate(Problem{p.r, p.s, p.M, p.N, p.r_stride, p.s_stride, p.dtype});
+            if (rc != SM_OK) return rc;
+        }
+        const int64_t sspan = span_bytes(p.M, p.N, p.s_stride, es);
+        if (spans_meet(p.s, sspan, p.y, yspan) || spans_meet(p.w, wspan, p.s, sspan))
+            return SM_ERR_OVERLAP;
+    }
+    return SM_OK;
+}
+
+int occ_rms_live(int dtype, int G, int V) {
+    RmsRowKernelFn fn = rms_row_kernel(dtype, G, V, 0);
+    return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
+}
+
+int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool live,
+                  sm_plan_info* pi) {
+    *pi = sm_plan_info{};
+    const int es = elem_bytes(p.dtype);
+    const int E = 16 / es;
+    const bool x_aligned = (p.x % 16 == 0) && (p.M == 1 || (p.x_stride * es) % 16 == 0);
+    const int64_t nw_max = ((x_aligned ? 0 : E - 1) + p.N + E - 1) / E;
+    auto phase = [&](uintptr_t a, int64_t sa) {
+        return ((p.x - a) % 16 == 0) && (p.M == 1 || (((p.x_stride - sa) * es) % 16 == 0));
+    };
+    pi->same_phase = phase(p.y, p.y_stride);
+    pi->dy_same_phase = p.r ? phase(p.r, p.r_stride) : 1;
+    const int streams = 3 + (p.r ? 1 : 0) + (p.s ? 1 : 0);  // x, w, y (+ r, s)
+    if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
+    int plan = o.plan;
+    if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
+    const bool auto_plan = plan == SM_PLAN_AUTO;
+    if (auto_plan) plan = one_pass_rule(p.M, p.N, nw_max) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
+    auto occ_fn = live ? occ_split_live : occ_split_host;
+    if (plan == SM_PLAN_SPLIT || plan == SM_PLAN_WIDE) {
+        int64_t P = 0, grid = 0;
+        int V = o.vecs_per_lane;
+        bool fused = false;
+        if (plan == SM_PLAN_SPLIT) {
+            if (V) {
+                if (V != 1 && V != 2 && V != 4) return SM_ERR_PLAN;
+                const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
+                fused = split_geometry(p.M, nw_max, V, slots, o.grid, P, grid);
+            } else {
+                V = split_auto_v(p.M, nw_max, 4, cus, nullptr, p.dtype, 2, occ_fn, P, grid);
+                fused = V != 0;
+                if (fused && o.grid > 0) {
+                    const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
+                    fused = split_geometry(p.M, nw_max, V, slots, o.grid, P, grid);
+                }
+            }
+            if (!fused && !auto_plan) return SM_ERR_PLAN;
+        }
+        if (!fused) {
+            // two launches of the split kernel (publish, then gather and apply): no
+            // workgroup waits, so slices need not be resident together
+            if (!V) V = 4;
+            if (V != 1 && V != 2 && V != 4) return SM_ERR_PLAN;
+            const int64_t S = (int64_t)kSplitLanes * V;
+            P = std::max<int64_t>(1, (nw_max + S - 1) / S);
+            if (P > INT32_MAX || p.M > INT64_MAX / P) return SM_ERR_PLAN;
+            const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
+            grid = o.grid > 0 ? o.grid : std::max<int64_t>(1, slots);
+            grid = std::min<int64_t>(grid, p.M * P);
+            if (grid * kSplitLanes > kMaxThreadsPerLaunch) return SM_ERR_PLAN;
+        }
+        const int64_t model = (fused ? streams : streams + 1 + (p.r ? 1 : 0)) * p.M * p.N * es;
+        pi->plan = fused ? SM_PLAN_SPLIT : SM_PLAN_WIDE;
+        pi->lanes_per_row = kSplitLanes;
+        pi->vecs_per_lane = V;
+        pi->block = kSplitLanes;
+        pi->grid = grid;
+        pi->waves_per_row = P;
+        pi->slice_windows = (int)((nw_max + P - 1) / P);
+        pi->launches = fused ? 1 : 2;
+        pi->nt_loads = (o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes)) ? 1 : 0;
+        pi->workspace_bytes = ((p.M * P * 32 + 255) / 256) * 256;
+        pi->model_bytes = model;
+        return SM_OK;
+    }
+    int G = 0, V = 0;
+    if (!pick_shape(kShapesBwd, nw_max, o.lanes_per_row, o.vecs_per_lane, G, V)) return SM_ERR_PLAN;
+    if (!rms_row_kernel(p.dtype, G, V, 0) || (int64_t)G * V < nw_max) return SM_ERR_PLAN;
+    const int block = row_block(G);
+    const int gpb = block / G;
+    const int64_t groups = (p.M + gpb - 1) / gpb;
+    const int occ = live ? std::max(1, occ_rms_live(p.dtype, G, V)) : std::max(1, 2048 / block);
+    const int64_t slots = (int64_t)occ * cus;
+    if (auto_plan && groups <= 2 * slots) plan = SM_PLAN_PERSISTENT;
+    int64_t grid = o.grid > 0 ? o.grid : (plan == SM_PLAN_PERSISTENT ? slots : groups);
+    grid = std::max<int64_t>(1, std::min<int64_t>(std::min(grid, groups),
+                                                  kMaxThreadsPerLaunch / block));
+    const int64_t model = streams * p.M * p.N * es;
+    pi->plan = plan;
+    pi->lanes_per_row = G;
+    pi->vecs_per_lane = V;
+    pi->nt_loads = ((o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes)) && G >= 128) ? 1 : 0;
+    pi->block = block;
+    pi->grid = grid;
+    pi->launches = 1;
+    pi->model_bytes = model;
+    return SM_OK;
+}
+
+int launch_rms(const RmsProblem& p, const sm_plan_info& pi, void* ws, const sm_softmax_opts& o,
+               hipStream_t stream) {
+    const hipEvent_t ev0 = o.start_event, ev1 = o.stop_event;
+    const int es = elem_bytes(p.dtype);
+    const auto* x = reinterpret_cast<const unsigned char*>(p.x);
+    const auto* r = p.r ? reinterpret_cast<const unsigned char*>(p.r) : x;  // never read without flag
+    const auto* w = reinterpret_cast<const unsigned char*>(p.w);
+    auto* y = reinterpret_cast<unsigned char*>(p.y);
+    auto* sp = p.s ? reinterpret_cast<unsigned char*>(p.s) : y;  // never written without flag
+    const int64_t xsb = p.x_stride * es, ysb = p.y_stride * es;
+    const int64_t rsb = p.r ? p.r_stride * es : xsb, ssb = p.s ? p.s_stride * es : 0;
+    auto phase = [&](uintptr_t a, int64_t sa) {
+        return ((p.x - a) % 16 == 0) && (p.M == 1 || (((p.x_stride - sa) * es) % 16 == 0));
+    };
+    int flags = 0;
+    if (p.r) flags |= kRmsResidual | (pi.dy_same_phase ? kRmsResPhase : 0);
+    if (pi.same_phase) flags |= kRmsOutPhase;
+    if (p.s) flags |= kRmsSumOut | (phase(p.s, p.s_stride) ? kRmsSumPhase : 0);
+    const int N = (int)p.N;
+    hipError_t e;
+    if (pi.plan == SM_PLAN_SPLIT || pi.plan == SM_PLAN_WIDE) {
+        void* sync = split_sync(stream, true, &e);
+        if (!sync) return hip_fail(e);
+        RmsSplitKernelFn fn = rms_split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
+        if (!fn) return SM_ERR_PLAN;
+        const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
+        const uint32_t tag = next_tag();
+        const int P = (int)pi.waves_per_row;
+        if (pi.plan == SM_PLAN_SPLIT) {
+            e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
+                         stream, ev0, ev1, x, r, w, y, sp, ws, sync, p.M, N, xsb, rsb, ysb, ssb, P,
+                         pi.slice_windows, tag, spin, p.eps, flags, 0);
+            return e == hipSuccess ? SM_OK : hip_fail(e);
+        }
+        e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
+                     stream, ev0, nullptr, x, r, w, y, sp, ws, sync, p.M, N, xsb, rsb, ysb, ssb, P,
+                     pi.slice_windows, tag, spin, p.eps, flags, 1);
+        if (e != hipSuccess) return hip_fail(e);
+        e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
+                     stream, nullptr, ev1, x, r, w, y, sp, ws, sync, p.M, N, xsb, rsb, ysb, ssb, P,
+                     pi.slice_windows, tag, spin, p.eps, flags, 2);
+        return e == hipSuccess ? SM_OK : hip_fail(e);
+    }
+    RmsRowKernelFn fn = rms_row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.nt_loads);
+    if (!fn) return SM_ERR_PLAN;
+    e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(pi.block), stream,
+                 ev0, ev1, x, r, w, y, sp, p.M, N, xsb, rsb, ysb, ssb, p.eps, flags);
+    return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
+int run_rms(const RmsProblem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes,
+            hipStream_t stream) {
+    int rc = validate_rms(p);
+    if (rc != SM_OK || p.M == 0 || p.N == 0) return rc;
+    DeviceView dv;
+    rc = live_device(&dv);
+    if (rc != SM_OK) return rc;
+    const sm_softmax_opts o = opts_or_default(opts);
+    sm_plan_info pi;
+    rc = make_plan_rms(p, o, dv.cus, true, &pi);
+    if (rc != SM_OK) return rc;
+    if (pi.workspace_bytes == 0) return launch_rms(p, pi, nullptr, o, stream);
+    if (ws) {
+        if (ws_bytes < (size_t)pi.workspace_bytes || (reinterpret_cast<uintptr_t>(ws) & 15))
+            return SM_ERR_WORKSPACE;
+        return launch_rms(p, pi, ws, o, stream);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    keep_pool_memory(dev);
+    void* tmp = nullptr;
+    e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = launch_rms(p, pi, tmp, o, stream);
+    e = hipFreeAsync(tmp, stream);
+    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
+    return rc;
+}
+
 }  // namespace
 }  // namespace smx
 
 using namespace smx;
 
 extern "C" {
+
+int sm_rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* y,
+                   void* residual_out, int64_t M, int64_t N, int64_t x_stride, int64_t res_stride,
+                   int64_t y_stride, int64_t res_out_stride, float eps, int dtype,
+                   hipStream_t stream) {
+    return sm_rmsnorm_fwd_ex(x, residual, weight, y, residual_out, M, N, x_stride, res_stride,
+                             y_stride, res_out_stride, eps, dtype, nullptr, nullptr, 0, stream);
+}
+
+int sm_rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* y,
+                      void* residual_out, int64_t M, int64_t N, int64_t x_stride,
+                      int64_t res_stride, int64_t y_stride, int64_t res_out_stride, float eps,
+                      int dtype, const sm_softmax_opts* opts, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    const RmsProblem p{reinterpret_cast<uintptr_t>(x),  reinterpret_cast<uintptr_t>(residual),
+                       reinterpret_cast<uintptr_t>(weight), reinterpret_cast<uintptr_t>(y),
+                       reinterpret_cast<uintptr_t>(residual_out), M, N, x_stride, res_stride,
+                       y_stride, res_out_stride, eps, dtype};
+    return run_rms(p, opts, workspace, workspace_bytes, stream);
+}
+
+int sm_rmsnorm_plan_query(const void* x, const void* residual, const void* weight, const void* y,
+                          const void* residual_out, int64_t M, int64_t N, int64_t x_stride,
+                          int64_t res_stride, int64_t y_stride, int64_t res_out_stride, float eps,
+                          int dtype, const sm_softmax_opts* opts, int num_cus,
+                          sm_plan_info* info) {
+    if (!info) return SM_ERR_INVALID;
+    const RmsProblem p{reinterpret_cast<uintptr_t>(x),  reinterpret_cast<uintptr_t>(residual),
+                       reinterpret_cast<uintptr_t>(weight), reinterpret_cast<uintptr_t>(y),
+                       reinterpret_cast<uintptr_t>(residual_out), M, N, x_stride, res_stride,
+                       y_stride, res_out_stride, eps, dtype};
+    int rc = validate_rms(p);
+    if (rc != SM_OK) return rc;
+    if (M == 0 || N == 0) {
+        *info = sm_plan_info{};
+        return SM_OK;
+    }
+    int cus = num_cus;
+    if (cus <= 0) {
+        DeviceView dv;
+        rc = live_device(&dv);
+        if (rc != SM_OK) return rc;
+        cus = dv.cus;
+    }
+    return make_plan_rms(p, opts_or_default(opts), cus, num_cus <= 0, info);
+}
 
 int sm_softmax_fwd(const void* in, void* out, int64_t M, int64_t N, int64_t in_stride,
                    int64_t out_stride, int dtype, hipStream_t stream) {

@@ -214,7 +214,7 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
         split_gather<DT>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
         const float m = lds_stat[0];
-        const float s = lds_stat[1] + lds_stat[2];
+        const float s = csum_value(lds_stat[1], lds_stat[2]);
         const bool ok = lds_stat[3] != 0.f;
         if (!ok && lane == 0) atomicAdd(&sync->failures, 1u);
 
@@ -355,7 +355,7 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
         split_gather_sum<DT == kF32>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
         const bool ok = lds_stat[3] != 0.f;
-        const float dot = ok ? lds_stat[1] + lds_stat[2] : __builtin_nanf("");
+        const float dot = ok ? csum_value(lds_stat[1], lds_stat[2]) : __builtin_nanf("");
         if (!ok && lane == 0) atomicAdd(&sync->failures, 1u);
 
         unsigned char* dxrow = dx + row * dx_sb;

@@ -110,7 +110,9 @@ def compare_bwd(g: torch.Tensor, y: torch.Tensor, dy: torch.Tensor, rows=None,
     rt, sc, at = TOL_BWD[dt]
     nan_ref, nan_g = np.isnan(ref), np.isnan(gd)
     assert np.array_equal(nan_ref, nan_g), f"{what}: NaN pattern differs ({nan_ref.sum()} vs {nan_g.sum()})"
-    ok = ~nan_ref
+    inf_ref = np.isinf(ref)
+    assert np.array_equal(gd[inf_ref], ref[inf_ref]), f"{what}: infinities differ"
+    ok = ~nan_ref & ~inf_ref
     err = np.abs(gd[ok] - ref[ok])
     bound = rt * np.abs(ref[ok]) + sc * s[ok] + at
     bad = err > bound
@@ -119,5 +121,48 @@ def compare_bwd(g: torch.Tensor, y: torch.Tensor, dy: torch.Tensor, rows=None,
         i, j = int(idx[0]), int(idx[1])
         raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst at "
                              f"({i},{j}): gpu={gd[i, j]!r} ref={ref[i, j]!r} scale={s[i, j]!r}")
+    return {"max_abs": float(err.max()) if err.size else 0.0,
+            "worst_frac_of_tol": float(np.max(err / bound)) if err.size else 0.0, "n": int(err.size)}
+
+
+# ------------------------------------------------------------------ residual RMSNorm
+# The GPU forms s = x + r in FP32 and rounds once (equal to the correctly rounded
+# sum for every dtype here, so s must match the oracle bit for bit), sums s^2 in FP32
+# (compensated for FP32 data), and rounds y once. The FP32 value of y is within about
+# 1e-6 relative of the FP64 one, so the rounded result is the oracle's rounding or
+# its neighbour:
+#   FP16/BF16: |g - r| <= u |r| + a   (u = 2^-10 / 2^-7, one unit in the last place
+#              relative to |r|; a the dtype's subnormal spacing)
+#   FP32:      |g - y| <= 1e-6 |y| + 2^-126   (y the FP64 result)
+# (The pages' own BF16 tolerance for this kernel, 0.02 absolute and relative, is
+# looser than both.)
+TOL_RMS = {"f32": (1e-6, 2.0 ** -126), "f16": (2.0 ** -10, 2.0 ** -24), "bf16": (2.0 ** -7, 2.0 ** -133)}
+
+
+def compare_rms(g: torch.Tensor, x: torch.Tensor, r, w: torch.Tensor, eps: float, s_gpu=None,
+                rows=None, what: str = "") -> dict:
+    dt = workloads.dtype_name(x)
+    rs = None if r is None else workloads.storage_numpy(r)
+    y, yr, sr = oracle.reference_rmsnorm(workloads.storage_numpy(x), rs, workloads.storage_numpy(w),
+                                         dt, eps, rows=rows)
+    if s_gpu is not None:
+        sg = workloads.storage_numpy(s_gpu.detach().cpu().contiguous())
+        assert np.array_equal(sg, sr), f"{what}: residual_out differs from the rounded sum"
+    gd = to_f64(g)
+    ref = y if dt == "f32" else oracle.decode(yr, dt)
+    rt, at = TOL_RMS[dt]
+    nan_ref, nan_g = np.isnan(ref), np.isnan(gd)
+    assert np.array_equal(nan_ref, nan_g), f"{what}: NaN pattern differs ({nan_ref.sum()} vs {nan_g.sum()})"
+    inf_ref = np.isinf(ref)
+    assert np.array_equal(gd[inf_ref], ref[inf_ref]), f"{what}: infinities differ"
+    ok = ~nan_ref & ~inf_ref
+    err = np.abs(gd[ok] - ref[ok])
+    bound = rt * np.abs(ref[ok]) + at
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(ok)[np.argmax(err - bound)]
+        i, j = int(idx[0]), int(idx[1])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst at "
+                             f"({i},{j}): gpu={gd[i, j]!r} ref={ref[i, j]!r}")
     return {"max_abs": float(err.max()) if err.size else 0.0,
             "worst_frac_of_tol": float(np.max(err / bound)) if err.size else 0.0, "n": int(err.size)}

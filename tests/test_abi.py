@@ -278,3 +278,68 @@ def test_backward_plan_rule():
     assert p["dy_same_phase"] == 0
     rc, p = q(8, 1000, F16, {"vecs_per_lane": 8})
     assert rc == PLAN  # backward rows hold at most 4 vectors per lane
+
+
+# ------------------------------------------------------------------ residual RMSNorm
+X, R, W, Y, S = BASE, BASE * 2, BASE * 3, BASE * 4, BASE * 5
+
+
+def rms_q(M, N, dt, opts=None, r=R, s=0, eps=1e-6, **kw):
+    a = dict(x=X, r=r, w=W, y=Y, s=s, sx=N, sr=N, sy=N, ss=N)
+    a.update(kw)
+    rc, info = sm.sm_rmsnorm_plan_query(a["x"], a["r"], a["w"], a["y"], a["s"], M, N, a["sx"],
+                                        a["sr"], a["sy"], a["ss"], eps, dt, opts, 256)
+    return rc, info.as_dict()
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=9), DTYPE),
+    (dict(x=0), INVALID), (dict(w=0), INVALID), (dict(y=0), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(sx=7), INVALID), (dict(sr=7), INVALID), (dict(sy=7), INVALID),
+    (dict(y=X + 16), OVERLAP),              # y overlaps x partially
+    (dict(y=R + 4), OVERLAP),               # y overlaps the residual partially
+    (dict(w=Y + 8), OVERLAP),               # the weight inside y
+    (dict(s=Y), OVERLAP),                   # residual_out on y
+    (dict(s=X + 4), OVERLAP),               # residual_out overlaps x partially
+    (dict(w=S, s=S - 16), OVERLAP),         # the weight inside residual_out
+    (dict(y=X), OK), (dict(y=R), OK), (dict(s=R), OK), (dict(s=X, y=Y), OK),  # exactly in place
+    (dict(r=0), OK),
+])
+def test_rmsnorm_validation(kw, want):
+    dt = kw.pop("dt", F32)
+    eps = kw.pop("eps", 1e-6)
+    rc, _ = rms_q(4, 8, dt, eps=eps, **kw)
+    assert rc == want, (kw, rc)
+
+
+def test_rmsnorm_zero_size_and_no_device():
+    assert sm.sm_rmsnorm_fwd(X, R, W, Y, 0, 0, 8, 8, 8, 8, 8, 1e-6, F32, 0) == OK
+    rc = sm.sm_rmsnorm_fwd(X, R, W, Y, 0, 4, 8, 8, 8, 8, 8, 1e-6, F32, 0)
+    assert rc in (OK, NO_DEVICE)
+
+
+def test_rmsnorm_plan_rule():
+    rc, p = rms_q(64, 8192, BF16)  # 1024 windows: one-pass 256 x 4
+    assert rc == OK and p["plan_name"] == "persistent"
+    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 4)
+    assert p["model_bytes"] == 4 * 64 * 8192 * 2 and p["dy_same_phase"] == 1
+    rc, p = rms_q(64, 8192, BF16, s=S)  # + residual_out
+    assert p["model_bytes"] == 5 * 64 * 8192 * 2
+    rc, p = rms_q(64, 8192, BF16, r=0)  # plain RMSNorm
+    assert p["model_bytes"] == 3 * 64 * 8192 * 2
+    rc, p = rms_q(4, 32769, BF16)       # few wide rows: SPLIT, V=2, 9 slices
+    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 9)
+    assert p["slice_windows"] == 456 and p["launches"] == 1
+    assert p["workspace_bytes"] == (4 * 9 * 32 + 255) // 256 * 256
+    rc, p = rms_q(4, 32769, BF16, {"plan": sm.SM_PLAN_WIDE})  # two launches, x and r read twice
+    assert p["plan_name"] == "wide" and p["launches"] == 2
+    assert p["model_bytes"] == 6 * 4 * 32769 * 2
+    rc, p = rms_q(1, 1 << 26, BF16)     # slices cannot be resident together: two launches
+    assert rc == OK and p["plan_name"] == "wide" and p["vecs_per_lane"] == 4
+    rc, p = rms_q(1, 1 << 26, BF16, {"plan": sm.SM_PLAN_SPLIT})
+    assert rc == PLAN
+    rc, p = rms_q(8, 1000, F16, {"vecs_per_lane": 8})
+    assert rc == PLAN                   # rows hold at most 4 vectors per lane
+    rc, p = rms_q(8, 1000, F16, r=R + 2)  # residual at another 16-byte phase
+    assert p["dy_same_phase"] == 0

@@ -91,6 +91,19 @@ def test_in_place(plan):
         compare_bwd(yd, y, dy, what=f"bwd in place over y {plan}")
 
 
+def test_infinite_dy():
+    """dy = +inf where y > 0 makes the dot +inf: dx is -inf where y > 0 and dy is finite,
+    NaN at the infinite entry (inf - inf) and where y = 0 (0 * -inf) -- on every plan,
+    in FP32 as in the FP64 oracle."""
+    for plan in ["resident", "persistent", "wide", "split"]:
+        y, dy = inputs(3, 3000, "f32", seed=6)
+        y[1, 100:200] = 0.0
+        dy[1, 17] = math.inf
+        g = run_bwd(y.to(DEV), dy.to(DEV), plan).cpu()
+        compare_bwd(g, y, dy, what=f"bwd +inf {plan}")
+        assert torch.isinf(g[1]).sum() > 0 and torch.isfinite(g[0]).all()
+
+
 def test_nan_rows():
     for plan in ["resident", "wide", "split"]:
         y, dy = inputs(3, 3000, "f32", seed=5)

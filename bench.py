@@ -171,7 +171,7 @@ def main(argv=None) -> int:
                          "summary as one JSON line, and exit")
     ap.add_argument("--grid-runs", type=int, default=2, help="repeat runs of the plan grid")
     ap.add_argument("--grid-steps", type=int, default=10, help="timed cold calls per plan and cell")
-    ap.add_argument("--grid-op", default="fwd", choices=["fwd", "bwd"])
+    ap.add_argument("--grid-op", default="fwd", choices=["fwd", "bwd", "rms"])
     ap.add_argument("--score-grid", metavar="GRID_JSON",
                     help="print the regret summary of a plan-grid file and exit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -535,6 +535,7 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
             raise RuntimeError("sm_bench_flush failed")
 
     bwd = args.grid_op == "bwd"
+    rms = args.grid_op == "rms"
     runs = []
     for run in range(args.grid_runs):
         cells = []
@@ -543,10 +544,13 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
             for M in GRID_ROWS:
                 x = (torch.randn(M, N, device=dev, generator=gen) * 3).to(torch.bfloat16)
                 out = torch.empty_like(x)
-                dy = None
+                dy = w = None
                 if bwd:
                     sm.softmax(x, out=x)  # y
                     dy = torch.randn(M, N, device=dev, generator=gen).to(torch.bfloat16)
+                if rms:  # residual and weight
+                    dy = torch.randn(M, N, device=dev, generator=gen).to(torch.bfloat16)
+                    w = (1 + 0.5 * torch.randn(N, device=dev, generator=gen)).to(torch.bfloat16)
                 keys, times, model = {}, {}, {}
                 for key, o in GRID_PLANS.items():
                     opts = sm._opts(o)
@@ -554,6 +558,10 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                         rc, info = sm.sm_softmax_bwd_plan_query(
                             x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N, N, N, N, sm.SM_BF16,
                             opts, 0)
+                    elif rms:
+                        rc, info = sm.sm_rmsnorm_plan_query(
+                            x.data_ptr(), dy.data_ptr(), w.data_ptr(), out.data_ptr(), 0, M, N, N, N,
+                            N, 0, 1e-6, sm.SM_BF16, opts, 0)
                     else:
                         rc, info = sm.sm_softmax_plan_query(x.data_ptr(), out.data_ptr(), M, N, N, N,
                                                             sm.SM_BF16, opts, 0)
@@ -569,6 +577,10 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                         if bwd:
                             r = sm.sm_softmax_bwd_ex(x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N,
                                                      N, N, N, sm.SM_BF16, opts, 0, 0, s_handle)
+                        elif rms:
+                            r = sm.sm_rmsnorm_fwd_ex(x.data_ptr(), dy.data_ptr(), w.data_ptr(),
+                                                     out.data_ptr(), 0, M, N, N, N, N, 0, 1e-6,
+                                                     sm.SM_BF16, opts, 0, 0, s_handle)
                         else:
                             r = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N,
                                                      sm.SM_BF16, opts, 0, 0, s_handle)
@@ -586,7 +598,7 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                     ev.close()
                     model[sig] = int(info.model_bytes)
                 cells.append({"M": M, "N": N, "keys": keys, "us": times})
-                del x, out, dy
+                del x, out, dy, w
             torch.cuda.empty_cache()
             log(f"[grid] run {run + 1}: width {N} done ({len(cells)} cells)")
         runs.append(cells)
@@ -640,7 +652,9 @@ def score_grid(data: dict) -> dict:
 
 
 def sweep(torch, sm, workloads, flush, s_handle, log, args):
-    """Cold timing of every workload under every plan that can take it."""
+    """Cold timing of every workload under every plan that can take it (softmax forward
+    and backward), then the residual RMSNorm shapes."""
+    sweep_rmsnorm(torch, sm, flush, s_handle, log, max(20, args.steps // 4))
     names = ["normal_f32_128x781", "normal_bf16_4096x4096",
              *[f"spiky_f16_8192x{n}" for n in workloads.SPIKE_WIDTHS],
              "offset_bf16_64x131072", "causal_bf16_524288x2048"]
@@ -706,6 +720,60 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
             log("[sweep] " + json.dumps(line))
         del x, out, dy
         torch.cuda.empty_cache()
+
+
+# residual RMSNorm shapes: the FP16 shapes of "Measured optimization case studies"
+# (residual RMSNorm section) and the BF16 batch x hidden shapes of the Warpline README
+RMS_SHAPES = [("f16", 32, 127), ("f16", 1024, 1024), ("f16", 512, 4097), ("f16", 16384, 4096),
+              ("f16", 4, 32769), ("f16", 64, 131072), ("bf16", 1, 1024), ("bf16", 8, 1024),
+              ("bf16", 16, 2048), ("bf16", 32, 4096), ("bf16", 64, 4096), ("bf16", 64, 8192)]
+
+
+def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
+    """Cold timing of the residual RMSNorm (y only) under every plan that can take it."""
+    plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    code = {"f16": sm.SM_F16, "bf16": sm.SM_BF16}
+    gen = torch.Generator(device="cuda").manual_seed(2026)
+    for dt, M, N in RMS_SHAPES:
+        x = (torch.randn(M, N, device="cuda", generator=gen) * 2).to(tdt[dt])
+        r = torch.randn(M, N, device="cuda", generator=gen).to(tdt[dt])
+        w = (1 + 0.5 * torch.randn(N, device="cuda", generator=gen)).to(tdt[dt])
+        y = torch.empty_like(x)
+        for pname, p in plans.items():
+            o = sm.SmOpts()
+            o.plan = p
+            rc, info = sm.sm_rmsnorm_plan_query(x.data_ptr(), r.data_ptr(), w.data_ptr(), y.data_ptr(),
+                                                0, M, N, N, N, N, 0, 1e-6, code[dt], o, 0)
+            if rc != 0:
+                continue
+
+            def call(events=(None, None)):
+                o.start_event, o.stop_event = events
+                rc = sm.sm_rmsnorm_fwd_ex(x.data_ptr(), r.data_ptr(), w.data_ptr(), y.data_ptr(), 0, M,
+                                          N, N, N, N, 0, 1e-6, code[dt], o, 0, 0, s_handle)
+                if rc != 0:
+                    raise sm.SoftmaxError(rc)
+
+            for _ in range(5):
+                flush()
+                call()
+            t = DispatchEvents(steps)
+            for _ in range(steps):
+                flush()
+                call(t.next_pair())
+            st = stats_us(t.samples_ms(torch))
+            t.close()
+            line = {"workload": f"rmsnorm_{dt}_{M}x{N}", "op": "rmsnorm", "plan": pname,
+                    "resolved": info.as_dict()["plan_name"], "G": info.lanes_per_row,
+                    "V": info.vecs_per_lane, "cpw": info.waves_per_row, "grid": info.grid,
+                    "model_bytes": info.model_bytes, "mean_us": round(st["mean_us"], 3),
+                    "median_us": round(st["median_us"], 3),
+                    "GBps": round(info.model_bytes / (st["mean_us"] * 1e-6) / 1e9, 1),
+                    "pct_peak": round(100 * info.model_bytes / (st["mean_us"] * 1e-6) / 1e9 / PEAK_GBPS, 2)}
+            log("[sweep] " + json.dumps(line))
+        del x, r, w, y
+    torch.cuda.empty_cache()
 
 
 def time_backward(torch, sm, y, dy, plan, flush, s_handle, steps, warmup):

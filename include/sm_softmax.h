@@ -253,9 +253,11 @@ int sm_softmax_bwd_plan_query(const void *y, const void *dy, const void *dx, int
  * RESIDENT/PERSISTENT rows (up to 4 vectors per lane), SPLIT for wide rows (one
  * launch, partial sums of squares exchanged between the row's workgroups), and
  * WIDE as two launches of the split kernel (publish, then gather and apply) when
- * a row's slices cannot be resident together. model_bytes counts x, w, y and, when
- * present, the residual and residual_out once per element (w per row, as the
- * pages' byte model does); WIDE reads x and the residual twice.
+ * a row's slices cannot be resident together, or when rows need more than 32
+ * slices and several rounds (measured faster). model_bytes counts the compulsory
+ * HBM bytes: x, y and, when present, the residual and residual_out once per element,
+ * w once (N elements); WIDE reads x and the residual twice. (The pages' requested-
+ * byte convention counts w once per row in addition.)
  * Returns SM_OK or a negative sm_status; validation as for sm_softmax_fwd.
  */
 int sm_rmsnorm_fwd(const void *x, const void *residual, const void *weight, void *y,

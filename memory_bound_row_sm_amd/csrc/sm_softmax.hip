@@ -225,11 +225,13 @@ bool split_geometry(int64_t M, int64_t nw, int V, int64_t cap_slots, int64_t fix
 }
 
 // Automatic SPLIT shape, in order of preference:
-//   1. the smallest V >= 2 whose rows need at most kSplitMaxAutoSlices slices and
+//   1. the smallest V >= vmin whose rows need at most kSplitMaxAutoSlices slices and
 //      whose slices of all rows fit in one round (most workgroups in flight);
-//   2. with rounds unavoidable, V = 4 when rows need at most kSplitRoundSlices
-//      slices of 1024 windows (shorter rounds than V = 8 at the same traffic);
+//   2. with rounds unavoidable, V = vround when rows need at most kSplitRoundSlices
+//      slices (shorter rounds than the widest slices at the same traffic);
 //   3. the largest V that fits at all (fewest slices per row).
+// Softmax: vmin = 2, vround = 4. Residual RMSNorm (it holds x, the residual and the
+// weight in registers): vmin = 1, vround = 2.
 // Returns 0 when no V fits. Measured on MI355X, cold BF16 (us, V = 1 / 2 / 4 / 8):
 // 1 x 1048576: 7.6 / 6.2 / 5.7 / 6.6; 8 x 262144: 5.8 / 5.4 / 5.6 / 6.9; 16 x 65536:
 // 4.6 / 4.5 / 5.1 / 6.4; 64 x 131072: - / 13.8 / 11.3 / 11.1. On the row-plan grid
@@ -239,12 +241,12 @@ bool split_geometry(int64_t M, int64_t nw, int V, int64_t cap_slots, int64_t fix
 constexpr int64_t kSplitMaxAutoSlices = 128;
 constexpr int64_t kSplitRoundSlices = 16;
 
-int split_auto_v(int64_t M, int64_t nw, int vmax, int64_t cus, void* ctx, int dtype, int bwd,
-                 int (*occ)(void*, int, int, int), int64_t& P, int64_t& grid) {
+int split_auto_v(int64_t M, int64_t nw, int vmin, int vmax, int vround, int64_t cus, void* ctx,
+                 int dtype, int bwd, int (*occ)(void*, int, int, int), int64_t& P, int64_t& grid) {
     int64_t cp[4] = {0, 0, 0, 0}, cg[4] = {0, 0, 0, 0};
     bool ok[4] = {false, false, false, false};
     int vs[4] = {0, 0, 0, 0}, n = 0;
-    for (int v = 2; v <= vmax; v *= 2, ++n) {
+    for (int v = vmin; v <= vmax; v *= 2, ++n) {
         const int64_t slots = (int64_t)std::max(1, occ(ctx, dtype, v, bwd)) * cus;
         vs[n] = v;
         ok[n] = split_geometry(M, nw, v, slots, 0, cp[n], cg[n]);
@@ -257,10 +259,10 @@ int split_auto_v(int64_t M, int64_t nw, int vmax, int64_t cus, void* ctx, int dt
         }
     }
     for (int i = 0; i < n; ++i) {  // 2
-        if (ok[i] && vs[i] == 4 && cp[i] <= kSplitRoundSlices) {
+        if (ok[i] && vs[i] == vround && cp[i] <= kSplitRoundSlices) {
             P = cp[i];
             grid = cg[i];
-            return 4;
+            return vround;
         }
     }
     for (int i = n - 1; i >= 0; --i) {  // 3
@@ -297,7 +299,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
             const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
             if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
         } else {
-            V = split_auto_v(p.M, nw_max, 8, dev.cus, dev.ctx, p.dtype, 0, dev.occ_split, P, grid);
+            V = split_auto_v(p.M, nw_max, 2, 8, 4, dev.cus, dev.ctx, p.dtype, 0, dev.occ_split, P, grid);
             if (V && o.grid > 0) {
                 const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
                 if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
@@ -682,7 +684,7 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
             const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 1)) * cus;
             if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
         } else {
-            V = split_auto_v(p.M, nw_max, 4, cus, nullptr, p.dtype, 1, occ_fn, P, grid);
+            V = split_auto_v(p.M, nw_max, 2, 4, 4, cus, nullptr, p.dtype, 1, occ_fn, P, grid);
             if (V && o.grid > 0) {
                 const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 1)) * cus;
                 if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
@@ -876,6 +878,8 @@ int validate_rms(const RmsProblem& p) {
     return SM_OK;
 }
 
+constexpr int64_t kRmsTwoLaunchSlices = 32;
+
 int occ_rms_live(int dtype, int G, int V) {
     RmsRowKernelFn fn = rms_row_kernel(dtype, G, V, 0);
     return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
@@ -893,7 +897,9 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
     };
     pi->same_phase = phase(p.y, p.y_stride);
     pi->dy_same_phase = p.r ? phase(p.r, p.r_stride) : 1;
-    const int streams = 3 + (p.r ? 1 : 0) + (p.s ? 1 : 0);  // x, w, y (+ r, s)
+    // compulsory HBM bytes: x, y (+ residual, residual_out) per element, w once
+    const int streams = 2 + (p.r ? 1 : 0) + (p.s ? 1 : 0);
+    const int64_t wbytes = p.N * es;
     if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
     int plan = o.plan;
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
@@ -910,8 +916,11 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
                 const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
                 fused = split_geometry(p.M, nw_max, V, slots, o.grid, P, grid);
             } else {
-                V = split_auto_v(p.M, nw_max, 4, cus, nullptr, p.dtype, 2, occ_fn, P, grid);
+                V = split_auto_v(p.M, nw_max, 1, 4, 2, cus, nullptr, p.dtype, 2, occ_fn, P, grid);
                 fused = V != 0;
+                // many slices per row and several rounds: two launches without waits
+                // measured faster (width 1048576, 8 to 1024 rows: 6 to 15%)
+                if (fused && auto_plan && p.M * P > grid && P > kRmsTwoLaunchSlices) fused = false;
                 if (fused && o.grid > 0) {
                     const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
                     fused = split_geometry(p.M, nw_max, V, slots, o.grid, P, grid);
@@ -932,7 +941,7 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
             grid = std::min<int64_t>(grid, p.M * P);
             if (grid * kSplitLanes > kMaxThreadsPerLaunch) return SM_ERR_PLAN;
         }
-        const int64_t model = (fused ? streams : streams + 1 + (p.r ? 1 : 0)) * p.M * p.N * es;
+        const int64_t model = (fused ? streams : streams + 1 + (p.r ? 1 : 0)) * p.M * p.N * es + wbytes;
         pi->plan = fused ? SM_PLAN_SPLIT : SM_PLAN_WIDE;
         pi->lanes_per_row = kSplitLanes;
         pi->vecs_per_lane = V;
@@ -958,7 +967,7 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
     int64_t grid = o.grid > 0 ? o.grid : (plan == SM_PLAN_PERSISTENT ? slots : groups);
     grid = std::max<int64_t>(1, std::min<int64_t>(std::min(grid, groups),
                                                   kMaxThreadsPerLaunch / block));
-    const int64_t model = streams * p.M * p.N * es;
+    const int64_t model = streams * p.M * p.N * es + wbytes;
     pi->plan = plan;
     pi->lanes_per_row = G;
     pi->vecs_per_lane = V;

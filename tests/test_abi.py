@@ -320,21 +320,28 @@ def test_rmsnorm_zero_size_and_no_device():
 
 
 def test_rmsnorm_plan_rule():
+    # model_bytes: compulsory HBM bytes (x, y, residual, residual_out per element; w once)
     rc, p = rms_q(64, 8192, BF16)  # 1024 windows: one-pass 256 x 4
     assert rc == OK and p["plan_name"] == "persistent"
     assert (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 4)
-    assert p["model_bytes"] == 4 * 64 * 8192 * 2 and p["dy_same_phase"] == 1
+    assert p["model_bytes"] == 3 * 64 * 8192 * 2 + 8192 * 2 and p["dy_same_phase"] == 1
     rc, p = rms_q(64, 8192, BF16, s=S)  # + residual_out
-    assert p["model_bytes"] == 5 * 64 * 8192 * 2
+    assert p["model_bytes"] == 4 * 64 * 8192 * 2 + 8192 * 2
     rc, p = rms_q(64, 8192, BF16, r=0)  # plain RMSNorm
-    assert p["model_bytes"] == 3 * 64 * 8192 * 2
-    rc, p = rms_q(4, 32769, BF16)       # few wide rows: SPLIT, V=2, 9 slices
-    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 9)
-    assert p["slice_windows"] == 456 and p["launches"] == 1
-    assert p["workspace_bytes"] == (4 * 9 * 32 + 255) // 256 * 256
+    assert p["model_bytes"] == 2 * 64 * 8192 * 2 + 8192 * 2
+    rc, p = rms_q(4, 32769, BF16)       # few wide rows: SPLIT, V=1, 17 slices of 241 windows
+    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (1, 17)
+    assert p["slice_windows"] == 241 and p["launches"] == 1
+    assert p["workspace_bytes"] == (4 * 17 * 32 + 255) // 256 * 256
     rc, p = rms_q(4, 32769, BF16, {"plan": sm.SM_PLAN_WIDE})  # two launches, x and r read twice
     assert p["plan_name"] == "wide" and p["launches"] == 2
-    assert p["model_bytes"] == 6 * 4 * 32769 * 2
+    assert p["model_bytes"] == 5 * 4 * 32769 * 2 + 32769 * 2
+    rc, p = rms_q(8, 1 << 20, BF16)     # 128 slices, one round: SPLIT
+    assert p["plan_name"] == "split" and p["grid"] == 1024
+    rc, p = rms_q(16, 1 << 20, BF16)    # 128 slices in two rounds: two launches without waits
+    assert p["plan_name"] == "wide" and p["launches"] == 2
+    rc, p = rms_q(16, 1 << 20, BF16, {"plan": sm.SM_PLAN_SPLIT})  # forced: rounds are allowed
+    assert p["plan_name"] == "split"
     rc, p = rms_q(1, 1 << 26, BF16)     # slices cannot be resident together: two launches
     assert rc == OK and p["plan_name"] == "wide" and p["vecs_per_lane"] == 4
     rc, p = rms_q(1, 1 << 26, BF16, {"plan": sm.SM_PLAN_SPLIT})

@@ -1,5 +1,5 @@
-"""FP64 row-softmax oracle (forward, backward, fused residual RMSNorm): a ctypes
-wrapper over ``liboracle_softmax.so``.
+"""FP64 row-softmax oracle (forward, backward, fused residual RMSNorm, attention):
+a ctypes wrapper over ``liboracle_softmax.so``.
 
 TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
 bench's CPU-baseline leg may import this package. The GPU library and its
@@ -67,9 +67,13 @@ class Oracle:
                                                 ctypes.c_int]
         lib.oracle_rmsnorm_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, vp, i64,
                                             ctypes.c_double, _DP, _DP, ctypes.c_int]
+        lib.oracle_attention_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                              i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                                              vp, i64, _DP, _DP, ctypes.c_int]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_softmax_rows,
-                  lib.oracle_softmax_bwd_rows, lib.oracle_rmsnorm_rows, lib.oracle_max_threads):
+                  lib.oracle_softmax_bwd_rows, lib.oracle_rmsnorm_rows, lib.oracle_attention_rows,
+                  lib.oracle_max_threads):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -215,6 +219,47 @@ class Oracle:
         return y, self.encode(y, dtype), self.encode(s, dtype)
 
 
+    def attention_f64(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype, scale: float,
+                      causal: bool, rows=None, threads: int = 0):
+        """(o_f64, lse_f64): attention of stored [BH, S, d] tensors (views with unit
+        column stride allowed); ``rows`` selects flat rows h * Sq + i."""
+        a, b, c = (_as_storage(t, dtype) for t in (q, k, v))
+        if a.ndim != 3 or b.ndim != 3 or c.ndim != 3:
+            raise ValueError("expected [BH, S, d] tensors")
+        BH, Sq, d = a.shape
+        Sk = b.shape[1]
+        if b.shape != (BH, Sk, d) or c.shape != (BH, Sk, d):
+            raise ValueError("k and v must be [BH, Sk, d] with q's BH and d")
+        es = a.dtype.itemsize
+        st = []
+        for t in (a, b, c):
+            if t.shape[2] > 1 and t.strides[2] != es:
+                raise ValueError("the last dimension must be contiguous")
+            if any(x % es or x < 0 for x in t.strides[:2]):
+                raise ValueError("strides must be non-negative multiples of the element size")
+            st += [t.strides[1] // es, t.strides[0] // es]
+        nrows = BH * Sq if rows is None else len(rows)
+        idx = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        if idx is not None and idx.size and (idx.min() < 0 or idx.max() >= BH * Sq):
+            raise IndexError("row index out of range")
+        o = np.empty((nrows, d), np.float64)
+        lse = np.empty(nrows, np.float64)
+        if nrows == 0:
+            return o, lse
+        rc = self.lib.oracle_attention_rows(
+            a.ctypes.data, b.ctypes.data, c.ctypes.data, _code(dtype), BH, Sq, Sk, d, *st,
+            float(scale), int(bool(causal)), None if idx is None else idx.ctypes.data, nrows,
+            o.ctypes.data_as(_DP), lse.ctypes.data_as(_DP), int(threads))
+        if rc:
+            raise ValueError("oracle_attention_rows rejected its arguments")
+        return o, lse
+
+    def reference_attention(self, q, k, v, dtype, scale, causal, rows=None, threads: int = 0):
+        """(o_f64, o_rounded, lse_f64)."""
+        o, lse = self.attention_f64(q, k, v, dtype, scale, causal, rows=rows, threads=threads)
+        return o, self.encode(o, dtype), lse
+
+
 _default = None
 
 
@@ -263,3 +308,11 @@ def rmsnorm_f64(x, residual, weight, dtype, eps, rows=None, threads: int = 0):
 
 def reference_rmsnorm(x, residual, weight, dtype, eps, rows=None, threads: int = 0):
     return default().reference_rmsnorm(x, residual, weight, dtype, eps, rows=rows, threads=threads)
+
+
+def attention_f64(q, k, v, dtype, scale, causal, rows=None, threads: int = 0):
+    return default().attention_f64(q, k, v, dtype, scale, causal, rows=rows, threads=threads)
+
+
+def reference_attention(q, k, v, dtype, scale, causal, rows=None, threads: int = 0):
+    return default().reference_attention(q, k, v, dtype, scale, causal, rows=rows, threads=threads)

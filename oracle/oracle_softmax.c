@@ -50,6 +50,15 @@
  *   3. y_j = s_j * w_j / sqrt(q / N + eps) in double (eps is the caller's; the
  *      pages give no value).
  *
+ * Scaled dot-product attention with the online softmax's result ("Fused Softmax on
+ * GPU", its closing section: fusing the softmax with the matmul before it is what
+ * FlashAttention does; the attention-logit workload of the same pages), per (head,
+ * query) row i, from stored q, k, v, in FP64:
+ *   1. S_j = scale * sum_d q_id k_jd for every key j; with the causal mask, keys
+ *      j > i + (Sk - Sq) are -inf (the last query sees every key);
+ *   2. P = softmax(S) exactly as above (an all -inf row gives zeros);
+ *   3. O_id = sum_j P_j v_jd; lse_i = m + log(s) (-inf for an all -inf row).
+ *
  * Readings where the pages are silent (listed in the design notes too):
  *   - a row whose entries are all -inf (and an empty row) has no finite
  *     maximum; the online-merge guard of "Measured optimization case studies",
@@ -358,6 +367,83 @@ int oracle_rmsnorm_rows(const void *x, const void *r, const void *w, int dtype, 
             if (s_out) memcpy(s_out + (size_t)k * (size_t)cols, a, sizeof(double) * (size_t)cols);
         }
         free(a);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Attention of selected rows.
+ *   q, k, v   : stored [BH][S][d] tensors (same dtype), element (h, i, c) at
+ *               base + h * head_stride + i * row_stride + c
+ *   rows      : flat row indices h * Sq + i, or NULL for all BH * Sq rows
+ *   o         : output, nrows x d doubles; lse: nrows doubles (may be NULL)
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_attention_rows(const void *q, const void *k, const void *v, int dtype, int64_t BH,
+                          int64_t Sq, int64_t Sk, int64_t d, int64_t q_rs, int64_t q_hs,
+                          int64_t k_rs, int64_t k_hs, int64_t v_rs, int64_t v_hs, double scale,
+                          int causal, const int64_t *rows, int64_t nrows, double *o, double *lse,
+                          int threads) {
+    int es = elem_size(dtype);
+    if (!es || BH < 0 || Sq < 0 || Sk < 0 || d <= 0 || nrows < 0) return -1;
+    if (nrows == 0) return 0;
+    const unsigned char *qb = (const unsigned char *)q;
+    const unsigned char *kb = (const unsigned char *)k;
+    const unsigned char *vb = (const unsigned char *)v;
+#ifdef _OPENMP
+    if (threads <= 0) threads = omp_get_max_threads();
+#else
+    threads = 1;
+#endif
+    int bad = 0;
+#pragma omp parallel num_threads(threads) reduction(| : bad)
+    {
+        double *buf = (double *)malloc(sizeof(double) * (size_t)(d + 2 * (Sk > 0 ? Sk : 1)));
+        if (!buf) bad = 1;
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < nrows; ++t) {
+            if (!buf) continue;
+            const int64_t r = rows ? rows[t] : t;
+            if (r < 0 || r >= BH * Sq) {
+                bad = 1;
+                continue;
+            }
+            const int64_t h = r / Sq, i = r % Sq;
+            double *qi = buf, *sv = buf + d, *pv = buf + d + Sk;
+            for (int64_t c = 0; c < d; ++c)
+                qi[c] = load_elem(qb + (size_t)(h * q_hs + i * q_rs + c) * es, dtype);
+            for (int64_t j = 0; j < Sk; ++j) {
+                if (causal && j > i + (Sk - Sq)) {
+                    sv[j] = -INFINITY;
+                    continue;
+                }
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    acc += qi[c] * load_elem(kb + (size_t)(h * k_hs + j * k_rs + c) * es, dtype);
+                sv[j] = scale * acc;
+            }
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Sk; ++j)
+                if (sv[j] > m) m = sv[j];
+            softmax_row(sv, Sk, pv);
+            double *oi = o + (size_t)t * (size_t)d;
+            for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+            for (int64_t j = 0; j < Sk; ++j) {
+                if (sv[j] == -INFINITY) continue; /* masked keys do not take part */
+                for (int64_t c = 0; c < d; ++c)
+                    oi[c] += pv[j] * load_elem(vb + (size_t)(h * v_hs + j * v_rs + c) * es, dtype);
+            }
+            if (lse) {
+                if (m == -INFINITY) {
+                    lse[t] = -INFINITY;
+                } else {
+                    double ssum = 0.0;
+                    for (int64_t j = 0; j < Sk; ++j) ssum += exp(sv[j] - m);
+                    lse[t] = m + log(ssum);
+                }
+            }
+        }
+        free(buf);
     }
     return bad ? -1 : 0;
 }

@@ -1,7 +1,8 @@
 """Planted mistakes: each one, compiled into a scratch copy of the oracle on the CPU,
 must fail at least one pin. This shows that the pins constrain every step of the
 oracle (decode, max, exp, sum, divide, row indexing, the all--inf reading, the
-one-step RNE encode, the backward, the residual RMSNorm), not just its happy path.
+one-step RNE encode, the backward, the residual RMSNorm, the attention), not just its
+happy path.
 
 The mutants are built from the committed C source with plain text edits and gcc;
 nothing here touches the GPU or the GPU library.
@@ -54,6 +55,12 @@ MUTANTS = [
     ("rms weight index", "a[cols + j] = load_elem(wb + (size_t)j * es, dtype);",
      "a[cols + j] = load_elem(wb, dtype);"),
     ("rms residual stride", "(size_t)(row * r_stride)", "(size_t)(row * x_stride)"),
+    ("attn drops scale", "sv[j] = scale * acc;", "sv[j] = acc;"),
+    ("attn mask off by one", "if (causal && j > i + (Sk - Sq))", "if (causal && j >= i + (Sk - Sq))"),
+    ("attn mask top-left", "if (causal && j > i + (Sk - Sq))", "if (causal && j > i)"),
+    ("attn reads k for v", "vb + (size_t)(h * v_hs + j * v_rs + c)", "kb + (size_t)(h * k_hs + j * k_rs + c)"),
+    ("attn k head stride", "kb + (size_t)(h * k_hs", "kb + (size_t)(h * q_hs"),
+    ("attn lse drops max", "lse[t] = m + log(ssum);", "lse[t] = log(ssum);"),
 ]
 
 
@@ -189,7 +196,22 @@ def pin_battery(orc: "oracle.Oracle"):
                                np.ascontiguousarray(rb.numpy()[:, 7:37]), w.numpy(), "f32", 1e-6)
         return np.array_equal(a, b)
 
-    for name, fn in [("rms vs torch", rms_torch), ("rms strided", rms_strided),
+    def attn_torch():
+        import torch.nn.functional as F
+        g = torch.Generator().manual_seed(8)
+        q = torch.randn(2, 6, 8, generator=g).to(torch.bfloat16)
+        k = torch.randn(2, 9, 8, generator=g).to(torch.bfloat16)
+        v = torch.randn(2, 9, 8, generator=g).to(torch.bfloat16)
+        stn = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+        o, lse = orc.attention_f64(stn(q), stn(k), stn(v), "bf16", 0.3, True)
+        mask = torch.arange(9)[None, :] <= torch.arange(6)[:, None] + 3
+        want = F.scaled_dot_product_attention(q.double(), k.double(), v.double(), attn_mask=mask,
+                                              scale=0.3).reshape(12, 8).numpy()
+        s = (torch.einsum("hid,hjd->hij", q.double(), k.double()) * 0.3).masked_fill(~mask, -math.inf)
+        wl = torch.logsumexp(s, -1).reshape(12).numpy()
+        return np.allclose(o, want, rtol=1e-12, atol=1e-14) and np.allclose(lse, wl, rtol=1e-13)
+
+    for name, fn in [("attn vs torch", attn_torch), ("rms vs torch", rms_torch), ("rms strided", rms_strided),
                      ("bwd vs torch", bwd_torch), ("bwd strided", bwd_strided),
                      ("brute force", brute), ("f16 decode", f16_decode), ("bf16 decode", bf16_decode),
                      ("f16 encode", encode_f16), ("constant rows", constant_rows),

@@ -1,6 +1,7 @@
 /*
  * sm_softmax.h -- C ABI of the MI355X (gfx950) fused row-softmax library (forward,
- * backward) and the fused residual RMSNorm on the same row layout.
+ * backward), the fused residual RMSNorm on the same row layout, and the fused
+ * attention forward that carries the online softmax into QK^T and PV.
  *
  * Operation (every entry point below computes exactly this):
  *
@@ -279,6 +280,44 @@ int sm_rmsnorm_plan_query(const void *x, const void *residual, const void *weigh
                           int64_t res_stride, int64_t y_stride, int64_t res_out_stride, float eps,
                           int dtype, const sm_softmax_opts *opts, int num_cus,
                           sm_plan_info *info);
+
+/*
+ * Fused attention forward with the online softmax (the step after the row softmax
+ * that "Fused Softmax on GPU" names in its closing section: fusing the online
+ * softmax with the matmul before it, as FlashAttention does). For each of BH heads
+ * and query row i, without writing the scores:
+ *
+ *     S_ij = scale * q_i . k_j     (masked to -inf for j > i + Sk - Sq when causal)
+ *     o_i  = sum_j softmax(S_i)_j v_j,   lse_i = log sum_j exp(S_ij)
+ *
+ *   q [BH][Sq][d], k and v [BH][Sk][d], o [BH][Sq][d]: device pointers, FP16 or BF16,
+ *     element (h, i, c) at base + h * head_stride + i * row_stride + c (elements);
+ *     bases 16-byte aligned, strides multiples of 8 elements, row strides >= d; the
+ *     heads of o must not share elements; o must not overlap q, k, v or lse
+ *   lse  : optional (NULL) FP32 [BH][Sq] contiguous; -inf for a query that sees no key
+ *   d    : 64 or 128
+ *   scale: finite (usually 1 / sqrt(d)); causal: 0 or 1 (the mask is aligned to the
+ *          bottom right, so the last query sees every key)
+ * Scores and statistics are FP32; the probabilities are rounded to the input dtype
+ * before the product with V (the FlashAttention contract); o is rounded once. A
+ * query that sees no key gives zeros (the all -inf row reading of the softmax).
+ * Workgroups of 4 waves own 128 query rows of one head and walk the keys in blocks
+ * of 64 through LDS; products run on v_mfma_f32_16x16x32.
+ * Returns SM_OK or a negative sm_status (SM_ERR_DTYPE for FP32).
+ */
+int sm_attention_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t BH,
+                     int64_t Sq, int64_t Sk, int64_t d, int64_t q_row_stride,
+                     int64_t q_head_stride, int64_t k_row_stride, int64_t k_head_stride,
+                     int64_t v_row_stride, int64_t v_head_stride, int64_t o_row_stride,
+                     int64_t o_head_stride, float scale, int causal, int dtype, hipStream_t stream);
+
+/* As sm_attention_fwd; opts supplies only the timing events (other fields ignored). */
+int sm_attention_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t BH, int64_t Sq, int64_t Sk, int64_t d, int64_t q_row_stride,
+                        int64_t q_head_stride, int64_t k_row_stride, int64_t k_head_stride,
+                        int64_t v_row_stride, int64_t v_head_stride, int64_t o_row_stride,
+                        int64_t o_head_stride, float scale, int causal, int dtype,
+                        const sm_softmax_opts *opts, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *sm_softmax_strerror(int status);

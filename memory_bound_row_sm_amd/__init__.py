@@ -21,7 +21,8 @@ __all__ = [
     "softmax", "plan_for", "EXPORTED_SYMBOLS", "sm_softmax_bwd", "sm_softmax_bwd_ex",
     "sm_softmax_bwd_plan_query", "softmax_backward", "plan_for_backward",
     "sm_softmax_sync_failures", "sync_failures", "sm_rmsnorm_fwd", "sm_rmsnorm_fwd_ex",
-    "sm_rmsnorm_plan_query", "rmsnorm", "plan_for_rmsnorm",
+    "sm_rmsnorm_plan_query", "rmsnorm", "plan_for_rmsnorm", "sm_attention_fwd",
+    "sm_attention_fwd_ex", "attention",
 ]
 
 SM_F32, SM_F16, SM_BF16 = 0, 1, 2
@@ -36,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "sm_softmax_bwd_ex", "sm_softmax_bwd_plan_query", "sm_softmax_strerror",
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_softmax_sync_failures",
     "sm_rmsnorm_fwd", "sm_rmsnorm_fwd_ex", "sm_rmsnorm_plan_query",
-    "sm_bench_copy", "sm_bench_flush",
+    "sm_attention_fwd", "sm_attention_fwd_ex", "sm_bench_copy", "sm_bench_flush",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -113,6 +114,9 @@ def lib() -> ctypes.CDLL:
         L.sm_rmsnorm_plan_query.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, cf,
                                             ci, ctypes.POINTER(SmOpts), ci,
                                             ctypes.POINTER(SmPlanInfo)]
+        attn = [vp, vp, vp, vp, vp] + [i64] * 12 + [cf, ci, ci]
+        L.sm_attention_fwd.argtypes = attn + [vp]
+        L.sm_attention_fwd_ex.argtypes = attn + [ctypes.POINTER(SmOpts), vp]
         L.sm_softmax_strerror.argtypes = [ci]
         L.sm_softmax_strerror.restype = ctypes.c_char_p
         L.sm_softmax_version.argtypes = []
@@ -124,7 +128,7 @@ def lib() -> ctypes.CDLL:
                   L.sm_softmax_bwd, L.sm_softmax_bwd_ex, L.sm_softmax_bwd_plan_query,
                   L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_softmax_sync_failures,
                   L.sm_rmsnorm_fwd, L.sm_rmsnorm_fwd_ex, L.sm_rmsnorm_plan_query,
-                  L.sm_bench_copy, L.sm_bench_flush):
+                  L.sm_attention_fwd, L.sm_attention_fwd_ex, L.sm_bench_copy, L.sm_bench_flush):
             f.restype = ci
         _lib = L
     return _lib
@@ -224,6 +228,22 @@ def sm_rmsnorm_plan_query(x_ptr: int, r_ptr: int, w_ptr: int, y_ptr: int, s_ptr:
                                      ctypes.byref(o) if o is not None else None, num_cus,
                                      ctypes.byref(info))
     return rc, info
+
+
+def sm_attention_fwd(q: int, k: int, v: int, o: int, lse: int, BH: int, Sq: int, Sk: int, d: int,
+                     strides, scale: float, causal: int, dtype: int, stream: int = 0) -> int:
+    """``strides``: (q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head) in elements."""
+    return lib().sm_attention_fwd(q, k or None, v or None, o, lse or None, BH, Sq, Sk, d, *strides,
+                                  scale, causal, dtype, stream)
+
+
+def sm_attention_fwd_ex(q: int, k: int, v: int, o: int, lse: int, BH: int, Sq: int, Sk: int, d: int,
+                        strides, scale: float, causal: int, dtype: int, opts=None,
+                        stream: int = 0) -> int:
+    oo = _opts(opts)
+    return lib().sm_attention_fwd_ex(q, k or None, v or None, o, lse or None, BH, Sq, Sk, d,
+                                     *strides, scale, causal, dtype,
+                                     ctypes.byref(oo) if oo is not None else None, stream)
 
 
 def sm_softmax_strerror(status: int) -> str:
@@ -418,3 +438,54 @@ def plan_for_rmsnorm(x, weight, residual=None, eps: float = 1e-6, out=None, resi
     if rc != 0:
         raise SoftmaxError(rc, "sm_rmsnorm_plan_query")
     return info.as_dict()
+
+
+def _heads_view(t):
+    """(BH, S, d, row_stride, head_stride) of a [..., S, d] tensor whose leading
+    dimensions collapse to one head stride."""
+    if t.dim() < 2 or (t.size(-1) > 1 and t.stride(-1) != 1):
+        raise ValueError("expected [..., S, d] with a contiguous last dimension")
+    S, d = t.size(-2), t.size(-1)
+    lead = t.shape[:-2]
+    BH = 1
+    for n in lead:
+        BH *= n
+    hs = t.stride(-3) if t.dim() > 2 else S * t.stride(-2)
+    exp = hs
+    for i in range(t.dim() - 3, -1, -1):
+        if t.size(i) != 1 and t.stride(i) != exp:
+            raise ValueError("leading dimensions do not collapse to one head stride")
+        exp *= t.size(i)
+    return BH, S, d, t.stride(-2), hs
+
+
+def attention(q, k, v, scale=None, causal: bool = False, out=None, lse=None, opts=None,
+              stream=None):
+    """Fused attention forward of device tensors [..., S, d] (FP16/BF16, d = 64 or 128):
+    softmax(scale * q k^T [causal, aligned bottom right]) v. Returns ``out``; fills
+    ``lse`` (FP32 [..., Sq]) when given."""
+    import math
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("attention expects device tensors")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    BH, Sq, d, qr, qh = _heads_view(q)
+    BHk, Sk, dk, kr, kh = _heads_view(k)
+    BHv, Sv, dv, vr, vh = _heads_view(v)
+    BHo, So, do, orr, oh = _heads_view(out)
+    if (BHk, dk) != (BH, d) or (BHv, Sv, dv) != (BH, Sk, d) or (BHo, So, do) != (BH, Sq, d):
+        raise ValueError("q, k, v and out shapes do not match")
+    if lse is not None and (lse.dtype != torch.float32 or lse.numel() != BH * Sq or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of BH * Sq elements")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = sm_attention_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else 0, BH, Sq, Sk, d,
+                                 (qr, qh, kr, kh, vr, vh, orr, oh), float(scale), int(bool(causal)),
+                                 _torch_dtype_code(q), opts, s)
+    if rc != 0:
+        raise SoftmaxError(rc, "sm_attention_fwd_ex")
+    return out

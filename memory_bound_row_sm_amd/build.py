@@ -20,7 +20,7 @@ OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsm_softmax.so")
 
 SOURCES = ["sm_softmax.hip", "sm_rows_f32.hip", "sm_rows_f16.hip", "sm_rows_bf16.hip", "sm_bwd.hip",
-           "sm_split.hip", "sm_rmsnorm.hip"]
+           "sm_split.hip", "sm_rmsnorm.hip", "sm_attention.hip"]
 ARCH = "gfx950"
 
 

@@ -62,6 +62,11 @@ using RmsSplitKernelFn = void (*)(const unsigned char*, const unsigned char*, co
                                   float, int, int);
 RmsRowKernelFn rms_row_kernel(int dtype, int G, int V, int NT);
 RmsSplitKernelFn rms_split_kernel(int dtype, int V, int NT);
+
+// Fused attention forward (sm_attention.hip): FP16/BF16, head dim 64 or 128.
+struct AttnArgs;
+using AttnKernelFn = void (*)(const AttnArgs);
+AttnKernelFn attention_kernel(int dtype, int d, int causal);
 BwdDotKernelFn bwd_dot_kernel(int dtype);
 BwdApplyKernelFn bwd_apply_kernel(int dtype);
 

@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 
+#include "sm_attention.hpp"
 #include "sm_bench.h"
 #include "sm_bwd.hpp"
 #include "sm_kernels.hpp"
@@ -1059,12 +1060,127 @@ int run_rms(const RmsProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
     return rc;
 }
 
+// ------------------------------------------------------------ fused attention
+struct AttnProblem {
+    uintptr_t q, k, v, o, lse;  // lse may be 0
+    int64_t BH, Sq, Sk, d;
+    int64_t q_rs, q_hs, k_rs, k_hs, v_rs, v_hs, o_rs, o_hs;  // elements
+    float scale;
+    int causal, dtype;
+};
+
+// Byte span of a [BH][S][d] tensor with the given strides (elements), or -1.
+int64_t span3(int64_t BH, int64_t S, int64_t d, int64_t rs, int64_t hs, int es) {
+    if (BH <= 0 || S <= 0) return 0;
+    const int64_t last = (BH - 1) * hs + (S - 1) * rs + d;
+    if (last <= 0 || last > INT64_MAX / es) return -1;
+    return last * es;
+}
+
+int validate_attn(const AttnProblem& p) {
+    if (p.dtype != SM_F16 && p.dtype != SM_BF16) return SM_ERR_DTYPE;
+    if (p.BH < 0 || p.Sq < 0 || p.Sk < 0) return SM_ERR_INVALID;
+    if (p.d != 64 && p.d != 128) return SM_ERR_INVALID;
+    if (!(p.scale == p.scale) || __builtin_isinf(p.scale)) return SM_ERR_INVALID;
+    if (p.BH == 0 || p.Sq == 0) return SM_OK;
+    if (p.Sq > INT32_MAX || p.Sk > INT32_MAX) return SM_ERR_INVALID;
+    const int es = 2;
+    if (!p.q || !p.o || (p.Sk > 0 && (!p.k || !p.v))) return SM_ERR_INVALID;
+    // 16-byte rows: base, row and head strides multiples of 8 elements
+    auto aligned = [&](uintptr_t ptr, int64_t rs, int64_t hs) {
+        return ptr % 16 == 0 && rs % 8 == 0 && hs % 8 == 0 && rs >= p.d && hs >= 0;
+    };
+    if (!aligned(p.q, p.q_rs, p.q_hs) || !aligned(p.o, p.o_rs, p.o_hs)) return SM_ERR_INVALID;
+    if (p.Sk > 0 && (!aligned(p.k, p.k_rs, p.k_hs) || !aligned(p.v, p.v_rs, p.v_hs)))
+        return SM_ERR_INVALID;
+    // output rows of different heads must not share elements
+    if (p.BH > 1 && p.o_hs < (p.Sq - 1) * p.o_rs + p.d) return SM_ERR_INVALID;
+    if (p.lse && p.lse % 4) return SM_ERR_INVALID;
+    const int64_t so = span3(p.BH, p.Sq, p.d, p.o_rs, p.o_hs, es);
+    const int64_t sq = span3(p.BH, p.Sq, p.d, p.q_rs, p.q_hs, es);
+    const int64_t sk = span3(p.BH, p.Sk, p.d, p.k_rs, p.k_hs, es);
+    const int64_t sv = span3(p.BH, p.Sk, p.d, p.v_rs, p.v_hs, es);
+    if (so < 0 || sq < 0 || sk < 0 || sv < 0) return SM_ERR_INVALID;
+    if (p.BH > INT64_MAX / p.Sq) return SM_ERR_INVALID;
+    const int64_t sl = p.lse ? p.BH * p.Sq * 4 : 0;
+    // the output is written while the inputs are still being read: no overlap at all
+    if (spans_meet(p.o, so, p.q, sq) || (sk && spans_meet(p.o, so, p.k, sk)) ||
+        (sv && spans_meet(p.o, so, p.v, sv)))
+        return SM_ERR_OVERLAP;
+    if (p.lse && (spans_meet(p.lse, sl, p.o, so) || spans_meet(p.lse, sl, p.q, sq) ||
+                  (sk && spans_meet(p.lse, sl, p.k, sk)) || (sv && spans_meet(p.lse, sl, p.v, sv))))
+        return SM_ERR_OVERLAP;
+    const int64_t qblocks = (p.Sq + kAttnBM - 1) / kAttnBM;
+    if (p.BH > INT32_MAX / qblocks) return SM_ERR_INVALID;
+    return SM_OK;
+}
+
+int run_attn(const AttnProblem& p, const sm_softmax_opts* opts, hipStream_t stream) {
+    int rc = validate_attn(p);
+    if (rc != SM_OK || p.BH == 0 || p.Sq == 0) return rc;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        t_last_hip_error = (int)e;
+        return SM_ERR_NO_DEVICE;
+    }
+    const sm_softmax_opts o = opts_or_default(opts);
+    AttnKernelFn fn = attention_kernel(p.dtype, (int)p.d, p.causal ? 1 : 0);
+    if (!fn) return SM_ERR_PLAN;
+    AttnArgs a;
+    a.q = reinterpret_cast<const unsigned char*>(p.q);
+    a.k = reinterpret_cast<const unsigned char*>(p.k ? p.k : p.q);
+    a.v = reinterpret_cast<const unsigned char*>(p.v ? p.v : p.q);
+    a.o = reinterpret_cast<unsigned char*>(p.o);
+    a.lse = reinterpret_cast<float*>(p.lse);
+    a.q_rs = p.q_rs * 2;
+    a.q_hs = p.q_hs * 2;
+    a.k_rs = p.k_rs * 2;
+    a.k_hs = p.k_hs * 2;
+    a.v_rs = p.v_rs * 2;
+    a.v_hs = p.v_hs * 2;
+    a.o_rs = p.o_rs * 2;
+    a.o_hs = p.o_hs * 2;
+    a.Sq = (int)p.Sq;
+    a.Sk = (int)p.Sk;
+    a.qblocks = (int)((p.Sq + kAttnBM - 1) / kAttnBM);
+    a.scale_log2 = p.scale * 1.44269504088896340736f;
+    const int64_t grid = p.BH * a.qblocks;
+    e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(kAttnThreads), stream,
+                 o.start_event, o.stop_event, a);
+    return e == hipSuccess ? SM_OK : hip_fail(e);
+}
+
 }  // namespace
 }  // namespace smx
 
 using namespace smx;
 
 extern "C" {
+
+int sm_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                     int64_t Sq, int64_t Sk, int64_t d, int64_t q_row_stride,
+                     int64_t q_head_stride, int64_t k_row_stride, int64_t k_head_stride,
+                     int64_t v_row_stride, int64_t v_head_stride, int64_t o_row_stride,
+                     int64_t o_head_stride, float scale, int causal, int dtype, hipStream_t stream) {
+    return sm_attention_fwd_ex(q, k, v, o, lse, BH, Sq, Sk, d, q_row_stride, q_head_stride,
+                               k_row_stride, k_head_stride, v_row_stride, v_head_stride,
+                               o_row_stride, o_head_stride, scale, causal, dtype, nullptr, stream);
+}
+
+int sm_attention_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t BH, int64_t Sq, int64_t Sk, int64_t d, int64_t q_row_stride,
+                        int64_t q_head_stride, int64_t k_row_stride, int64_t k_head_stride,
+                        int64_t v_row_stride, int64_t v_head_stride, int64_t o_row_stride,
+                        int64_t o_head_stride, float scale, int causal, int dtype,
+                        const sm_softmax_opts* opts, hipStream_t stream) {
+    const AttnProblem p{reinterpret_cast<uintptr_t>(q),   reinterpret_cast<uintptr_t>(k),
+                        reinterpret_cast<uintptr_t>(v),   reinterpret_cast<uintptr_t>(o),
+                        reinterpret_cast<uintptr_t>(lse), BH, Sq, Sk, d, q_row_stride,
+                        q_head_stride, k_row_stride, k_head_stride, v_row_stride, v_head_stride,
+                        o_row_stride, o_head_stride, scale, causal, dtype};
+    return run_attn(p, opts, stream);
+}
 
 int sm_rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* y,
                    void* residual_out, int64_t M, int64_t N, int64_t x_stride, int64_t res_stride,

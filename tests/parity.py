@@ -166,3 +166,42 @@ def compare_rms(g: torch.Tensor, x: torch.Tensor, r, w: torch.Tensor, eps: float
                              f"({i},{j}): gpu={gd[i, j]!r} ref={ref[i, j]!r}")
     return {"max_abs": float(err.max()) if err.size else 0.0,
             "worst_frac_of_tol": float(np.max(err / bound)) if err.size else 0.0, "n": int(err.size)}
+
+
+# ------------------------------------------------------------------ fused attention
+# The kernel forms the scores in FP32 (exact products of 16-bit inputs), the row
+# statistics in FP32, and rounds the probabilities to the input dtype before the
+# product with V (the FlashAttention contract). Rounding P moves o_i by at most
+# 2^-(p+1) * sum_j P_ij |v_j| (p fraction bits), so with a factor 4 of margin:
+#   |g - r| <= u |r| + c * sum_j P_ij |v_jd| + a,
+# u one unit in the last place relative (2^-7 BF16, 2^-10 FP16), c = 2^-7 (BF16) /
+# 2^-10 (FP16), a the subnormal spacing; sum_j P |v| is the oracle's attention of |v|.
+# A wrong mask, scale or index moves o by the order of sum_j P |v| and fails.
+TOL_ATTN = {"f16": (2.0 ** -10, 2.0 ** -10, 2.0 ** -24), "bf16": (2.0 ** -7, 2.0 ** -7, 2.0 ** -133)}
+
+
+def compare_attn(g: torch.Tensor, q, k, v, scale: float, causal: bool, rows=None, lse_gpu=None,
+                 what: str = "") -> dict:
+    dt = workloads.dtype_name(q)
+    qs, ks, vs = (workloads.storage_numpy(t.detach().cpu().contiguous()) for t in (q, k, v))
+    o, orr, lse = oracle.reference_attention(qs, ks, vs, dt, scale, causal, rows=rows)
+    vabs = vs & np.uint16(0x7FFF)
+    mag, _ = oracle.attention_f64(qs, ks, vabs, dt, scale, causal, rows=rows)
+    gd = to_f64(g).reshape(o.shape)
+    ref = oracle.decode(orr, dt)
+    u, c, a = TOL_ATTN[dt]
+    assert not np.isnan(gd).any(), f"{what}: NaN in the output"
+    err = np.abs(gd - ref)
+    bound = u * np.abs(ref) + c * mag + a
+    bad = err > bound
+    if bad.any():
+        i, j = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst at "
+                             f"({i},{j}): gpu={gd[i, j]!r} ref={ref[i, j]!r} scale={mag[i, j]!r}")
+    if lse_gpu is not None:
+        lg = lse_gpu.detach().cpu().double().numpy().reshape(-1)
+        fin = np.isfinite(lse)
+        assert np.array_equal(np.isneginf(lg), ~fin), f"{what}: lse -inf pattern differs"
+        assert np.allclose(lg[fin], lse[fin], rtol=2e-6, atol=2e-6), f"{what}: lse differs"
+    return {"max_abs": float(err.max()) if err.size else 0.0,
+            "worst_frac_of_tol": float(np.max(err / bound)) if err.size else 0.0, "n": int(err.size)}

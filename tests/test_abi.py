@@ -350,3 +350,36 @@ def test_rmsnorm_plan_rule():
     assert rc == PLAN                   # rows hold at most 4 vectors per lane
     rc, p = rms_q(8, 1000, F16, r=R + 2)  # residual at another 16-byte phase
     assert p["dy_same_phase"] == 0
+
+
+# ------------------------------------------------------------------ fused attention
+def attn(BH=2, Sq=64, Sk=64, d=128, q=BASE, k=BASE * 2, v=BASE * 3, o=BASE * 4, lse=0,
+         strides=None, scale=0.125, causal=1, dt=BF16):
+    st = strides or (d, Sq * d, d, Sk * d, d, Sk * d, d, Sq * d)
+    return sm.sm_attention_fwd(q, k, v, o, lse, BH, Sq, Sk, d, st, scale, causal, dt, 0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=F32), DTYPE), (dict(dt=9), DTYPE),
+    (dict(d=96), INVALID), (dict(d=0), INVALID),
+    (dict(q=BASE + 2), INVALID),                       # not 16-byte aligned
+    (dict(strides=(130, 64 * 130, 128, 8192, 128, 8192, 128, 8192)), INVALID),  # row stride % 8
+    (dict(strides=(120, 64 * 120, 128, 8192, 128, 8192, 128, 8192)), INVALID),  # row stride < d
+    (dict(strides=(128, 8192, 128, 8192, 128, 8192, 128, 64)), INVALID),        # o heads overlap
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(o=BASE + 4096), OVERLAP),                    # o inside q
+    (dict(o=BASE * 3 + 1024), OVERLAP),                # o inside v
+    (dict(lse=BASE * 4 + 64), OVERLAP),                # lse inside o
+    (dict(lse=BASE * 5 + 2), INVALID),                 # lse not 4-byte aligned
+    (dict(BH=0), OK), (dict(Sq=0), OK),
+])
+def test_attention_validation(kw, want):
+    rc = attn(**kw)
+    assert rc == want, (kw, rc)
+
+
+def test_attention_valid_call_without_device():
+    rc = attn(lse=BASE * 5)
+    assert rc in (OK, NO_DEVICE)
+    rc = attn(Sk=0, k=0, v=0)  # no keys: every query gets zeros
+    assert rc in (OK, NO_DEVICE)

@@ -1,0 +1,113 @@
+"""GPU parity of the fused attention forward (sm_attention_fwd) against the FP64 oracle:
+head dims 64 and 128, causal and not, Sq = Sk and Sq != Sk (queries that see no key),
+ragged lengths, strided head layouts, log-sum-exp, repeatability, torch's FP32 SDPA,
+and the attention-shaped workload (8 x 32 heads, 2048 x 2048, d = 128) at full size
+with sampled rows."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_sm_amd as sm
+import workloads
+from parity import compare_attn, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    sm.lib()
+
+
+def qkv(BH, Sq, Sk, d, dt, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(BH, Sq, d, generator=g) * scale).to(TDT[dt])
+    k = (torch.randn(BH, Sk, d, generator=g) * scale).to(TDT[dt])
+    v = torch.randn(BH, Sk, d, generator=g).to(TDT[dt])
+    return q, k, v
+
+
+def run(q, k, v, causal, scale=None, lse=False):
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.full_like(qd, float("nan"))
+    ls = torch.full((q.shape[0] * q.shape[1],), float("nan"), device=DEV) if lse else None
+    sm.attention(qd, kd, vd, scale=scale, causal=causal, out=o, lse=ls)
+    torch.cuda.synchronize()
+    return o, ls
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("BH,Sq,Sk", [(2, 128, 128), (3, 200, 333), (1, 1, 1), (2, 257, 64),
+                                      (1, 64, 1000), (2, 130, 70)])
+def test_shapes(dt, d, causal, BH, Sq, Sk):
+    q, k, v = qkv(BH, Sq, Sk, d, dt, seed=Sq * 7 + Sk)
+    scale = 1.0 / math.sqrt(d)
+    o, ls = run(q, k, v, causal, scale, lse=True)
+    st = compare_attn(o, q, k, v, scale, causal, lse_gpu=ls, what=f"{dt} d={d} causal={causal} {BH}x{Sq}x{Sk}")
+    assert st["worst_frac_of_tol"] <= 1.0
+    if causal and Sq > Sk:  # queries i < Sq - Sk see no key
+        n = Sq - Sk
+        assert (o[:, :n].float() == 0).all()
+        assert torch.isneginf(ls.view(BH, Sq)[:, :n]).all()
+
+
+def test_large_scores_and_scale():
+    """Scores of magnitude ~100 (sharp softmax) and a non-default scale."""
+    q, k, v = qkv(2, 300, 300, 128, "bf16", seed=5, scale=3.0)
+    for causal in (False, True):
+        o, ls = run(q, k, v, causal, scale=0.3, lse=True)
+        compare_attn(o, q, k, v, 0.3, causal, lse_gpu=ls, what=f"sharp causal={causal}")
+
+
+def test_strided_heads():
+    """q, k, v as [1, S, H, d] tensors viewed as [H, S, d] (row stride H * d, head stride d)."""
+    H, S, d = 4, 160, 64
+    g = torch.Generator().manual_seed(11)
+    base = [torch.randn(1, S, H, d, generator=g).to(torch.bfloat16) for _ in range(3)]
+    views = [b.to(DEV).transpose(1, 2)[0] for b in base]  # [H, S, d], strided
+    o = torch.full((H, S, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    sm.attention(*views, causal=True, out=o)
+    torch.cuda.synchronize()
+    cpu = [b.transpose(1, 2)[0].contiguous() for b in base]
+    compare_attn(o, *cpu, 1.0 / math.sqrt(d), True, what="strided heads")
+
+
+def test_repeatable_and_torch_fp32():
+    q, k, v = qkv(4, 512, 512, 128, "bf16", seed=3)
+    a, _ = run(q, k, v, True)
+    b, _ = run(q, k, v, True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    want = torch.nn.functional.scaled_dot_product_attention(q.float(), k.float(), v.float(), is_causal=True)
+    assert float((a.float().cpu() - want).abs().max()) < 2e-2
+
+
+def test_attention_workload_full_size_sampled():
+    """8 x 32 heads, 2048 queries and keys, d = 128, causal, BF16: q, k as in the
+    attention-logit workload (per-head seeded N(0,1)), v ~ N(0,1). Sampled rows against
+    the oracle: the first, second and last query of every head and one random query."""
+    B, H, S, d = 8, 32, 2048, 128
+    g = torch.Generator().manual_seed(2026)
+    q = torch.randn(B * H, S, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B * H, S, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B * H, S, d, generator=g).to(torch.bfloat16)
+    o, ls = run(q, k, v, True, lse=True)
+    rng = np.random.default_rng(7)
+    rows = set()
+    for h in range(B * H):
+        rows.update({h * S, h * S + 1, h * S + S - 1, h * S + int(rng.integers(0, S))})
+    rows = np.array(sorted(rows), dtype=np.int64)
+    sel = torch.from_numpy(rows)
+    st = compare_attn(o.view(-1, d).cpu()[sel], q, k, v, 1.0 / math.sqrt(d), True, rows=rows,
+                      lse_gpu=ls.cpu()[sel], what="attention workload sampled")
+    log(f"[attn] workload sampled {rows.size} rows: {st}")
+    # the first query of every head sees only key 0: o = v_0 rounded
+    assert torch.equal(o[:, 0].cpu().view(torch.int16), v[:, 0].view(torch.int16))

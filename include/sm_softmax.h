@@ -292,8 +292,8 @@ int sm_rmsnorm_plan_query(const void *x, const void *residual, const void *weigh
  *
  *   q [BH][Sq][d], k and v [BH][Sk][d], o [BH][Sq][d]: device pointers, FP16 or BF16,
  *     element (h, i, c) at base + h * head_stride + i * row_stride + c (elements);
- *     bases 16-byte aligned, strides multiples of 8 elements, row strides >= d; the
- *     heads of o must not share elements; o must not overlap q, k, v or lse
+ *     bases 16-byte aligned, strides multiples of 8 elements, d <= row strides <=
+ *     2^24; the heads of o must not share elements; o must not overlap q, k, v or lse
  *   lse  : optional (NULL) FP32 [BH][Sq] contiguous; -inf for a query that sees no key
  *   d    : 64 or 128
  *   scale: finite (usually 1 / sqrt(d)); causal: 0 or 1 (the mask is aligned to the
@@ -301,8 +301,10 @@ int sm_rmsnorm_plan_query(const void *x, const void *residual, const void *weigh
  * Scores and statistics are FP32; the probabilities are rounded to the input dtype
  * before the product with V (the FlashAttention contract); o is rounded once. A
  * query that sees no key gives zeros (the all -inf row reading of the softmax).
- * Workgroups of 4 waves own 128 query rows of one head and walk the keys in blocks
- * of 64 through LDS; products run on v_mfma_f32_16x16x32.
+ * Workgroups of 4 waves own 128 query rows of one head (causal: two such q-blocks,
+ * i and n-1-i, so every workgroup does about the same work) and walk the keys in
+ * blocks of 64 through LDS; products run on v_mfma_f32_16x16x32. The result does not
+ * depend on the grid order: repeated calls give identical bits.
  * Returns SM_OK or a negative sm_status (SM_ERR_DTYPE for FP32).
  */
 int sm_attention_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t BH,

@@ -21,7 +21,8 @@
 //                 operands, so no shuffle of P is needed, and the output tile keeps
 //                 the query in the lane column, so the rescale is per lane.
 // The next key block's K and V are loaded into registers while the current block
-// is computed, and written to LDS after it (one buffer, two barriers per block).
+// is computed, and written to LDS after it (one buffer, two barriers per block); V
+// is transposed on the way (8-byte stores of 4 keys per d column).
 //
 // Causal masking is aligned to the bottom right: query i sees keys j <= i + Sk - Sq.
 // A query that sees no key (Sq > Sk) gets zeros and lse = -inf (the all -inf row
@@ -39,16 +40,12 @@ struct AttnElem;
 template <>
 struct AttnElem<1> {  // FP16
     typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ uint16_t bits(float f) {
-        return __builtin_bit_cast(uint16_t, (_Float16)f);
-    }
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
 };
 template <>
 struct AttnElem<2> {  // BF16
     typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ uint16_t bits(float f) {
-        return __builtin_bit_cast(uint16_t, (__bf16)f);
-    }
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
 };
 
 typedef float attn_f4 __attribute__((ext_vector_type(4)));
@@ -67,9 +64,14 @@ __device__ __forceinline__ attn_f4 mfma16(const attn_u4 a, const attn_u4 b, attn
     }
 }
 
-constexpr int kAttnBM = 128;  // query rows per workgroup
+constexpr int kAttnBM = 128;  // query rows per q-block (a workgroup's pass)
 constexpr int kAttnBN = 64;   // keys per block
 constexpr int kAttnThreads = 256;
+constexpr int kAttnXcds = 8;  // MI355X: 8 accelerator dies, each with its own L2
+// The running shift of a query row is raised only when a block's maximum exceeds it
+// by more than this (log2 units): exponentials stay <= 2^8, and most blocks skip the
+// rescale of the output accumulators.
+constexpr float kAttnLazy = 8.0f;
 
 struct AttnArgs {
     const unsigned char* q;
@@ -79,11 +81,30 @@ struct AttnArgs {
     float* lse;
     int64_t q_rs, q_hs, k_rs, k_hs, v_rs, v_hs, o_rs, o_hs;  // bytes
     int Sq, Sk, qblocks;
+    int items;         // work items per head: qblocks, or ceil(qblocks / 2) when causal
     float scale_log2;  // scale * log2(e)
 };
 
+// Item of workgroup b out of G: workgroups are handed to the XCDs in turn (b % 8),
+// so item ids are laid out to give each XCD one contiguous range of items -- whole
+// heads -- whose K and V then stay in that XCD's L2. A bijection for any G.
+__device__ __forceinline__ int64_t attn_item(int64_t b, int64_t G) {
+    const int64_t x = b % kAttnXcds, j = b / kAttnXcds;
+    const int64_t q = G / kAttnXcds, r = G % kAttnXcds;
+    return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+// Two FP32 values rounded to the dtype (nearest even) and packed, low half = first:
+// one v_cvt_pk_{bf16,f16}_f32.
+template <int DT>
+__device__ __forceinline__ uint32_t attn_pack2(float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef typename AttnElem<DT>::v2 e2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, e2));
+}
+
 template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kAttnThreads)
+__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 k_attention_fwd(const AttnArgs a) {
     constexpr int BN = kAttnBN;
     constexpr int KS = D + 8;       // K row stride in LDS (elements): 16-byte pad
@@ -92,196 +113,248 @@ k_attention_fwd(const AttnArgs a) {
     constexpr int LOADS = BN * KCH / kAttnThreads;  // 16-byte chunks per thread per tile
     constexpr int DSUB = D / 16;    // 16-wide d subtiles of the output
     constexpr int KK = D / 32;      // 32-wide d steps of the score product
-    __shared__ uint16_t ks[BN * KS];
-    __shared__ uint16_t vt[D * VS];
+    constexpr float kInf = __builtin_huge_valf();
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 15;       // lane column: a query (S^T, O^T) or a key/d row (A ops)
     const int grp = lane >> 4;       // lane group 0..3
-    const int64_t bh = blockIdx.x / a.qblocks;
-    const int q0 = (int)(blockIdx.x % a.qblocks) * kAttnBM + wave * 32;
     const int off = a.Sk - a.Sq;     // causal: query i sees keys j <= i + off
+
+    const int64_t item = attn_item(blockIdx.x, gridDim.x);
+    const int64_t bh = item / a.items;
+    const int it0 = (int)(item - bh * a.items);
+    // causal: q-blocks it0 and qblocks-1-it0 (heavy one first) share an item, so every
+    // item walks about the same number of key blocks
+    const int qb_hi = CAUSAL ? a.qblocks - 1 - it0 : it0;
+    const int npass = (CAUSAL && it0 < qb_hi) ? 2 : 1;
 
     const unsigned char* qh = a.q + bh * a.q_hs;
     const unsigned char* kh = a.k + bh * a.k_hs;
     const unsigned char* vh = a.v + bh * a.v_hs;
+    // a negative scale is folded into Q's sign (exact), so the score maximum is taken
+    // on the unscaled products and scaled once
+    const float c = __builtin_fabsf(a.scale_log2);
+    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-    // Q as the B operand of S^T = K Q^T: lane (col, grp) holds row q0 + u*16 + col,
-    // d = kk*32 + grp*8 .. +8 (rows past Sq read as zeros and are never stored)
-    attn_u4 qb[2][KK];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int qi = q0 + u * 16 + col;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            attn_u4 z = {0u, 0u, 0u, 0u};
-            if (qi < a.Sq) z = *reinterpret_cast<const attn_u4*>(qh + qi * a.q_rs + (kk * 32 + grp * 8) * 2);
-            qb[u][kk] = z;
-        }
-    }
-
-    attn_f4 oacc[DSUB][2];
-#pragma unroll
-    for (int s = 0; s < DSUB; ++s)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) oacc[s][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
-    float l[2] = {0.f, 0.f};  // this lane group's part of the running sum
-
-    // key range of this workgroup (causal: up to the last query's diagonal)
-    const int qlast = (int)(blockIdx.x % a.qblocks) * kAttnBM + kAttnBM - 1;
-    int kend = a.Sk;
-    if (CAUSAL) kend = min(a.Sk, max(0, qlast + off + 1));
-    const int nblk = (kend + BN - 1) / BN;
-
-    // register staging of one K/V tile: chunk c = tid + 256 * it -> row c / KCH, chunk c % KCH
-    attn_u4 kreg[LOADS], vreg[LOADS];
+    // Register staging of one K/V tile. K: chunk t = tid + 256 * it -> row t / KCH,
+    // chunk t % KCH (row-major copy into LDS). V: thread (kg = tid % VG, ch = tid / VG)
+    // loads keys KPT * kg .. + KPT - 1 of d-chunk ch and writes each of its 8 d columns
+    // as one store of KPT keys into V^T: the VG lanes of one chunk write one contiguous
+    // 128-byte stretch of a V^T row (no bank conflicts, no 2-byte stores).
+    constexpr int KPT = BN * KCH / kAttnThreads;  // keys per thread of the V tile (D / 32)
+    constexpr int VG = BN / KPT;                  // key groups per d-chunk
+    static_assert(KPT == 2 || KPT == 4, "V staging assumes d = 64 or 128");
+    attn_u4 kreg[LOADS], vreg[KPT];
+    const int vkg = tid % VG, vch = tid / VG;
+    // 32-bit lane offsets inside a tile (row strides are below 2^24 elements), added to
+    // the tile's wave-uniform base: one VGPR per address
+    constexpr int KR = kAttnThreads / KCH;  // K rows covered by one pass of the threads
+    const int krow = tid / KCH;
+    const uint32_t k_lane = (uint32_t)krow * (uint32_t)a.k_rs + (uint32_t)(tid % KCH) * 16u;
+    const uint32_t k_step = (uint32_t)KR * (uint32_t)a.k_rs;
+    const uint32_t v_lane = (uint32_t)(vkg * KPT) * (uint32_t)a.v_rs + (uint32_t)vch * 16u;
+    const uint32_t v_rs32 = (uint32_t)a.v_rs;
     auto fetch = [&](int kb) {
+        const unsigned char* kt = kh + (int64_t)kb * a.k_rs;
+        const unsigned char* vtile = vh + (int64_t)kb * a.v_rs;
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
-            const int c = tid + kAttnThreads * it;
-            const int r = kb + c / KCH, ch = c % KCH;
-            attn_u4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-            if (r < a.Sk) {
-                zk = *reinterpret_cast<const attn_u4*>(kh + r * a.k_rs + ch * 16);
-                zv = *reinterpret_cast<const attn_u4*>(vh + r * a.v_rs + ch * 16);
-            }
+            attn_u4 zk = {0u, 0u, 0u, 0u};
+            if (kb + krow + KR * it < a.Sk)
+                zk = *reinterpret_cast<const attn_u4*>(kt + (k_lane + (uint32_t)it * k_step));
             kreg[it] = zk;
-            vreg[it] = zv;
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            attn_u4 zv = {0u, 0u, 0u, 0u};
+            if (kb + vkg * KPT + e < a.Sk)
+                zv = *reinterpret_cast<const attn_u4*>(vtile + (v_lane + (uint32_t)e * v_rs32));
+            vreg[e] = zv;
         }
     };
     auto stage = [&]() {
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
-            const int c = tid + kAttnThreads * it;
-            const int r = c / KCH, ch = c % KCH;
+            const int t = tid + kAttnThreads * it;
+            const int r = t / KCH, ch = t % KCH;
             *reinterpret_cast<attn_u4*>(&ks[r * KS + ch * 8]) = kreg[it];
-            // V transposed: element e of the chunk is V[r][ch*8 + e] -> vt[ch*8 + e][r]
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w = vreg[it][e];
-                vt[(ch * 8 + 2 * e) * VS + r] = (uint16_t)(w & 0xFFFFu);
-                vt[(ch * 8 + 2 * e + 1) * VS + r] = (uint16_t)(w >> 16);
+        for (int w = 0; w < 4; ++w) {  // word w of a key's chunk holds d columns 2w, 2w+1
+            uint16_t* lo_row = &vt[(vch * 8 + 2 * w) * VS + vkg * KPT];
+            uint16_t* hi_row = lo_row + VS;
+            const uint32_t a0 = vreg[0][w], a1 = vreg[1][w];
+            const uint32_t lo01 = (a0 & 0xFFFFu) | (a1 << 16), hi01 = (a0 >> 16) | (a1 & 0xFFFF0000u);
+            if constexpr (KPT == 4) {
+                const uint32_t a2 = vreg[2][w], a3 = vreg[3][w];
+                const uint32_t lo23 = (a2 & 0xFFFFu) | (a3 << 16), hi23 = (a2 >> 16) | (a3 & 0xFFFF0000u);
+                *reinterpret_cast<attn_u2*>(lo_row) = attn_u2{lo01, lo23};
+                *reinterpret_cast<attn_u2*>(hi_row) = attn_u2{hi01, hi23};
+            } else {
+                *reinterpret_cast<uint32_t*>(lo_row) = lo01;
+                *reinterpret_cast<uint32_t*>(hi_row) = hi01;
             }
         }
     };
 
-    if (nblk > 0) fetch(0);
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int kb = blk * BN;
-        __syncthreads();  // every wave is done reading the previous tile
-        stage();
-        __syncthreads();
-        if (blk + 1 < nblk) fetch(kb + BN);  // next tile in flight during this one
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qblk = pass == 0 ? qb_hi : it0;
+        const int q0 = qblk * kAttnBM + wave * 32;  // this wave's first query row
 
-        // S^T tiles: t = key subtile (16 keys), u = query subtile
-        attn_f4 s[4][2];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) s[t][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const attn_u4 ka = *reinterpret_cast<const attn_u4*>(&ks[(t * 16 + col) * KS + kk * 32 + grp * 8]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
-            }
-        }
-
-        // online softmax on the lane's 16 keys of each query column
-        attn_u4 pb[2][2];  // P as the B operand: [u][32-key step]
+        // Q as the B operand of S^T = K Q^T: lane (col, grp) holds row q0 + u*16 + col,
+        // d = kk*32 + grp*8 .. +8 (rows past Sq read as zeros and are never stored)
+        attn_u4 qb[2][KK];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int qi = q0 + u * 16 + col;
-            float bmax = -__builtin_huge_valf();
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kj = kb + t * 16 + grp * 4 + i;
-                    float x = s[t][u][i] * a.scale_log2;
-                    const bool masked = kj >= a.Sk || (CAUSAL && kj > qi + off);
-                    x = masked ? -__builtin_huge_valf() : x;
-                    s[t][u][i] = x;
-                    bmax = __builtin_fmaxf(bmax, x);
+            for (int kk = 0; kk < KK; ++kk) {
+                attn_u4 z = {0u, 0u, 0u, 0u};
+                if (qi < a.Sq) {
+                    z = *reinterpret_cast<const attn_u4*>(qh + qi * a.q_rs + (kk * 32 + grp * 8) * 2);
+                    z ^= qflip;
                 }
+                qb[u][kk] = z;
             }
-            bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 16));
-            bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 32));
-            const float mn = __builtin_fmaxf(m[u], bmax);
-            // a query with no visible key so far keeps shift 0 and sum 0
-            const float ms = (mn == -__builtin_huge_valf()) ? 0.f : mn;
-            const float alpha = __builtin_amdgcn_exp2f(m[u] - ms);  // m = -inf -> 0
-            m[u] = mn;
-            float psum = 0.f;
-            float p[4][4];
+        }
+
+        attn_f4 oacc[DSUB][2];
+#pragma unroll
+        for (int s = 0; s < DSUB; ++s)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) oacc[s][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
+        float m[2] = {-kInf, -kInf};  // running shift per query (scaled, log2 units)
+        float ms[2] = {0.f, 0.f};     // m, or 0 while m = -inf
+        float l[2] = {0.f, 0.f};      // this lane group's part of the running sum
+
+        // key range of this q-block (causal: up to its last query's diagonal)
+        int kend = a.Sk;
+        if (CAUSAL) kend = min(a.Sk, max(0, qblk * kAttnBM + kAttnBM - 1 + off + 1));
+        const int nblk = (kend + BN - 1) / BN;
+
+        if (nblk > 0) fetch(0);
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int kb = blk * BN;
+            __syncthreads();  // every wave is done reading the previous tile
+            stage();
+            __syncthreads();
+            if (blk + 1 < nblk) fetch(kb + BN);  // next tile in flight during this one
+            // every key of the block lies past every query's diagonal for this wave
+            if (CAUSAL && kb > q0 + 31 + off) continue;
+
+            // S^T tiles: t = key subtile (16 keys), u = query subtile
+            attn_f4 s[4][2];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[t][i] = __builtin_amdgcn_exp2f(s[t][u][i] - ms);
-                    psum += p[t][i];
+                for (int u = 0; u < 2; ++u) s[t][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const attn_u4 ka = *reinterpret_cast<const attn_u4*>(&ks[(t * 16 + col) * KS + kk * 32 + grp * 8]);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
                 }
-            l[u] = l[u] * alpha + psum;
+            }
+
+            // Blocks cut by the end of the keys or by a diagonal of this wave's queries
+            // are scaled and masked element by element (cc = 1 then); all others keep the
+            // raw products and fold the scale into the exponent's FMA.
+            const bool need_mask = (kb + BN > a.Sk) || (CAUSAL && kb + BN - 1 > q0 + off);
+            const float cc = need_mask ? 1.f : c;
+            attn_u4 pb[2][2];  // P as the B operand: [u][32-key step]
 #pragma unroll
-            for (int d = 0; d < DSUB; ++d) oacc[d][u] *= alpha;
+            for (int u = 0; u < 2; ++u) {
+                if (need_mask) {
+                    // key kb + grp*4 + (t*16 + i) is visible iff t*16 + i <= lim
+                    int lim = a.Sk - 1;
+                    if (CAUSAL) lim = min(lim, q0 + u * 16 + col + off);
+                    lim -= kb + grp * 4;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                // 32-key step c: slots 0..3 <- subtile 2c, slots 4..7 <- subtile 2c+1
-                uint32_t w[4];
+                    for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int t = 2 * c + h;
-                    w[2 * h] = (uint32_t)AttnElem<DT>::bits(p[t][0]) |
-                               ((uint32_t)AttnElem<DT>::bits(p[t][1]) << 16);
-                    w[2 * h + 1] = (uint32_t)AttnElem<DT>::bits(p[t][2]) |
-                                   ((uint32_t)AttnElem<DT>::bits(p[t][3]) << 16);
+                        for (int i = 0; i < 4; ++i)
+                            s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i] * c;
                 }
-                pb[u][c] = attn_u4{w[0], w[1], w[2], w[3]};
+                float bmax = -kInf;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bmax = __builtin_fmaxf(bmax, s[t][u][i]);
+                bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 16));
+                bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 32));
+                bmax *= cc;  // scaled (c >= 0 keeps the order)
+                const bool grow = bmax > m[u] + kAttnLazy;
+                if (__any(grow)) {
+                    const float mn = grow ? bmax : m[u];
+                    const float sn = (mn == -kInf) ? 0.f : mn;
+                    const float alpha = __builtin_amdgcn_exp2f(m[u] - sn);  // m = -inf -> 0
+                    m[u] = mn;
+                    ms[u] = sn;
+                    l[u] *= alpha;
+#pragma unroll
+                    for (int d = 0; d < DSUB; ++d) oacc[d][u] *= alpha;
+                }
+                float p[4][4];
+                float psum = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][u][i], cc, -ms[u]));
+                        psum += p[t][i];
+                    }
+                l[u] += psum;
+#pragma unroll
+                for (int cs = 0; cs < 2; ++cs) {
+                    // 32-key step cs: slots 0..3 <- subtile 2cs, slots 4..7 <- subtile 2cs+1
+                    const int t0 = 2 * cs, t1 = 2 * cs + 1;
+                    pb[u][cs] = attn_u4{attn_pack2<DT>(p[t0][0], p[t0][1]), attn_pack2<DT>(p[t0][2], p[t0][3]),
+                                        attn_pack2<DT>(p[t1][0], p[t1][1]), attn_pack2<DT>(p[t1][2], p[t1][3])};
+                }
+            }
+
+            // O^T += V^T P^T: A = V^T rows d, keys in the same slot order as P
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+#pragma unroll
+                for (int d = 0; d < DSUB; ++d) {
+                    const uint16_t* vrow = &vt[(d * 16 + col) * VS];
+                    const attn_u2 lo = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs) * 16 + grp * 4);
+                    const attn_u2 hi = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs + 1) * 16 + grp * 4);
+                    const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);
+                }
             }
         }
 
-        // O^T += V^T P^T: A = V^T rows d, keys in the same slot order as P
+        // finish: the full row sum over the 4 lane groups, normalise, store
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int u = 0; u < 2; ++u) {
+            float lt = l[u];
+            lt += __shfl_xor(lt, 16);
+            lt += __shfl_xor(lt, 32);
+            const int qi = q0 + u * 16 + col;
+            if (qi >= a.Sq) continue;
+            const float r = (lt > 0.f) ? 1.0f / lt : 0.f;
+            unsigned char* orow = a.o + bh * a.o_hs + qi * a.o_rs;
 #pragma unroll
             for (int d = 0; d < DSUB; ++d) {
-                const uint16_t* vrow = &vt[(d * 16 + col) * VS];
-                const attn_u2 lo = *reinterpret_cast<const attn_u2*>(vrow + (2 * c) * 16 + grp * 4);
-                const attn_u2 hi = *reinterpret_cast<const attn_u2*>(vrow + (2 * c + 1) * 16 + grp * 4);
-                const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][c], oacc[d][u]);
+                *reinterpret_cast<attn_u2*>(orow + (d * 16 + grp * 4) * 2) =
+                    attn_u2{attn_pack2<DT>(oacc[d][u][0] * r, oacc[d][u][1] * r),
+                            attn_pack2<DT>(oacc[d][u][2] * r, oacc[d][u][3] * r)};
             }
-        }
-    }
-
-    // finish: the full row sum over the 4 lane groups, normalise, store
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        float lt = l[u];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-        const int qi = q0 + u * 16 + col;
-        if (qi >= a.Sq) continue;
-        const float r = (lt > 0.f) ? 1.0f / lt : 0.f;
-        unsigned char* orow = a.o + bh * a.o_hs + qi * a.o_rs;
-#pragma unroll
-        for (int d = 0; d < DSUB; ++d) {
-            const uint32_t w0 = (uint32_t)AttnElem<DT>::bits(oacc[d][u][0] * r) |
-                                ((uint32_t)AttnElem<DT>::bits(oacc[d][u][1] * r) << 16);
-            const uint32_t w1 = (uint32_t)AttnElem<DT>::bits(oacc[d][u][2] * r) |
-                                ((uint32_t)AttnElem<DT>::bits(oacc[d][u][3] * r) << 16);
-            *reinterpret_cast<attn_u2*>(orow + (d * 16 + grp * 4) * 2) = attn_u2{w0, w1};
-        }
-        if (a.lse && grp == 0) {
-            // natural log-sum-exp of the scaled scores: (m + log2 l) * ln 2
-            a.lse[bh * a.Sq + qi] = (lt > 0.f) ? (m[u] + __builtin_log2f(lt)) * 0.69314718055994530942f
-                                               : -__builtin_huge_valf();
+            if (a.lse && grp == 0) {
+                // natural log-sum-exp of the scaled scores: (shift + log2 l) * ln 2
+                a.lse[bh * a.Sq + qi] = (lt > 0.f) ? (ms[u] + __builtin_log2f(lt)) * 0.69314718055994530942f
+                                                   : -kInf;
+            }
         }
     }
 }

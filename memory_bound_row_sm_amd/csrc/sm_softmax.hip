@@ -1061,6 +1061,8 @@ int run_rms(const RmsProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
 }
 
 // ------------------------------------------------------------ fused attention
+constexpr int64_t kAttnMaxRowStride = int64_t(1) << 24;  // elements
+
 struct AttnProblem {
     uintptr_t q, k, v, o, lse;  // lse may be 0
     int64_t BH, Sq, Sk, d;
@@ -1087,8 +1089,10 @@ int validate_attn(const AttnProblem& p) {
     const int es = 2;
     if (!p.q || !p.o || (p.Sk > 0 && (!p.k || !p.v))) return SM_ERR_INVALID;
     // 16-byte rows: base, row and head strides multiples of 8 elements
+    // row strides below 2^24 elements: a K/V tile is addressed with 32-bit offsets
     auto aligned = [&](uintptr_t ptr, int64_t rs, int64_t hs) {
-        return ptr % 16 == 0 && rs % 8 == 0 && hs % 8 == 0 && rs >= p.d && hs >= 0;
+        return ptr % 16 == 0 && rs % 8 == 0 && hs % 8 == 0 && rs >= p.d && rs <= kAttnMaxRowStride &&
+               hs >= 0;
     };
     if (!aligned(p.q, p.q_rs, p.q_hs) || !aligned(p.o, p.o_rs, p.o_hs)) return SM_ERR_INVALID;
     if (p.Sk > 0 && (!aligned(p.k, p.k_rs, p.k_hs) || !aligned(p.v, p.v_rs, p.v_hs)))
@@ -1144,8 +1148,10 @@ int run_attn(const AttnProblem& p, const sm_softmax_opts* opts, hipStream_t stre
     a.Sq = (int)p.Sq;
     a.Sk = (int)p.Sk;
     a.qblocks = (int)((p.Sq + kAttnBM - 1) / kAttnBM);
+    // causal: q-blocks i and qblocks-1-i form one item (equal work per item)
+    a.items = p.causal ? (a.qblocks + 1) / 2 : a.qblocks;
     a.scale_log2 = p.scale * 1.44269504088896340736f;
-    const int64_t grid = p.BH * a.qblocks;
+    const int64_t grid = p.BH * a.items;
     e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)grid), dim3(kAttnThreads), stream,
                  o.start_event, o.stop_event, a);
     return e == hipSuccess ? SM_OK : hip_fail(e);

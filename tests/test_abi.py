@@ -366,6 +366,7 @@ def attn(BH=2, Sq=64, Sk=64, d=128, q=BASE, k=BASE * 2, v=BASE * 3, o=BASE * 4, 
     (dict(strides=(130, 64 * 130, 128, 8192, 128, 8192, 128, 8192)), INVALID),  # row stride % 8
     (dict(strides=(120, 64 * 120, 128, 8192, 128, 8192, 128, 8192)), INVALID),  # row stride < d
     (dict(strides=(128, 8192, 128, 8192, 128, 8192, 128, 64)), INVALID),        # o heads overlap
+    (dict(BH=1, strides=(128, 8192, (1 << 24) + 8, 0, 128, 8192, 128, 8192)), INVALID),  # k row stride > 2^24
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(o=BASE + 4096), OVERLAP),                    # o inside q
     (dict(o=BASE * 3 + 1024), OVERLAP),                # o inside v

@@ -68,6 +68,27 @@ def test_large_scores_and_scale():
         compare_attn(o, q, k, v, 0.3, causal, lse_gpu=ls, what=f"sharp causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_negative_and_zero_scale(causal):
+    """A negative scale (folded into the sign of Q) and scale 0 (uniform weights over the
+    visible keys)."""
+    q, k, v = qkv(3, 200, 260, 64, "bf16", seed=21)
+    for scale in (-0.125, -1.5, 0.0):
+        o, ls = run(q, k, v, causal, scale=scale, lse=True)
+        compare_attn(o, q, k, v, scale, causal, lse_gpu=ls, what=f"scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_item_order_over_many_workgroups(causal):
+    """Grids of 15 and 30 work items (not multiples of the 8 XCDs), an odd q-block count
+    (the middle q-block of a head has no causal partner) and Sq != Sk."""
+    for BH, Sq, Sk in [(5, 700, 700), (3, 1300, 1500), (2, 640, 129)]:
+        q, k, v = qkv(BH, Sq, Sk, 128, "f16", seed=BH * Sq)
+        o, ls = run(q, k, v, causal, lse=True)
+        compare_attn(o, q, k, v, 1.0 / math.sqrt(128), causal, lse_gpu=ls,
+                     what=f"{BH}x{Sq}x{Sk} causal={causal}")
+
+
 def test_strided_heads():
     """q, k, v as [1, S, H, d] tensors viewed as [H, S, d] (row stride H * d, head stride d)."""
     H, S, d = 4, 160, 64

@@ -103,19 +103,37 @@ __device__ __forceinline__ uint32_t attn_pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, e2));
 }
 
+// Max / sum over the 4 lane groups of a lane column (lanes l, l^16, l^32, l^48).
+// gfx950's v_permlane32_swap / v_permlane16_swap of a value with itself pair every
+// lane with lane l^32 / l^16 (position in the row kept): two swaps, no LDS traffic.
+__device__ __forceinline__ float attn_xgroup(float x, bool is_max) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const float a0 = __builtin_bit_cast(float, r32[0]), a1 = __builtin_bit_cast(float, r32[1]);
+    const float y = is_max ? __builtin_fmaxf(a0, a1) : a0 + a1;
+    const uint32_t c = __builtin_bit_cast(uint32_t, y);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+    const float b0 = __builtin_bit_cast(float, r16[0]), b1 = __builtin_bit_cast(float, r16[1]);
+    return is_max ? __builtin_fmaxf(b0, b1) : b0 + b1;
+}
+
 template <int DT, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 k_attention_fwd(const AttnArgs a) {
     constexpr int BN = kAttnBN;
-    constexpr int KS = D + 8;       // K row stride in LDS (elements): 16-byte pad
-    constexpr int VS = BN + 8;      // V^T row stride in LDS (elements)
+    // LDS row strides (elements), chosen by measured bank conflicts: K rows 16 bytes
+    // longer than d (272 B at d = 128), V^T rows 8 bytes longer than BN (136 B); V^T
+    // rows of 144 B had 3x the conflict cycles, 128-B or 288-B K rows far more
+    constexpr int KS = D + 8;
+    constexpr int VS = BN + 4;
     constexpr int KCH = D / 8;      // 16-byte chunks per K/V row
     constexpr int LOADS = BN * KCH / kAttnThreads;  // 16-byte chunks per thread per tile
     constexpr int DSUB = D / 16;    // 16-wide d subtiles of the output
     constexpr int KK = D / 32;      // 32-wide d steps of the score product
     constexpr float kInf = __builtin_huge_valf();
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+    // two K and V^T tiles: the next block is staged while the current one is read
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2 * BN * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[2 * D * VS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,16 +194,18 @@ k_attention_fwd(const AttnArgs a) {
             vreg[e] = zv;
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](int buf) {
+        uint16_t* kdst = ks + buf * (BN * KS);
+        uint16_t* vdst = vt + buf * (D * VS);
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
             const int t = tid + kAttnThreads * it;
             const int r = t / KCH, ch = t % KCH;
-            *reinterpret_cast<attn_u4*>(&ks[r * KS + ch * 8]) = kreg[it];
+            *reinterpret_cast<attn_u4*>(&kdst[r * KS + ch * 8]) = kreg[it];
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {  // word w of a key's chunk holds d columns 2w, 2w+1
-            uint16_t* lo_row = &vt[(vch * 8 + 2 * w) * VS + vkg * KPT];
+            uint16_t* lo_row = &vdst[(vch * 8 + 2 * w) * VS + vkg * KPT];
             uint16_t* hi_row = lo_row + VS;
             const uint32_t a0 = vreg[0][w], a1 = vreg[1][w];
             const uint32_t lo01 = (a0 & 0xFFFFu) | (a1 << 16), hi01 = (a0 >> 16) | (a1 & 0xFFFF0000u);
@@ -236,110 +256,114 @@ k_attention_fwd(const AttnArgs a) {
         if (CAUSAL) kend = min(a.Sk, max(0, qblk * kAttnBM + kAttnBM - 1 + off + 1));
         const int nblk = (kend + BN - 1) / BN;
 
-        if (nblk > 0) fetch(0);
+        // One barrier per block: after it, every wave has read tile blk and tile blk+1
+        // is in LDS; the loads of tile blk+1 are in flight while tile blk is computed.
+        if (nblk > 0) {
+            fetch(0);
+            stage(0);
+        }
+        __syncthreads();
         for (int blk = 0; blk < nblk; ++blk) {
             const int kb = blk * BN;
-            __syncthreads();  // every wave is done reading the previous tile
-            stage();
-            __syncthreads();
-            if (blk + 1 < nblk) fetch(kb + BN);  // next tile in flight during this one
-            // every key of the block lies past every query's diagonal for this wave
-            if (CAUSAL && kb > q0 + 31 + off) continue;
-
-            // S^T tiles: t = key subtile (16 keys), u = query subtile
-            attn_f4 s[4][2];
+            const uint16_t* kcur = ks + (blk & 1) * (BN * KS);
+            const uint16_t* vcur = vt + (blk & 1) * (D * VS);
+            if (blk + 1 < nblk) fetch(kb + BN);
+            // skipped when every key of the block lies past every query's diagonal for this wave
+            if (!(CAUSAL && kb > q0 + 31 + off)) {
+                // S^T tiles: t = key subtile (16 keys), u = query subtile
+                attn_f4 s[4][2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) s[t][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
+                    for (int u = 0; u < 2; ++u) s[t][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
+                for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const attn_u4 ka = *reinterpret_cast<const attn_u4*>(&ks[(t * 16 + col) * KS + kk * 32 + grp * 8]);
+                    for (int t = 0; t < 4; ++t) {
+                        const attn_u4 ka = *reinterpret_cast<const attn_u4*>(&kcur[(t * 16 + col) * KS + kk * 32 + grp * 8]);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
+                        for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
+                    }
                 }
-            }
 
-            // Blocks cut by the end of the keys or by a diagonal of this wave's queries
-            // are scaled and masked element by element (cc = 1 then); all others keep the
-            // raw products and fold the scale into the exponent's FMA.
-            const bool need_mask = (kb + BN > a.Sk) || (CAUSAL && kb + BN - 1 > q0 + off);
-            const float cc = need_mask ? 1.f : c;
-            attn_u4 pb[2][2];  // P as the B operand: [u][32-key step]
+                // Blocks cut by the end of the keys or by a diagonal of this wave's queries
+                // are scaled and masked element by element (cc = 1 then); all others keep the
+                // raw products and fold the scale into the exponent's FMA.
+                const bool need_mask = (kb + BN > a.Sk) || (CAUSAL && kb + BN - 1 > q0 + off);
+                const float cc = need_mask ? 1.f : c;
+                attn_u4 pb[2][2];  // P as the B operand: [u][32-key step]
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (need_mask) {
-                    // key kb + grp*4 + (t*16 + i) is visible iff t*16 + i <= lim
-                    int lim = a.Sk - 1;
-                    if (CAUSAL) lim = min(lim, q0 + u * 16 + col + off);
-                    lim -= kb + grp * 4;
+                for (int u = 0; u < 2; ++u) {
+                    if (need_mask) {
+                        // key kb + grp*4 + (t*16 + i) is visible iff t*16 + i <= lim
+                        int lim = a.Sk - 1;
+                        if (CAUSAL) lim = min(lim, q0 + u * 16 + col + off);
+                        lim -= kb + grp * 4;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i] * c;
+                    }
+                    float bmax = -kInf;
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i] * c;
-                }
-                float bmax = -kInf;
+                        for (int i = 0; i < 4; ++i) bmax = __builtin_fmaxf(bmax, s[t][u][i]);
+                    bmax = attn_xgroup(bmax, true);
+                    bmax *= cc;  // scaled (c >= 0 keeps the order)
+                    const bool grow = bmax > m[u] + kAttnLazy;
+                    if (__any(grow)) {
+                        const float mn = grow ? bmax : m[u];
+                        const float sn = (mn == -kInf) ? 0.f : mn;
+                        const float alpha = __builtin_amdgcn_exp2f(m[u] - sn);  // m = -inf -> 0
+                        m[u] = mn;
+                        ms[u] = sn;
+                        l[u] *= alpha;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) bmax = __builtin_fmaxf(bmax, s[t][u][i]);
-                bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 16));
-                bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 32));
-                bmax *= cc;  // scaled (c >= 0 keeps the order)
-                const bool grow = bmax > m[u] + kAttnLazy;
-                if (__any(grow)) {
-                    const float mn = grow ? bmax : m[u];
-                    const float sn = (mn == -kInf) ? 0.f : mn;
-                    const float alpha = __builtin_amdgcn_exp2f(m[u] - sn);  // m = -inf -> 0
-                    m[u] = mn;
-                    ms[u] = sn;
-                    l[u] *= alpha;
-#pragma unroll
-                    for (int d = 0; d < DSUB; ++d) oacc[d][u] *= alpha;
-                }
-                float p[4][4];
-                float psum = 0.f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][u][i], cc, -ms[u]));
-                        psum += p[t][i];
+                        for (int d = 0; d < DSUB; ++d) oacc[d][u] *= alpha;
                     }
-                l[u] += psum;
+                    float p[4][4];
+                    float psum = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][u][i], cc, -ms[u]));
+                            psum += p[t][i];
+                        }
+                    l[u] += psum;
+#pragma unroll
+                    for (int cs = 0; cs < 2; ++cs) {
+                        // 32-key step cs: slots 0..3 <- subtile 2cs, slots 4..7 <- subtile 2cs+1
+                        const int t0 = 2 * cs, t1 = 2 * cs + 1;
+                        pb[u][cs] = attn_u4{attn_pack2<DT>(p[t0][0], p[t0][1]), attn_pack2<DT>(p[t0][2], p[t0][3]),
+                                            attn_pack2<DT>(p[t1][0], p[t1][1]), attn_pack2<DT>(p[t1][2], p[t1][3])};
+                    }
+                }
+
+                // O^T += V^T P^T: A = V^T rows d, keys in the same slot order as P
 #pragma unroll
                 for (int cs = 0; cs < 2; ++cs) {
-                    // 32-key step cs: slots 0..3 <- subtile 2cs, slots 4..7 <- subtile 2cs+1
-                    const int t0 = 2 * cs, t1 = 2 * cs + 1;
-                    pb[u][cs] = attn_u4{attn_pack2<DT>(p[t0][0], p[t0][1]), attn_pack2<DT>(p[t0][2], p[t0][3]),
-                                        attn_pack2<DT>(p[t1][0], p[t1][1]), attn_pack2<DT>(p[t1][2], p[t1][3])};
+#pragma unroll
+                    for (int d = 0; d < DSUB; ++d) {
+                        const uint16_t* vrow = &vcur[(d * 16 + col) * VS];
+                        const attn_u2 lo = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs) * 16 + grp * 4);
+                        const attn_u2 hi = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs + 1) * 16 + grp * 4);
+                        const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);
+                    }
                 }
             }
-
-            // O^T += V^T P^T: A = V^T rows d, keys in the same slot order as P
-#pragma unroll
-            for (int cs = 0; cs < 2; ++cs) {
-#pragma unroll
-                for (int d = 0; d < DSUB; ++d) {
-                    const uint16_t* vrow = &vt[(d * 16 + col) * VS];
-                    const attn_u2 lo = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs) * 16 + grp * 4);
-                    const attn_u2 hi = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs + 1) * 16 + grp * 4);
-                    const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);
-                }
-            }
+            if (blk + 1 < nblk) stage((blk + 1) & 1);
+            __syncthreads();
         }
 
         // finish: the full row sum over the 4 lane groups, normalise, store
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            float lt = l[u];
-            lt += __shfl_xor(lt, 16);
-            lt += __shfl_xor(lt, 32);
+            const float lt = attn_xgroup(l[u], false);
             const int qi = q0 + u * 16 + col;
             if (qi >= a.Sq) continue;
             const float r = (lt > 0.f) ? 1.0f / lt : 0.f;

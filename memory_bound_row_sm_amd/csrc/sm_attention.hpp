@@ -104,17 +104,20 @@ __device__ __forceinline__ uint32_t attn_pack2(float x, float y) {
 }
 
 // Max / sum over the 4 lane groups of a lane column (lanes l, l^16, l^32, l^48).
-// gfx950's v_permlane32_swap / v_permlane16_swap of a value with itself pair every
-// lane with lane l^32 / l^16 (position in the row kept): two swaps, no LDS traffic.
+// gfx950's v_permlane32_swap / v_permlane16_swap exchange lanes between two registers:
+// given two copies of x they return x and its partner lane l^32 / l^16 (position in the
+// row kept), with no LDS traffic. The two results are copied to scalars before the
+// bit cast: a bit cast of an element of the returned vector reads element 0.
+__device__ __forceinline__ float attn_swap_op(float x, bool is_max, bool half32) {
+    const uint32_t a = __builtin_bit_cast(uint32_t, x);
+    const auto r = half32 ? __builtin_amdgcn_permlane32_swap(a, a, false, false)
+                          : __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    const uint32_t u0 = r[0], u1 = r[1];
+    const float r0 = __builtin_bit_cast(float, u0), r1 = __builtin_bit_cast(float, u1);
+    return is_max ? __builtin_fmaxf(r0, r1) : r0 + r1;
+}
 __device__ __forceinline__ float attn_xgroup(float x, bool is_max) {
-    const uint32_t b = __builtin_bit_cast(uint32_t, x);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-    const float a0 = __builtin_bit_cast(float, r32[0]), a1 = __builtin_bit_cast(float, r32[1]);
-    const float y = is_max ? __builtin_fmaxf(a0, a1) : a0 + a1;
-    const uint32_t c = __builtin_bit_cast(uint32_t, y);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
-    const float b0 = __builtin_bit_cast(float, r16[0]), b1 = __builtin_bit_cast(float, r16[1]);
-    return is_max ? __builtin_fmaxf(b0, b1) : b0 + b1;
+    return attn_swap_op(attn_swap_op(x, is_max, true), is_max, false);
 }
 
 template <int DT, int D, bool CAUSAL>

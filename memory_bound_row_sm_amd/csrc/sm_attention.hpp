@@ -15,14 +15,15 @@
 //   online softmax: scale, mask, block max across the 4 lane groups, rescale the
 //                 running sum and the output, p = exp2(s - m), P rounded to the
 //                 input dtype as the B operand of the next product.
-//   O^T += V^T P^T (d x queries): A = V^T from LDS (V is stored transposed in LDS),
-//                 B = P straight from the score registers. The contraction order
+//   O^T += V^T P^T (d x queries): A = V^T, read from the row-major V tile in LDS
+//                 with gfx950's transposed LDS read; B = P straight from the score
+//                 registers. The contraction order
 //                 over the 32 keys of an MFMA step is permuted identically on both
 //                 operands, so no shuffle of P is needed, and the output tile keeps
 //                 the query in the lane column, so the rescale is per lane.
 // The next key block's K and V are loaded into registers while the current block
-// is computed, and written to LDS after it (one buffer, two barriers per block); V
-// is transposed on the way (8-byte stores of 4 keys per d column).
+// is computed, and written to the other of two LDS buffers after it (one barrier
+// per block).
 //
 // Causal masking is aligned to the bottom right: query i sees keys j <= i + Sk - Sq.
 // A query that sees no key (Sq > Sk) gets zeros and lse = -inf (the all -inf row
@@ -125,18 +126,19 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
 k_attention_fwd(const AttnArgs a) {
     constexpr int BN = kAttnBN;
     // LDS row strides (elements), chosen by measured bank conflicts: K rows 16 bytes
-    // longer than d (272 B at d = 128), V^T rows 8 bytes longer than BN (136 B); V^T
-    // rows of 144 B had 3x the conflict cycles, 128-B or 288-B K rows far more
+    // longer than d (272 B at d = 128: 128-B or 288-B K rows had far more conflicts);
+    // V rows 32 bytes longer than d, so that the 4 rows one 16-lane transposed read
+    // touches fall on disjoint banks
     constexpr int KS = D + 8;
-    constexpr int VS = BN + 4;
+    constexpr int VR = D + 16;
     constexpr int KCH = D / 8;      // 16-byte chunks per K/V row
     constexpr int LOADS = BN * KCH / kAttnThreads;  // 16-byte chunks per thread per tile
     constexpr int DSUB = D / 16;    // 16-wide d subtiles of the output
     constexpr int KK = D / 32;      // 32-wide d steps of the score product
     constexpr float kInf = __builtin_huge_valf();
-    // two K and V^T tiles: the next block is staged while the current one is read
+    // two K and V tiles (row-major): the next block is staged while the current one is read
     __shared__ __attribute__((aligned(16))) uint16_t ks[2 * BN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[2 * D * VS];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2 * BN * VR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -161,67 +163,50 @@ k_attention_fwd(const AttnArgs a) {
     const float c = __builtin_fabsf(a.scale_log2);
     const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-    // Register staging of one K/V tile. K: chunk t = tid + 256 * it -> row t / KCH,
-    // chunk t % KCH (row-major copy into LDS). V: thread (kg = tid % VG, ch = tid / VG)
-    // loads keys KPT * kg .. + KPT - 1 of d-chunk ch and writes each of its 8 d columns
-    // as one store of KPT keys into V^T: the VG lanes of one chunk write one contiguous
-    // 128-byte stretch of a V^T row (no bank conflicts, no 2-byte stores).
-    constexpr int KPT = BN * KCH / kAttnThreads;  // keys per thread of the V tile (D / 32)
-    constexpr int VG = BN / KPT;                  // key groups per d-chunk
-    static_assert(KPT == 2 || KPT == 4, "V staging assumes d = 64 or 128");
-    attn_u4 kreg[LOADS], vreg[KPT];
-    const int vkg = tid % VG, vch = tid / VG;
-    // 32-bit lane offsets inside a tile (row strides are below 2^24 elements), added to
-    // the tile's wave-uniform base: one VGPR per address
-    constexpr int KR = kAttnThreads / KCH;  // K rows covered by one pass of the threads
-    const int krow = tid / KCH;
-    const uint32_t k_lane = (uint32_t)krow * (uint32_t)a.k_rs + (uint32_t)(tid % KCH) * 16u;
+    // Register staging of one K/V tile: chunk t = tid + 256 * it -> row t / KCH, chunk
+    // t % KCH, copied row-major into LDS. Lane offsets inside a tile are 32-bit (row
+    // strides are below 2^24 elements), added to the tile's wave-uniform base.
+    attn_u4 kreg[LOADS], vreg[LOADS];
+    constexpr int KR = kAttnThreads / KCH;  // rows covered by one pass of the threads
+    const int krow = tid / KCH, kch = tid % KCH;
+    const uint32_t k_lane = (uint32_t)krow * (uint32_t)a.k_rs + (uint32_t)kch * 16u;
     const uint32_t k_step = (uint32_t)KR * (uint32_t)a.k_rs;
-    const uint32_t v_lane = (uint32_t)(vkg * KPT) * (uint32_t)a.v_rs + (uint32_t)vch * 16u;
-    const uint32_t v_rs32 = (uint32_t)a.v_rs;
+    const uint32_t v_lane = (uint32_t)krow * (uint32_t)a.v_rs + (uint32_t)kch * 16u;
+    const uint32_t v_step = (uint32_t)KR * (uint32_t)a.v_rs;
     auto fetch = [&](int kb) {
         const unsigned char* kt = kh + (int64_t)kb * a.k_rs;
         const unsigned char* vtile = vh + (int64_t)kb * a.v_rs;
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
-            attn_u4 zk = {0u, 0u, 0u, 0u};
-            if (kb + krow + KR * it < a.Sk)
+            attn_u4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+            if (kb + krow + KR * it < a.Sk) {
                 zk = *reinterpret_cast<const attn_u4*>(kt + (k_lane + (uint32_t)it * k_step));
+                zv = *reinterpret_cast<const attn_u4*>(vtile + (v_lane + (uint32_t)it * v_step));
+            }
             kreg[it] = zk;
-        }
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            attn_u4 zv = {0u, 0u, 0u, 0u};
-            if (kb + vkg * KPT + e < a.Sk)
-                zv = *reinterpret_cast<const attn_u4*>(vtile + (v_lane + (uint32_t)e * v_rs32));
-            vreg[e] = zv;
+            vreg[it] = zv;
         }
     };
     auto stage = [&](int buf) {
         uint16_t* kdst = ks + buf * (BN * KS);
-        uint16_t* vdst = vt + buf * (D * VS);
+        uint16_t* vdst = vs + buf * (BN * VR);
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
-            const int t = tid + kAttnThreads * it;
-            const int r = t / KCH, ch = t % KCH;
-            *reinterpret_cast<attn_u4*>(&kdst[r * KS + ch * 8]) = kreg[it];
+            const int r = krow + KR * it;
+            *reinterpret_cast<attn_u4*>(&kdst[r * KS + kch * 8]) = kreg[it];
+            *reinterpret_cast<attn_u4*>(&vdst[r * VR + kch * 8]) = vreg[it];
         }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // word w of a key's chunk holds d columns 2w, 2w+1
-            uint16_t* lo_row = &vdst[(vch * 8 + 2 * w) * VS + vkg * KPT];
-            uint16_t* hi_row = lo_row + VS;
-            const uint32_t a0 = vreg[0][w], a1 = vreg[1][w];
-            const uint32_t lo01 = (a0 & 0xFFFFu) | (a1 << 16), hi01 = (a0 >> 16) | (a1 & 0xFFFF0000u);
-            if constexpr (KPT == 4) {
-                const uint32_t a2 = vreg[2][w], a3 = vreg[3][w];
-                const uint32_t lo23 = (a2 & 0xFFFFu) | (a3 << 16), hi23 = (a2 >> 16) | (a3 & 0xFFFF0000u);
-                *reinterpret_cast<attn_u2*>(lo_row) = attn_u2{lo01, lo23};
-                *reinterpret_cast<attn_u2*>(hi_row) = attn_u2{hi01, hi23};
-            } else {
-                *reinterpret_cast<uint32_t*>(lo_row) = lo01;
-                *reinterpret_cast<uint32_t*>(hi_row) = hi01;
-            }
-        }
+    };
+    // V^T operand through gfx950's transposed LDS read (ds_read_b64_tr_b16): in each
+    // 16-lane group, lane i receives element i % 4 of the 8-byte pieces addressed by
+    // lanes 4k + i / 4, k = 0..3. Lane (col, grp) addresses key row key0 + col / 4, d
+    // columns dbase + 4 * (col % 4) .. + 3, and so receives V[key0 + k][dbase + col].
+    const int vrd = (col >> 2) * VR + 4 * (col & 3);
+    auto vt_read = [&](const uint16_t* vtile, int key0, int dbase) -> attn_u2 {
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(vtile + key0 * VR + dbase + vrd));
+        return __builtin_bit_cast(attn_u2, r);
     };
 
     for (int pass = 0; pass < npass; ++pass) {
@@ -269,7 +254,7 @@ k_attention_fwd(const AttnArgs a) {
         for (int blk = 0; blk < nblk; ++blk) {
             const int kb = blk * BN;
             const uint16_t* kcur = ks + (blk & 1) * (BN * KS);
-            const uint16_t* vcur = vt + (blk & 1) * (D * VS);
+            const uint16_t* vcur = vs + (blk & 1) * (BN * VR);
             if (blk + 1 < nblk) fetch(kb + BN);
             // skipped when every key of the block lies past every query's diagonal for this wave
             if (!(CAUSAL && kb > q0 + 31 + off)) {
@@ -350,9 +335,8 @@ k_attention_fwd(const AttnArgs a) {
                 for (int cs = 0; cs < 2; ++cs) {
 #pragma unroll
                     for (int d = 0; d < DSUB; ++d) {
-                        const uint16_t* vrow = &vcur[(d * 16 + col) * VS];
-                        const attn_u2 lo = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs) * 16 + grp * 4);
-                        const attn_u2 hi = *reinterpret_cast<const attn_u2*>(vrow + (2 * cs + 1) * 16 + grp * 4);
+                        const attn_u2 lo = vt_read(vcur, (2 * cs) * 16 + grp * 4, d * 16);
+                        const attn_u2 hi = vt_read(vcur, (2 * cs + 1) * 16 + grp * 4, d * 16);
                         const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
                         for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);

@@ -25,8 +25,16 @@ The softmax backward (dx = y * (dy - sum(y * dy)), byte model 3 * M * N * elem, 
 5 * M * N * elem on the two-pass wide path) is timed the same way on the same shape,
 with y the forward's output and a seeded dy, and reported beside the headline.
 
+The fused attention forward (softmax(scale * Q K^T) V with the online softmax, the
+fusion "Fused Softmax on GPU" names in its closing section) is timed on the
+attention-shaped workload -- 8 x 32 heads, 2048 queries and keys, d = 128, BF16,
+causal -- against the MFMA roofline: FLOPs = 4 * heads * d * visible (query, key)
+pairs over the dense BF16 peak of 2.5 PFLOP/s; torch's SDPA on the same tensors is
+reported beside it as a reference point.
+
 Prints ONE JSON line on stdout. ``--sweep`` also times every workload and plan,
-forward and backward, and writes those lines to stderr.
+forward and backward, the residual RMSNorm shapes and the attention shapes, and
+writes those lines to stderr.
 """
 from __future__ import annotations
 
@@ -45,6 +53,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16/FP16 MFMA
+# attention-shaped workload: 8 x 32 heads, 2048 x 2048, head dim 128, BF16, causal
+ATTN_WORKLOAD = {"heads": 8 * 32, "S": 2048, "d": 128, "dtype": "bf16", "causal": True}
 FLUSH_BYTES = 1 << 30
 WORKLOAD = "normal_bf16_4096x4096"
 # device code of the one-pass row kernels: a traffic record stays valid while these
@@ -165,6 +176,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing on the host")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-attention", action="store_true", help="skip the attention timing")
     ap.add_argument("--plan-grid", metavar="OUT_JSON",
                     help="time every plan on the row-plan grid (18 row counts x 10 widths, "
                          "BF16 forward), write the cell times to OUT_JSON, print the regret "
@@ -334,9 +346,15 @@ def main(argv=None) -> int:
     if not args.no_backward:
         bwd = bench_backward(torch, sm, workloads, out, flush, s_handle, args.steps, args.warmup, log)
 
+    # ---------------------------------------------------------------- attention forward
+    attn = None
+    if not args.no_attention:
+        attn = bench_attention(torch, sm, s_handle, args.steps, args.warmup, log)
+
     # ---------------------------------------------------------------- sweep (stderr)
     if args.sweep:
         sweep(torch, sm, workloads, flush, s_handle, log, args)
+        sweep_attention(torch, sm, s_handle, log, max(10, args.steps // 10))
 
     # ---------------------------------------------------------------- CPU baseline
     cpu, parity = None, {"passed": None, "note": "oracle leg skipped (--no-cpu-baseline)"}
@@ -378,6 +396,7 @@ def main(argv=None) -> int:
                      "unit": "GB/s", "frac": round(gbps / PEAK_GBPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "backward": bwd,
+        "attention": attn,
     }
     print(json.dumps(result), flush=True)
     return 0 if parity.get("passed") is not False else 1
@@ -821,6 +840,116 @@ def bench_backward(torch, sm, workloads, y, flush, s_handle, steps, warmup, log)
     if not info["max_abs_row_sum"] < 0.05:
         raise RuntimeError(f"backward rows do not sum to about 0: {info['max_abs_row_sum']}")
     return res
+
+
+def attention_pairs(Sq: int, Sk: int, causal: bool) -> int:
+    """Visible (query, key) pairs of one head; the causal mask is aligned to the bottom
+    right (query i sees keys j <= i + Sk - Sq)."""
+    if not causal:
+        return Sq * Sk
+    off = Sk - Sq
+    return sum(max(0, min(Sk, i + off + 1)) for i in range(Sq))
+
+
+def time_attention(torch, sm, q, k, v, o, causal, s_handle, steps, warmup):
+    """sm_attention_fwd_ex on [BH][S][d] tensors, each call bracketed by its own events."""
+    BH, Sq, d = q.shape
+    Sk = k.shape[1]
+    dt = {torch.float16: sm.SM_F16, torch.bfloat16: sm.SM_BF16}[q.dtype]
+    st_ = (q.stride(1), q.stride(0), k.stride(1), k.stride(0), v.stride(1), v.stride(0),
+           o.stride(1), o.stride(0))
+    opts = sm.SmOpts()
+
+    def call(events=(None, None)):
+        opts.start_event, opts.stop_event = events
+        rc = sm.sm_attention_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0, BH, Sq,
+                                    Sk, d, st_, 1.0 / float(d) ** 0.5, int(causal), dt, opts, s_handle)
+        if rc != 0:
+            raise sm.SoftmaxError(rc, "sm_attention_fwd_ex")
+
+    for _ in range(warmup):
+        call()
+    t = DispatchEvents(steps)
+    for _ in range(steps):
+        call(t.next_pair())
+    st = stats_us(t.samples_ms(torch))
+    t.close()
+    return st
+
+
+def time_torch_sdpa(torch, q, k, v, causal, steps):
+    """torch's scaled_dot_product_attention on the same tensors (a reference point; it
+    aligns the causal mask top-left, the same as bottom-right when Sq == Sk)."""
+    F = torch.nn.functional
+    qq, kk, vv = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+    for _ in range(3):
+        F.scaled_dot_product_attention(qq, kk, vv, is_causal=causal)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        F.scaled_dot_product_attention(qq, kk, vv, is_causal=causal)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def attention_inputs(torch, BH, S, d, dtype, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return [torch.randn(BH, S, d, device="cuda", generator=g).to(tdt) for _ in range(3)]
+
+
+def bench_attention(torch, sm, s_handle, steps, warmup, log):
+    w = ATTN_WORKLOAD
+    BH, S, d, causal = w["heads"], w["S"], w["d"], w["causal"]
+    q, k, v = attention_inputs(torch, BH, S, d, w["dtype"], 2026)
+    o = torch.full_like(q, float("nan"))
+    st = time_attention(torch, sm, q, k, v, o, causal, s_handle, min(steps, 50), min(warmup, 5))
+    torch.cuda.synchronize()
+    # exact properties of a correct output: finite, and the first query of every head
+    # sees only key 0, so its output row is v_0 itself
+    if not bool(torch.isfinite(o).all()) or not torch.equal(o[:, 0].view(torch.int16),
+                                                            v[:, 0].view(torch.int16)):
+        raise RuntimeError("attention property gate failed")
+    flops = 4 * BH * d * attention_pairs(S, S, causal)
+    tflops = flops / (st["mean_us"] * 1e-6) / 1e12
+    ref_us = time_torch_sdpa(torch, q, k, v, causal, 10)
+    res = {"op": "fused attention forward (online softmax)", "workload": "attention_bf16_256x2048x2048_d128",
+           "heads": BH, "Sq": S, "Sk": S, "d": d, "causal": causal, "dtype": w["dtype"],
+           "flops": flops, "mean_us": round(st["mean_us"], 2), "median_us": round(st["median_us"], 2),
+           "TFLOPs": round(tflops, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+           "torch_sdpa_us": round(ref_us, 2), "speedup_vs_torch_sdpa": round(ref_us / st["mean_us"], 3)}
+    log(f"[bench] attention: {res}")
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return res
+
+
+ATTN_SHAPES = [("bf16", 256, 2048, 128, True), ("bf16", 256, 2048, 128, False),
+               ("f16", 256, 2048, 128, True), ("bf16", 256, 2048, 64, True),
+               ("bf16", 256, 2048, 64, False), ("bf16", 64, 4096, 128, True),
+               ("bf16", 32, 8192, 128, True), ("bf16", 1024, 512, 128, True)]
+
+
+def sweep_attention(torch, sm, s_handle, log, steps):
+    """Attention forward at the sweep's shapes, against the MFMA roofline and torch's SDPA."""
+    for dt, BH, S, d, causal in ATTN_SHAPES:
+        q, k, v = attention_inputs(torch, BH, S, d, dt, 7)
+        o = torch.empty_like(q)
+        st = time_attention(torch, sm, q, k, v, o, causal, s_handle, steps, 3)
+        tflops = 4 * BH * d * attention_pairs(S, S, causal) / (st["mean_us"] * 1e-6) / 1e12
+        ref_us = time_torch_sdpa(torch, q, k, v, causal, 5)
+        line = {"workload": f"attention_{dt}_{BH}x{S}x{S}_d{d}", "op": "attention",
+                "causal": causal, "mean_us": round(st["mean_us"], 2),
+                "median_us": round(st["median_us"], 2), "TFLOPs": round(tflops, 1),
+                "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                "torch_sdpa_us": round(ref_us, 2)}
+        log("[sweep] " + json.dumps(line))
+        del q, k, v, o
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -54,3 +54,16 @@ def test_stats_and_summaries():
     st = bench.stats_us([0.001, 0.002, 0.003, 0.004])
     assert st["median_us"] == 2.5 and st["min_us"] == 1.0 and st["max_us"] == 4.0
     assert st["mean_us"] == 2.5 and st["n"] == 4
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (5, 3), (3, 5), (64, 64), (130, 70), (2048, 2048)])
+def test_attention_pair_count(Sq, Sk):
+    """The attention FLOP model counts the (query, key) pairs the bottom-right causal
+    mask leaves visible: brute force over the mask, and S(S+1)/2 when Sq == Sk."""
+    import numpy as np
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    assert bench.attention_pairs(Sq, Sk, True) == int((j <= i + Sk - Sq).sum())
+    assert bench.attention_pairs(Sq, Sk, False) == Sq * Sk
+    if Sq == Sk:
+        assert bench.attention_pairs(Sq, Sk, True) == Sq * (Sq + 1) // 2

@@ -2,8 +2,9 @@
 //
 // O = softmax(scale * Q K^T [causal]) V per (batch-head, query row), never writing
 // the score matrix: the step after the row softmax that "Fused Softmax on GPU"
-// names in its closing section, "Wrapping Up" (fusing the online softmax with the matmul before
-// it, as FlashAttention does), on the attention-logit workload of the same pages.
+// names in its closing section, "Wrapping Up" (fusing the online softmax with the
+// matmul before it, as FlashAttention does), on the attention-logit workload of the
+// same pages.
 //
 // Tiling. A workgroup of 4 waves owns 128 query rows of one head (32 per wave, two
 // 16-row subtiles) and walks the keys in blocks of 64. Contractions run on

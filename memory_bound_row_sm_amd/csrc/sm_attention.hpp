@@ -22,9 +22,9 @@
 //                 over the 32 keys of an MFMA step is permuted identically on both
 //                 operands, so no shuffle of P is needed, and the output tile keeps
 //                 the query in the lane column, so the rescale is per lane.
-// The next key block's K and V are loaded into registers while the current block
-// is computed, and written to the other of two LDS buffers after it (one barrier
-// per block).
+// The next key block's K and V are loaded from global memory straight into the
+// other of two LDS buffers while the current block is computed (one barrier per
+// block).
 //
 // Causal masking is aligned to the bottom right: query i sees keys j <= i + Sk - Sq.
 // A query that sees no key (Sq > Sk) gets zeros and lse = -inf (the all -inf row
@@ -74,6 +74,8 @@ constexpr int kAttnXcds = 8;  // MI355X: 8 accelerator dies, each with its own L
 // by more than this (log2 units): exponentials stay <= 2^8, and most blocks skip the
 // rescale of the output accumulators.
 constexpr float kAttnLazy = 8.0f;
+// s_waitcnt vmcnt(0) with the other counters at their maxima (gfx9 encoding)
+constexpr int kVmcnt0 = 0x0F70;
 
 struct AttnArgs {
     const unsigned char* q;
@@ -126,20 +128,22 @@ template <int DT, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 k_attention_fwd(const AttnArgs a) {
     constexpr int BN = kAttnBN;
-    // LDS row strides (elements), chosen by measured bank conflicts: K rows 16 bytes
-    // longer than d (272 B at d = 128: 128-B or 288-B K rows had far more conflicts);
-    // V rows 32 bytes longer than d, so that the 4 rows one 16-lane transposed read
-    // touches fall on disjoint banks
-    constexpr int KS = D + 8;
-    constexpr int VR = D + 16;
     constexpr int KCH = D / 8;      // 16-byte chunks per K/V row
     constexpr int LOADS = BN * KCH / kAttnThreads;  // 16-byte chunks per thread per tile
     constexpr int DSUB = D / 16;    // 16-wide d subtiles of the output
     constexpr int KK = D / 32;      // 32-wide d steps of the score product
     constexpr float kInf = __builtin_huge_valf();
-    // two K and V tiles (row-major): the next block is staged while the current one is read
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2 * BN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[2 * BN * VR];
+    // two K and two V tiles of BN rows x d, four separate LDS objects (so that the
+    // compiler sees that a block's reads and the next block's loads touch different
+    // memory and does not wait for the loads): the next block is loaded while the
+    // current one is read. Rows are unpadded; the 16-byte chunks of a row are XOR-swizzled
+    // (slot = row * KCH + (chunk ^ f(row))) so that the reads below hit distinct banks:
+    // K: 16 lanes read chunk kk*4+grp of rows t*16 + col; V: 16 lanes read 2 chunks of
+    // 4 consecutive rows (transposed read).
+    __shared__ __attribute__((aligned(16))) uint16_t ks0[BN * D], ks1[BN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t vs0[BN * D], vs1[BN * D];
+    auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+    auto vswz = [](int row) { return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,49 +168,52 @@ k_attention_fwd(const AttnArgs a) {
     const float c = __builtin_fabsf(a.scale_log2);
     const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-    // Register staging of one K/V tile: chunk t = tid + 256 * it -> row t / KCH, chunk
-    // t % KCH, copied row-major into LDS. Lane offsets inside a tile are 32-bit (row
-    // strides are below 2^24 elements), added to the tile's wave-uniform base.
-    attn_u4 kreg[LOADS], vreg[LOADS];
-    constexpr int KR = kAttnThreads / KCH;  // rows covered by one pass of the threads
-    const int krow = tid / KCH, kch = tid % KCH;
-    const uint32_t k_lane = (uint32_t)krow * (uint32_t)a.k_rs + (uint32_t)kch * 16u;
-    const uint32_t k_step = (uint32_t)KR * (uint32_t)a.k_rs;
-    const uint32_t v_lane = (uint32_t)krow * (uint32_t)a.v_rs + (uint32_t)kch * 16u;
-    const uint32_t v_step = (uint32_t)KR * (uint32_t)a.v_rs;
-    auto fetch = [&](int kb) {
+    // Tiles go from global memory straight into LDS (global_load_lds_dwordx4): wave w's
+    // load instruction `it` fills the 64 consecutive 16-byte slots (it * 4 + w) * 64 ..
+    // + 63 of a tile, lane l the slot of that range with index l, so each lane fetches the
+    // chunk that the swizzle puts in its slot. Offsets are 32-bit (row strides are below
+    // 2^24 elements) from the tile's wave-uniform base. Rows past the last key load the
+    // last key's row instead: finite data whose scores are masked and whose weights are 0.
+    uint32_t koff[LOADS], voff[LOADS];
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+        const int slot = (it * 4 + wave) * 64 + lane;
+        const int r = slot / KCH, pos = slot % KCH;
+        koff[it] = (uint32_t)r * (uint32_t)a.k_rs + (uint32_t)(pos ^ kswz(r)) * 16u;
+        voff[it] = (uint32_t)r * (uint32_t)a.v_rs + (uint32_t)(pos ^ vswz(r)) * 16u;
+    }
+    auto issue = [&](int kb, uint16_t* kdst, uint16_t* vdst) {
         const unsigned char* kt = kh + (int64_t)kb * a.k_rs;
         const unsigned char* vtile = vh + (int64_t)kb * a.v_rs;
+        const bool full = kb + BN <= a.Sk;
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
-            attn_u4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-            if (kb + krow + KR * it < a.Sk) {
-                zk = *reinterpret_cast<const attn_u4*>(kt + (k_lane + (uint32_t)it * k_step));
-                zv = *reinterpret_cast<const attn_u4*>(vtile + (v_lane + (uint32_t)it * v_step));
+            uint32_t ko = koff[it], vo = voff[it];
+            if (!full) {
+                const int slot = (it * 4 + wave) * 64 + lane;
+                const int r = slot / KCH, pos = slot % KCH;
+                const uint32_t rr = (uint32_t)min(r, a.Sk - 1 - kb);
+                ko = rr * (uint32_t)a.k_rs + (uint32_t)(pos ^ kswz(r)) * 16u;
+                vo = rr * (uint32_t)a.v_rs + (uint32_t)(pos ^ vswz(r)) * 16u;
             }
-            kreg[it] = zk;
-            vreg[it] = zv;
-        }
-    };
-    auto stage = [&](int buf) {
-        uint16_t* kdst = ks + buf * (BN * KS);
-        uint16_t* vdst = vs + buf * (BN * VR);
-#pragma unroll
-        for (int it = 0; it < LOADS; ++it) {
-            const int r = krow + KR * it;
-            *reinterpret_cast<attn_u4*>(&kdst[r * KS + kch * 8]) = kreg[it];
-            *reinterpret_cast<attn_u4*>(&vdst[r * VR + kch * 8]) = vreg[it];
+            uint16_t* kd = kdst + (it * 4 + wave) * 64 * 8;
+            uint16_t* vd = vdst + (it * 4 + wave) * 64 * 8;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ko),
+                                             (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vtile + vo),
+                                             (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
         }
     };
     // V^T operand through gfx950's transposed LDS read (ds_read_b64_tr_b16): in each
     // 16-lane group, lane i receives element i % 4 of the 8-byte pieces addressed by
     // lanes 4k + i / 4, k = 0..3. Lane (col, grp) addresses key row key0 + col / 4, d
     // columns dbase + 4 * (col % 4) .. + 3, and so receives V[key0 + k][dbase + col].
-    const int vrd = (col >> 2) * VR + 4 * (col & 3);
     auto vt_read = [&](const uint16_t* vtile, int key0, int dbase) -> attn_u2 {
         typedef short s4 __attribute__((ext_vector_type(4)));
-        const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s4*)(vtile + key0 * VR + dbase + vrd));
+        const int row = key0 + (col >> 2);
+        const int chunk = (dbase >> 3) + ((col & 3) >> 1);
+        const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(
+            vtile + row * D + (chunk ^ vswz(row)) * 8 + (col & 1) * 4));
         return __builtin_bit_cast(attn_u2, r);
     };
 
@@ -245,107 +252,133 @@ k_attention_fwd(const AttnArgs a) {
         if (CAUSAL) kend = min(a.Sk, max(0, qblk * kAttnBM + kAttnBM - 1 + off + 1));
         const int nblk = (kend + BN - 1) / BN;
 
-        // One barrier per block: after it, every wave has read tile blk and tile blk+1
-        // is in LDS; the loads of tile blk+1 are in flight while tile blk is computed.
-        if (nblk > 0) {
-            fetch(0);
-            stage(0);
-        }
-        __syncthreads();
-        for (int blk = 0; blk < nblk; ++blk) {
-            const int kb = blk * BN;
-            const uint16_t* kcur = ks + (blk & 1) * (BN * KS);
-            const uint16_t* vcur = vs + (blk & 1) * (BN * VR);
-            if (blk + 1 < nblk) fetch(kb + BN);
+        // One key block of this wave: S^T, online softmax, O^T (kcur, vcur: the tiles).
+        auto compute = [&](const uint16_t* kcur, const uint16_t* vcur, int kb) {
             // skipped when every key of the block lies past every query's diagonal for this wave
-            if (!(CAUSAL && kb > q0 + 31 + off)) {
-                // S^T tiles: t = key subtile (16 keys), u = query subtile
-                attn_f4 s[4][2];
+            if (CAUSAL && kb > q0 + 31 + off) return;
+            // S^T tiles: t = key subtile (16 keys), u = query subtile
+            attn_f4 s[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) s[t][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int row = t * 16 + col;
+                    const attn_u4 ka = *reinterpret_cast<const attn_u4*>(
+                        &kcur[row * D + ((kk * 4 + grp) ^ kswz(row)) * 8]);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
+                }
+            }
+
+            // Blocks cut by the end of the keys or by a diagonal of this wave's queries
+            // are scaled and masked element by element (cc = 1 then); all others keep the
+            // raw products and fold the scale into the exponent's FMA.
+            const bool need_mask = (kb + BN > a.Sk) || (CAUSAL && kb + BN - 1 > q0 + off);
+            const float cc = need_mask ? 1.f : c;
+            if (need_mask) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    // key kb + grp*4 + (t*16 + i) is visible iff t*16 + i <= lim
+                    int lim = a.Sk - 1;
+                    if (CAUSAL) lim = min(lim, q0 + u * 16 + col + off);
+                    lim -= kb + grp * 4;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i] * c;
+                }
+            }
+            // Both subtiles' statistics first (trees, not chains), then one rescale
+            // branch for the two, then the exponentials of both in one stretch of code.
+            float bmax[2];
+            bool grow[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float q4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    q4[t] = __builtin_fmaxf(__builtin_fmaxf(s[t][u][0], s[t][u][1]),
+                                            __builtin_fmaxf(s[t][u][2], s[t][u][3]));
+                bmax[u] = __builtin_fmaxf(__builtin_fmaxf(q4[0], q4[1]), __builtin_fmaxf(q4[2], q4[3]));
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                bmax[u] = attn_xgroup(bmax[u], true) * cc;  // scaled (c >= 0 keeps the order)
+                grow[u] = bmax[u] > m[u] + kAttnLazy;
+            }
+            if (__any(grow[0] || grow[1])) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const float mn = grow[u] ? bmax[u] : m[u];
+                    const float sn = (mn == -kInf) ? 0.f : mn;
+                    const float alpha = __builtin_amdgcn_exp2f(m[u] - sn);  // m = -inf -> 0
+                    m[u] = mn;
+                    ms[u] = sn;
+                    l[u] *= alpha;
+#pragma unroll
+                    for (int d = 0; d < DSUB; ++d) oacc[d][u] *= alpha;
+                }
+            }
+            attn_u4 pb[2][2];  // P as the B operand: [u][32-key step]
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float p[4][4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) s[t][u] = attn_f4{0.f, 0.f, 0.f, 0.f};
+                    for (int i = 0; i < 4; ++i)
+                        p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][u][i], cc, -ms[u]));
+                float ps[4];
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const attn_u4 ka = *reinterpret_cast<const attn_u4*>(&kcur[(t * 16 + col) * KS + kk * 32 + grp * 8]);
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
-                    }
-                }
-
-                // Blocks cut by the end of the keys or by a diagonal of this wave's queries
-                // are scaled and masked element by element (cc = 1 then); all others keep the
-                // raw products and fold the scale into the exponent's FMA.
-                const bool need_mask = (kb + BN > a.Sk) || (CAUSAL && kb + BN - 1 > q0 + off);
-                const float cc = need_mask ? 1.f : c;
-                attn_u4 pb[2][2];  // P as the B operand: [u][32-key step]
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    if (need_mask) {
-                        // key kb + grp*4 + (t*16 + i) is visible iff t*16 + i <= lim
-                        int lim = a.Sk - 1;
-                        if (CAUSAL) lim = min(lim, q0 + u * 16 + col + off);
-                        lim -= kb + grp * 4;
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i] * c;
-                    }
-                    float bmax = -kInf;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) bmax = __builtin_fmaxf(bmax, s[t][u][i]);
-                    bmax = attn_xgroup(bmax, true);
-                    bmax *= cc;  // scaled (c >= 0 keeps the order)
-                    const bool grow = bmax > m[u] + kAttnLazy;
-                    if (__any(grow)) {
-                        const float mn = grow ? bmax : m[u];
-                        const float sn = (mn == -kInf) ? 0.f : mn;
-                        const float alpha = __builtin_amdgcn_exp2f(m[u] - sn);  // m = -inf -> 0
-                        m[u] = mn;
-                        ms[u] = sn;
-                        l[u] *= alpha;
-#pragma unroll
-                        for (int d = 0; d < DSUB; ++d) oacc[d][u] *= alpha;
-                    }
-                    float p[4][4];
-                    float psum = 0.f;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][u][i], cc, -ms[u]));
-                            psum += p[t][i];
-                        }
-                    l[u] += psum;
-#pragma unroll
-                    for (int cs = 0; cs < 2; ++cs) {
-                        // 32-key step cs: slots 0..3 <- subtile 2cs, slots 4..7 <- subtile 2cs+1
-                        const int t0 = 2 * cs, t1 = 2 * cs + 1;
-                        pb[u][cs] = attn_u4{attn_pack2<DT>(p[t0][0], p[t0][1]), attn_pack2<DT>(p[t0][2], p[t0][3]),
-                                            attn_pack2<DT>(p[t1][0], p[t1][1]), attn_pack2<DT>(p[t1][2], p[t1][3])};
-                    }
-                }
-
-                // O^T += V^T P^T: A = V^T rows d, keys in the same slot order as P
+                for (int t = 0; t < 4; ++t) ps[t] = (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
+                l[u] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
                 for (int cs = 0; cs < 2; ++cs) {
-#pragma unroll
-                    for (int d = 0; d < DSUB; ++d) {
-                        const attn_u2 lo = vt_read(vcur, (2 * cs) * 16 + grp * 4, d * 16);
-                        const attn_u2 hi = vt_read(vcur, (2 * cs + 1) * 16 + grp * 4, d * 16);
-                        const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);
-                    }
+                    // 32-key step cs: slots 0..3 <- subtile 2cs, slots 4..7 <- subtile 2cs+1
+                    const int t0 = 2 * cs, t1 = 2 * cs + 1;
+                    pb[u][cs] = attn_u4{attn_pack2<DT>(p[t0][0], p[t0][1]), attn_pack2<DT>(p[t0][2], p[t0][3]),
+                                        attn_pack2<DT>(p[t1][0], p[t1][1]), attn_pack2<DT>(p[t1][2], p[t1][3])};
                 }
             }
-            if (blk + 1 < nblk) stage((blk + 1) & 1);
+
+            // O^T += V^T P^T: A = V^T rows d, keys in the same slot order as P
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+#pragma unroll
+                for (int d = 0; d < DSUB; ++d) {
+                    const attn_u2 lo = vt_read(vcur, (2 * cs) * 16 + grp * 4, d * 16);
+                    const attn_u2 hi = vt_read(vcur, (2 * cs + 1) * 16 + grp * 4, d * 16);
+                    const attn_u4 va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);
+                }
+            }
+        
+        };
+
+        // One barrier per block: after it, every wave has read tile blk and tile blk+1
+        // is in LDS; the loads of tile blk+1 are in flight while tile blk is computed.
+        // Unrolled by two so that each block names its LDS buffers at compile time.
+        if (nblk > 0) issue(0, ks0, vs0);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        for (int blk = 0; blk < nblk; blk += 2) {
+            const int kb = blk * BN;
+            if (blk + 1 < nblk) issue(kb + BN, ks1, vs1);
+            compute(ks0, vs0, kb);
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's loads of the next tile are in LDS
             __syncthreads();
+            if (blk + 1 < nblk) {
+                if (blk + 2 < nblk) issue(kb + 2 * BN, ks0, vs0);
+                compute(ks1, vs1, kb + BN);
+                __builtin_amdgcn_s_waitcnt(kVmcnt0);
+                __syncthreads();
+            }
         }
 
         // finish: the full row sum over the 4 lane groups, normalise, store

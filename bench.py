@@ -299,6 +299,7 @@ def main(argv=None) -> int:
     cold = stats_us(ev.samples_ms(torch))
     ev.close()
     log(f"[bench] timed {args.steps} cold steps in {wall:.3f} s wall (flush sweeps included)")
+    state = {"after_softmax_cold_lane": gpu_state()}
 
     # ---------------------------------------------------------------- warm lane (diagnostic)
     warm = None
@@ -350,11 +351,12 @@ def main(argv=None) -> int:
     attn = None
     if not args.no_attention:
         attn = bench_attention(torch, sm, s_handle, args.steps, args.warmup, log)
+        state["after_attention"] = gpu_state()
 
     # ---------------------------------------------------------------- sweep (stderr)
     if args.sweep:
         sweep(torch, sm, workloads, flush, s_handle, log, args)
-        sweep_attention(torch, sm, s_handle, log, max(10, args.steps // 10))
+        sweep_attention(torch, sm, s_handle, log, max(20, args.steps // 10))
 
     # ---------------------------------------------------------------- CPU baseline
     cpu, parity = None, {"passed": None, "note": "oracle leg skipped (--no-cpu-baseline)"}
@@ -397,6 +399,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "backward": bwd,
         "attention": attn,
+        "gpu_state": state,
     }
     print(json.dumps(result), flush=True)
     return 0 if parity.get("passed") is not False else 1
@@ -673,12 +676,12 @@ def score_grid(data: dict) -> dict:
 def sweep(torch, sm, workloads, flush, s_handle, log, args):
     """Cold timing of every workload under every plan that can take it (softmax forward
     and backward), then the residual RMSNorm shapes."""
-    sweep_rmsnorm(torch, sm, flush, s_handle, log, max(20, args.steps // 4))
+    sweep_rmsnorm(torch, sm, flush, s_handle, log, max(100, args.steps // 2))
     names = ["normal_f32_128x781", "normal_bf16_4096x4096",
              *[f"spiky_f16_8192x{n}" for n in workloads.SPIKE_WIDTHS],
              "offset_bf16_64x131072", "causal_bf16_524288x2048"]
     plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
-    steps = max(20, args.steps // 4)
+    steps = max(100, args.steps // 2)  # at least 100 timed samples per (workload, plan)
     for name in names:
         x = workloads.generate(name).to("cuda")
         # the GPU idled while the input was built on the host: bring the clocks back up
@@ -840,6 +843,37 @@ def bench_backward(torch, sm, workloads, y, flush, s_handle, steps, warmup, log)
     if not info["max_abs_row_sum"] < 0.05:
         raise RuntimeError(f"backward rows do not sum to about 0: {info['max_abs_row_sum']}")
     return res
+
+
+def gpu_state() -> dict | None:
+    """Clock, power and temperature of GPU 0 from `amd-smi metric` (a child process;
+    None where the tool is missing or fails): the mean and range of the XCDs' current
+    graphics clocks, socket power, hotspot and memory temperature."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "-t", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"] if isinstance(d, dict) else d
+        g = g[0] if isinstance(g, list) else g
+
+        def val(x):
+            return x.get("value") if isinstance(x, dict) else None
+
+        clocks = [val(v.get("clk")) for k, v in g.get("clock", {}).items()
+                  if k.startswith("gfx") and isinstance(v, dict)]
+        clocks = [c for c in clocks if isinstance(c, (int, float))]
+        mem = [val(v.get("clk")) for k, v in g.get("clock", {}).items()
+               if k.startswith("mem") and isinstance(v, dict)]
+        return {"gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
+                "gfx_clk_mhz_min": min(clocks) if clocks else None,
+                "gfx_clk_mhz_max": max(clocks) if clocks else None,
+                "mem_clk_mhz": mem[0] if mem else None,
+                "socket_power_w": val(g.get("power", {}).get("socket_power")),
+                "hotspot_c": val(g.get("temperature", {}).get("hotspot")),
+                "mem_temp_c": val(g.get("temperature", {}).get("mem"))}
+    except Exception:  # the snapshot is a diagnostic: never fail the bench for it
+        return None
 
 
 def attention_pairs(Sq: int, Sk: int, causal: bool) -> int:

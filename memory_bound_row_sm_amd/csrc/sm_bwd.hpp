@@ -136,42 +136,69 @@ __device__ __forceinline__ void store_dx(const float (&fy)[NV][Elem<DT>::per_vec
     }
 }
 
-// Raw (still encoded) windows of dy for the windows of y: 16-byte loads when dy
-// shares y's 16-byte phase, element loads packed into words otherwise. Windows
-// from nwin on and columns outside [0, N) read as 0.
+// Raw (encoded) words of a second operand on the row's window grid: 16-byte loads when
+// it shares the row's 16-byte phase. Otherwise the bytes of window w (columns c0 ..
+// c0 + E - 1, c0 = w*E - head) start sb bytes into an aligned 16-byte window, with
+// sb = (operand address - head*ES) mod 16 the same for every window of the row: they are
+// taken from the two aligned windows around them with a byte funnel shift
+// (v_alignbyte_b32), and an aligned window is loaded only where it holds a byte of the
+// operand's row [src, src + N*ES). Windows from wend on read as 0; columns outside
+// [0, N) hold whatever the loaded windows hold there (callers zero or ignore them).
 template <int DT, int NV, bool NT>
 __device__ __forceinline__ void load_dy_raw(uint32_t (&r)[NV][4], const unsigned char* dyrow,
-                                            int head, int N, int64_t w0, int wstep, int nwin,
+                                            int head, int N, int64_t w0, int wstep, int64_t wend,
                                             bool dy_phase) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
+    const uint32_t sb = (uint32_t)((reinterpret_cast<uintptr_t>(dyrow) - (uintptr_t)head * ES) & 15u);
+    const uint32_t q = sb >> 2, rb = sb & 3u;
+    const int64_t nbytes = (int64_t)N * ES;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int64_t w = w0 + (int64_t)wstep * v;
         if (dy_phase) {
             uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-            if (w < nwin) raw = load16<NT>(dyrow - (size_t)head * ES + 16 * (size_t)w);
+            if (w < wend) raw = load16<NT>(dyrow - (size_t)head * ES + 16 * (size_t)w);
             r[v][0] = raw.x;
             r[v][1] = raw.y;
             r[v][2] = raw.z;
             r[v][3] = raw.w;
         } else {
-            const int64_t c0 = w * E - head;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[v][i] = 0u;
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                const int64_t c = c0 + k;
-                if (w < nwin && c >= 0 && c < N) {
-                    const unsigned char* p = dyrow + (size_t)c * ES;
-                    if constexpr (DT == kF32) {
-                        r[v][k] = *reinterpret_cast<const uint32_t*>(p);
-                    } else {
-                        const uint32_t h = *reinterpret_cast<const uint16_t*>(p);
-                        r[v][k >> 1] |= (k & 1) ? (h << 16) : h;
-                    }
-                }
+            uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = make_uint4(0u, 0u, 0u, 0u);
+            if (w < wend) {
+                // byte offset from dyrow of the aligned window holding column c0 (pointer
+                // arithmetic on dyrow keeps the loads global, not flat)
+                const int64_t lo_off = (w * E - head) * (int64_t)ES - (int64_t)sb;
+                if (lo_off < nbytes && lo_off + 16 > 0) lo = load16<NT>(dyrow + lo_off);
+                if (lo_off + 16 < nbytes && lo_off + 32 > 0) hi = load16<NT>(dyrow + lo_off + 16);
             }
+            // dword k of the 32 bytes (no local arrays: they would be placed in LDS)
+            auto dw = [&](int k) -> uint32_t {
+                const uint4& t = k < 4 ? lo : hi;
+                switch (k & 3) {
+                case 0: return t.x;
+                case 1: return t.y;
+                case 2: return t.z;
+                default: return t.w;
+                }
+            };
+            // dwords q .. q+4 (q = sb / 4 in 0..3), then the byte shift rb
+            uint32_t d0 = 0u, d1 = 0u, d2 = 0u, d3 = 0u, d4 = 0u;
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                const uint32_t a01 = (q & 1u) ? dw(j + 1) : dw(j);
+                const uint32_t a23 = (q & 1u) ? dw(j + 3) : dw(j + 2);
+                const uint32_t dj = (q & 2u) ? a23 : a01;
+                if (j == 0) d0 = dj;
+                if (j == 1) d1 = dj;
+                if (j == 2) d2 = dj;
+                if (j == 3) d3 = dj;
+                if (j == 4) d4 = dj;
+            }
+            r[v][0] = __builtin_amdgcn_alignbyte(d1, d0, rb);
+            r[v][1] = __builtin_amdgcn_alignbyte(d2, d1, rb);
+            r[v][2] = __builtin_amdgcn_alignbyte(d3, d2, rb);
+            r[v][3] = __builtin_amdgcn_alignbyte(d4, d3, rb);
         }
     }
 }

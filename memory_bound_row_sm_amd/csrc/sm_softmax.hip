@@ -228,11 +228,11 @@ bool split_geometry(int64_t M, int64_t nw, int V, int64_t cap_slots, int64_t fix
 // Automatic SPLIT shape, in order of preference:
 //   1. the smallest V >= vmin whose rows need at most kSplitMaxAutoSlices slices and
 //      whose slices of all rows fit in one round (most workgroups in flight);
-//   2. with rounds unavoidable, V = vround when rows need at most kSplitRoundSlices
-//      slices (shorter rounds than the widest slices at the same traffic);
+//   2. with rounds unavoidable, V = vround when rows need at most round_max slices
+//      (shorter rounds than the widest slices at the same traffic);
 //   3. the largest V that fits at all (fewest slices per row).
-// Softmax: vmin = 2, vround = 4. Residual RMSNorm (it holds x, the residual and the
-// weight in registers): vmin = 1, vround = 2.
+// Softmax: vmin = 2, vround = 4, round_max = 16. Residual RMSNorm (it holds x, the
+// residual and the weight in registers): vmin = 1, vround = 2, round_max = 8.
 // Returns 0 when no V fits. Measured on MI355X, cold BF16 (us, V = 1 / 2 / 4 / 8):
 // 1 x 1048576: 7.6 / 6.2 / 5.7 / 6.6; 8 x 262144: 5.8 / 5.4 / 5.6 / 6.9; 16 x 65536:
 // 4.6 / 4.5 / 5.1 / 6.4; 64 x 131072: - / 13.8 / 11.3 / 11.1. On the row-plan grid
@@ -241,9 +241,13 @@ bool split_geometry(int64_t M, int64_t nw, int V, int64_t cap_slots, int64_t fix
 // from 262144 up.
 constexpr int64_t kSplitMaxAutoSlices = 128;
 constexpr int64_t kSplitRoundSlices = 16;
+// RMSNorm, refitted on its grid once phase-shifted weights load as aligned windows
+// (the 4-vector slices got faster there): mean regret 2.8% -> 0.6%
+constexpr int64_t kRmsRoundSlices = 8;
 
-int split_auto_v(int64_t M, int64_t nw, int vmin, int vmax, int vround, int64_t cus, void* ctx,
-                 int dtype, int bwd, int (*occ)(void*, int, int, int), int64_t& P, int64_t& grid) {
+int split_auto_v(int64_t M, int64_t nw, int vmin, int vmax, int vround, int64_t round_max,
+                 int64_t cus, void* ctx, int dtype, int bwd, int (*occ)(void*, int, int, int),
+                 int64_t& P, int64_t& grid) {
     int64_t cp[4] = {0, 0, 0, 0}, cg[4] = {0, 0, 0, 0};
     bool ok[4] = {false, false, false, false};
     int vs[4] = {0, 0, 0, 0}, n = 0;
@@ -260,7 +264,7 @@ int split_auto_v(int64_t M, int64_t nw, int vmin, int vmax, int vround, int64_t 
         }
     }
     for (int i = 0; i < n; ++i) {  // 2
-        if (ok[i] && vs[i] == vround && cp[i] <= kSplitRoundSlices) {
+        if (ok[i] && vs[i] == vround && cp[i] <= round_max) {
             P = cp[i];
             grid = cg[i];
             return vround;
@@ -300,7 +304,8 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
             const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
             if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
         } else {
-            V = split_auto_v(p.M, nw_max, 2, 8, 4, dev.cus, dev.ctx, p.dtype, 0, dev.occ_split, P, grid);
+            V = split_auto_v(p.M, nw_max, 2, 8, 4, kSplitRoundSlices, dev.cus, dev.ctx, p.dtype, 0,
+                             dev.occ_split, P, grid);
             if (V && o.grid > 0) {
                 const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
                 if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
@@ -685,7 +690,8 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
             const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 1)) * cus;
             if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
         } else {
-            V = split_auto_v(p.M, nw_max, 2, 4, 4, cus, nullptr, p.dtype, 1, occ_fn, P, grid);
+            V = split_auto_v(p.M, nw_max, 2, 4, 4, kSplitRoundSlices, cus, nullptr, p.dtype, 1, occ_fn,
+                             P, grid);
             if (V && o.grid > 0) {
                 const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 1)) * cus;
                 if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
@@ -879,7 +885,7 @@ int validate_rms(const RmsProblem& p) {
     return SM_OK;
 }
 
-constexpr int64_t kRmsTwoLaunchSlices = 32;
+constexpr int64_t kRmsTwoLaunchSlices = 64;
 
 int occ_rms_live(int dtype, int G, int V) {
     RmsRowKernelFn fn = rms_row_kernel(dtype, G, V, 0);
@@ -917,7 +923,8 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
                 const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
                 fused = split_geometry(p.M, nw_max, V, slots, o.grid, P, grid);
             } else {
-                V = split_auto_v(p.M, nw_max, 1, 4, 2, cus, nullptr, p.dtype, 2, occ_fn, P, grid);
+                V = split_auto_v(p.M, nw_max, 1, 4, 2, kRmsRoundSlices, cus, nullptr, p.dtype, 2, occ_fn,
+                                 P, grid);
                 fused = V != 0;
                 // many slices per row and several rounds: two launches without waits
                 // measured faster (width 1048576, 8 to 1024 rows: 6 to 15%)

@@ -111,15 +111,30 @@ def test_repeatable_and_torch_fp32():
     assert float((a.float().cpu() - want).abs().max()) < 2e-2
 
 
-def test_attention_workload_full_size_sampled():
-    """8 x 32 heads, 2048 queries and keys, d = 128, causal, BF16: q, k as in the
+def test_no_keys_and_no_queries():
+    """Sk = 0: every query sees no key (zeros, lse = -inf); Sq = 0: nothing to do."""
+    q = torch.randn(3, 70, 64).to(torch.bfloat16)
+    k = torch.empty(3, 0, 64, dtype=torch.bfloat16)
+    for causal in (False, True):
+        o, ls = run(q, k, k.clone(), causal, lse=True)
+        assert (o.float() == 0).all() and torch.isneginf(ls).all()
+    qe = torch.empty(2, 0, 128, device=DEV, dtype=torch.float16)
+    ke = torch.randn(2, 5, 128, device=DEV).half()
+    oe = torch.empty_like(qe)
+    sm.attention(qe, ke, ke, causal=True, out=oe)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_attention_workload_full_size_sampled(dt):
+    """8 x 32 heads, 2048 queries and keys, d = 128, causal: q, k as in the
     attention-logit workload (per-head seeded N(0,1)), v ~ N(0,1). Sampled rows against
     the oracle: the first, second and last query of every head and one random query."""
     B, H, S, d = 8, 32, 2048, 128
     g = torch.Generator().manual_seed(2026)
-    q = torch.randn(B * H, S, d, generator=g).to(torch.bfloat16)
-    k = torch.randn(B * H, S, d, generator=g).to(torch.bfloat16)
-    v = torch.randn(B * H, S, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(B * H, S, d, generator=g).to(TDT[dt])
+    k = torch.randn(B * H, S, d, generator=g).to(TDT[dt])
+    v = torch.randn(B * H, S, d, generator=g).to(TDT[dt])
     o, ls = run(q, k, v, True, lse=True)
     rng = np.random.default_rng(7)
     rows = set()
@@ -128,7 +143,7 @@ def test_attention_workload_full_size_sampled():
     rows = np.array(sorted(rows), dtype=np.int64)
     sel = torch.from_numpy(rows)
     st = compare_attn(o.view(-1, d).cpu()[sel], q, k, v, 1.0 / math.sqrt(d), True, rows=rows,
-                      lse_gpu=ls.cpu()[sel], what="attention workload sampled")
-    log(f"[attn] workload sampled {rows.size} rows: {st}")
+                      lse_gpu=ls.cpu()[sel], what=f"attention workload sampled {dt}")
+    log(f"[attn] workload sampled {dt} {rows.size} rows: {st}")
     # the first query of every head sees only key 0: o = v_0 rounded
     assert torch.equal(o[:, 0].cpu().view(torch.int16), v[:, 0].view(torch.int16))

@@ -273,6 +273,18 @@ k_attention_fwd(const AttnArgs a) {
                     for (int u = 0; u < 2; ++u) s[t][u] = mfma16<DT>(ka, qb[u][kk], s[t][u]);
                 }
             }
+            if constexpr (D == 128) {
+                // d = 128: 4 K fragment reads issued ahead of the MFMAs that use them,
+                // then one read per MFMA pair (measured 3% faster; d = 64 was faster
+                // with the compiler's own order)
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+                for (int i = 0; i < KK * 4 - 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
 
             // Blocks cut by the end of the keys or by a diagonal of this wave's queries
             // are scaled and masked element by element (cc = 1 then); all others keep the
@@ -357,6 +369,16 @@ k_attention_fwd(const AttnArgs a) {
 #pragma unroll
                     for (int u = 0; u < 2; ++u) oacc[d][u] = mfma16<DT>(va, pb[u][cs], oacc[d][u]);
                 }
+            }
+            if constexpr (D == 128) {
+                // transposed V reads (2 per MFMA pair): 8 ahead, then 2 per MFMA pair
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+                for (int i = 0; i < 2 * DSUB - 4; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
             }
         
         };

@@ -221,3 +221,113 @@ def test_backward_wide_row_shape_auto():
     st = compare_bwd(dx, y.cpu(), dy, what="bwd 64x131072 split")
     log(f"[split] backward wide rows: {st}")
     assert sm.sync_failures() == before
+
+
+def _each_plan(call, what):
+    """Run ``call(plan)`` for the automatic plan, SPLIT and WIDE; a forced SPLIT may
+    refuse rows whose slices cannot all be resident (SM_ERR_PLAN), nothing else.
+    Returns the plans that ran."""
+    ran = []
+    for plan in (sm.SM_PLAN_AUTO, SPLIT, sm.SM_PLAN_WIDE):
+        try:
+            call(plan)
+        except sm.SoftmaxError as e:
+            assert plan == SPLIT and e.status == -7, (what, plan, e)
+            continue
+        ran.append(plan)
+    assert sm.SM_PLAN_AUTO in ran and sm.SM_PLAN_WIDE in ran
+    return ran
+
+
+def _split_limit(query, lo, hi):
+    """Largest row width N in [lo, hi) at which ``query(N)`` (a forced-SPLIT plan query
+    for 2 BF16 rows, True when it succeeds) holds, by bisection; the query's success is
+    monotone in N because every vector width needs more slices per row as N grows. The
+    limit comes from the live occupancy of the SPLIT kernels on this device."""
+    assert query(lo) and not query(hi)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if query(mid):
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def _fwd_split_fits(ptr):
+    def q(N):
+        rc, _ = sm.sm_softmax_plan_query(ptr, ptr, 2, N, N, N, sm.SM_BF16, {"plan": SPLIT})
+        assert rc in (0, -7), rc
+        return rc == 0
+    return q
+
+
+def _bwd_split_fits(ptr):
+    def q(N):
+        rc, _ = sm.sm_softmax_bwd_plan_query(ptr, ptr, ptr, 2, N, N, N, N, sm.SM_BF16,
+                                             {"plan": SPLIT})
+        assert rc in (0, -7), rc
+        return rc == 0
+    return q
+
+
+def _widest_forward(N, split_expected):
+    x = _rand(2, N, "bf16", seed=N % 997)
+    xd = x.to(DEV)
+    info = sm.plan_for(xd)
+    log(f"[split] widest forward N={N}: auto plan {info['plan_name']} P={info['waves_per_row']}")
+
+    def call(plan):
+        out = torch.full_like(xd, float("nan"))
+        sm.softmax(xd, out=out, opts={"plan": plan})
+        torch.cuda.synchronize()
+        compare(out, x, what=f"widest forward N={N} plan={plan}")
+        del out
+
+    ran = _each_plan(call, f"forward N={N}")
+    assert (SPLIT in ran) == split_expected, (N, ran)
+    assert info["plan_name"] == ("split" if split_expected else "wide")
+    assert sm.sync_failures() == 0
+
+
+def _widest_backward(N, split_expected):
+    y, dy = _bwd_inputs(2, N, "bf16", seed=N % 991)
+    yd, dyd = y.to(DEV), dy.to(DEV)
+    info = sm.plan_for_backward(yd, dyd)
+    log(f"[split] widest backward N={N}: auto plan {info['plan_name']} P={info['waves_per_row']}")
+
+    def call(plan):
+        dx = torch.full_like(yd, float("nan"))
+        sm.softmax_backward(yd, dyd, dx=dx, opts={"plan": plan})
+        torch.cuda.synchronize()
+        compare_bwd(dx, y, dy, what=f"widest backward N={N} plan={plan}")
+        del dx
+
+    ran = _each_plan(call, f"backward N={N}")
+    assert (SPLIT in ran) == split_expected, (N, ran)
+    assert info["plan_name"] == ("split" if split_expected else "wide")
+    assert sm.sync_failures() == 0
+
+
+def test_widest_rows_forward():
+    """The widest BF16 rows one launch of SPLIT can hold on this device (every slice of a
+    row resident at once, from the SPLIT kernels' live occupancy) and one element past
+    them, where the automatic plan falls back to the two-pass WIDE plan, plus a row of
+    2^24 + 12345 elements: the automatic plan and both forced plans against the oracle."""
+    buf = torch.empty(8, dtype=torch.bfloat16, device=DEV)
+    lim = _split_limit(_fwd_split_fits(buf.data_ptr()), 1 << 16, 1 << 26)
+    log(f"[split] forward SPLIT limit for 2 BF16 rows: N = {lim}")
+    _widest_forward(lim, True)
+    _widest_forward(lim + 1, False)
+    _widest_forward((1 << 24) + 12345, False)
+
+
+def test_widest_rows_backward():
+    """As the forward test, for the backward's SPLIT limit (two inputs per element, so
+    fewer vectors per lane)."""
+    buf = torch.empty(8, dtype=torch.bfloat16, device=DEV)
+    lim = _split_limit(_bwd_split_fits(buf.data_ptr()), 1 << 16, 1 << 26)
+    log(f"[split] backward SPLIT limit for 2 BF16 rows: N = {lim}")
+    _widest_backward(lim, True)
+    _widest_backward(lim + 1, False)
+    _widest_backward((1 << 23) + 7, False)

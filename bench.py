@@ -315,24 +315,27 @@ def main(argv=None) -> int:
     dst = torch.empty_like(src)
     src.fill_(1)
 
-    def copy(grid, events=(None, None)):
-        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), grid, s_handle, *events)
+    def copy(grid, scope, events=(None, None)):
+        rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), grid, scope, s_handle,
+                              *events)
         if rc != 0:
             raise sm.SoftmaxError(rc, "sm_bench_copy")
 
-    copy_cold, copy_grid = None, None
-    for grid in (512, 1024, 2048):  # the ceiling is the best of a few launch shapes
-        for _ in range(args.warmup):
-            flush()
-            copy(grid)
-        ev = DispatchEvents(args.steps)
-        for _ in range(args.steps):
-            flush()
-            copy(grid, ev.next_pair())
-        st = stats_us(ev.samples_ms(torch))
-        ev.close()
-        if copy_cold is None or st["mean_us"] < copy_cold["mean_us"]:
-            copy_cold, copy_grid = st, grid
+    # the ceiling is the best of a few launch shapes under either store policy
+    copy_cold, copy_grid, copy_scope = None, None, None
+    for scope in (0, 1):
+        for grid in (512, 1024, 2048):
+            for _ in range(args.warmup):
+                flush()
+                copy(grid, scope)
+            ev = DispatchEvents(args.steps)
+            for _ in range(args.steps):
+                flush()
+                copy(grid, scope, ev.next_pair())
+            st = stats_us(ev.samples_ms(torch))
+            ev.close()
+            if copy_cold is None or st["mean_us"] < copy_cold["mean_us"]:
+                copy_cold, copy_grid, copy_scope = st, grid, scope
     del src, dst
 
     gbps = model_bytes / (cold["mean_us"] * 1e-6) / 1e9
@@ -391,6 +394,7 @@ def main(argv=None) -> int:
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "copy_ceiling_us": round(copy_cold["mean_us"], 3),
         "copy_ceiling_grid": copy_grid,
+        "copy_ceiling_stores": "device_scope" if copy_scope else "plain",
         "frac_of_copy_ceiling": round(gbps / copy_gbps, 4),
         "timed_region_wall_s": round(wall, 4),
         "parity": parity,
@@ -452,13 +456,14 @@ def record_traffic(fetch_csv: str, write_csv: str) -> dict:
     moves a known number of bytes; its counts give the scale of each counter."""
     f, w = summarize_counters(fetch_csv), summarize_counters(write_csv)
     soft = [k for k in f if "k_softmax_rows" in k]
-    if len(soft) != 1 or "smx::k_copy16" not in f:
+    cp = "smx::k_copy16<false>"  # plain stores: the calibration copy
+    if len(soft) != 1 or cp not in f or cp not in w:
         raise RuntimeError(f"expected one softmax row kernel and the copy kernel, found {sorted(f)}")
     k = soft[0]
     M, N, es = 4096, 4096, 2
     copy_bytes = M * N * es  # the copy moves the model's bytes: half read, half written
-    ff = (copy_bytes / 1024) / f["smx::k_copy16"]["FETCH_SIZE"]
-    wf = (copy_bytes / 1024) / w["smx::k_copy16"]["WRITE_SIZE"]
+    ff = (copy_bytes / 1024) / f[cp]["FETCH_SIZE"]
+    wf = (copy_bytes / 1024) / w[cp]["WRITE_SIZE"]
     fetch = f[k]["FETCH_SIZE"] * ff * 1024
     write = w[k]["WRITE_SIZE"] * wf * 1024
     alg = byte_model(M, N, es)
@@ -466,10 +471,10 @@ def record_traffic(fetch_csv: str, write_csv: str) -> dict:
            "algorithmic_bytes_per_launch": alg,
            "fetch_size_kib_raw": f[k]["FETCH_SIZE"], "write_size_kib_raw": w[k]["WRITE_SIZE"],
            "dispatches": {"fetch": f[k]["dispatches"], "write": w[k]["dispatches"]},
-           "calibration": {"copy_kernel": f"smx::k_copy16 moving {copy_bytes >> 20} MiB in and "
+           "calibration": {"copy_kernel": f"{cp} moving {copy_bytes >> 20} MiB in and "
                                           f"{copy_bytes >> 20} MiB out",
-                           "copy_fetch_size_kib_raw": f["smx::k_copy16"]["FETCH_SIZE"],
-                           "copy_write_size_kib_raw": w["smx::k_copy16"]["WRITE_SIZE"],
+                           "copy_fetch_size_kib_raw": f[cp]["FETCH_SIZE"],
+                           "copy_write_size_kib_raw": w[cp]["WRITE_SIZE"],
                            "fetch_factor": round(ff, 5), "write_factor": round(wf, 5)},
            "hbm_fetch_bytes_per_launch": int(round(fetch)),
            "hbm_write_bytes_per_launch": int(round(write)),

@@ -28,13 +28,16 @@ extern "C" {
  *   bytes    : a multiple of 16
  *   grid     : workgroups of 256 threads (0 = 8 per CU); each thread moves
  *              16 bytes per step of a grid-stride loop
+ *   store_scope : 0 = plain stores (written back from L2 when the dispatch
+ *              ends); 1 = device-scope stores, which write through each XCD's
+ *              L2 (the policy of the library's row kernels)
  *   start_event, stop_event : optional (NULL) events attached to the kernel
  *              dispatch, as in sm_softmax_opts
  * Returns SM_OK (0) or a negative sm_status (SM_ERR_INVALID for bad
- * alignment or size, SM_ERR_HIP for a failed launch).
+ * alignment, size or store_scope, SM_ERR_HIP for a failed launch).
  */
-int sm_bench_copy(const void *src, void *dst, size_t bytes, int grid, hipStream_t stream,
-                  hipEvent_t start_event, hipEvent_t stop_event);
+int sm_bench_copy(const void *src, void *dst, size_t bytes, int grid, int store_scope,
+                  hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event);
 
 /*
  * Read every 16-byte word of `buf` and write nothing, so that afterwards the L2

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SM_SOFTMAX_VERSION 10000 /* 1.0.0 */
+#define SM_SOFTMAX_VERSION 10100 /* 1.1.0 */
 
 typedef enum sm_dtype { SM_F32 = 0, SM_F16 = 1, SM_BF16 = 2 } sm_dtype;
 

@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsm_softmax.so")
+ABI_VERSION = 10100  # SM_SOFTMAX_VERSION of the signatures declared below
 
 
 class SmOpts(ctypes.Structure):
@@ -122,7 +123,7 @@ def lib() -> ctypes.CDLL:
         L.sm_softmax_version.argtypes = []
         L.sm_softmax_last_hip_error.argtypes = []
         L.sm_softmax_sync_failures.argtypes = [vp, ctypes.POINTER(ctypes.c_uint)]
-        L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, vp, vp, vp]
+        L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, ci, vp, vp, vp]
         L.sm_bench_flush.argtypes = [vp, ctypes.c_size_t, vp]
         for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
                   L.sm_softmax_bwd, L.sm_softmax_bwd_ex, L.sm_softmax_bwd_plan_query,
@@ -130,6 +131,10 @@ def lib() -> ctypes.CDLL:
                   L.sm_rmsnorm_fwd, L.sm_rmsnorm_fwd_ex, L.sm_rmsnorm_plan_query,
                   L.sm_attention_fwd, L.sm_attention_fwd_ex, L.sm_bench_copy, L.sm_bench_flush):
             f.restype = ci
+        if L.sm_softmax_version() != ABI_VERSION:
+            raise RuntimeError(
+                f"{lib_path} reports version {L.sm_softmax_version()}, the binding expects "
+                f"{ABI_VERSION}: rebuild with `python -c 'import __graft_entry__ as g; g.build()'`")
         _lib = L
     return _lib
 
@@ -265,9 +270,9 @@ def sm_softmax_sync_failures(stream: int = 0) -> tuple[int, int]:
     return rc, c.value
 
 
-def sm_bench_copy(src: int, dst: int, nbytes: int, grid: int = 0, stream: int = 0,
-                  start_event=None, stop_event=None) -> int:
-    return lib().sm_bench_copy(src, dst, nbytes, grid, stream, start_event, stop_event)
+def sm_bench_copy(src: int, dst: int, nbytes: int, grid: int = 0, store_scope: int = 0,
+                  stream: int = 0, start_event=None, stop_event=None) -> int:
+    return lib().sm_bench_copy(src, dst, nbytes, grid, store_scope, stream, start_event, stop_event)
 
 
 def sm_bench_flush(buf: int, nbytes: int, stream: int = 0) -> int:

@@ -25,9 +25,16 @@ namespace smx {
 // ------------------------------------------------------------ measurement kernels
 // 16-byte copy (bandwidth ceiling, counter calibration) and a read-only sweep
 // that evicts earlier data from L2 and MALL without leaving dirty lines behind.
+// SC1: device-scope stores, the row kernels' store policy; else plain stores.
+template <bool SC1>
 __global__ void __launch_bounds__(256) k_copy16(const uint4* src, uint4* dst, int64_t n) {
     const int64_t step = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) dst[i] = src[i];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
+        if constexpr (SC1)
+            store16(reinterpret_cast<unsigned char*>(dst + i), src[i]);
+        else
+            dst[i] = src[i];
+    }
 }
 
 __global__ void __launch_bounds__(256) k_sweep_read16(const uint4* buf, int64_t n) {
@@ -1354,10 +1361,10 @@ int sm_softmax_sync_failures(hipStream_t stream, unsigned int* count) {
     return SM_OK;
 }
 
-int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_t stream,
-                  hipEvent_t start_event, hipEvent_t stop_event) {
+int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, int store_scope,
+                  hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event) {
     if (!src || !dst || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) ||
-        (reinterpret_cast<uintptr_t>(dst) & 15))
+        (reinterpret_cast<uintptr_t>(dst) & 15) || (store_scope != 0 && store_scope != 1))
         return SM_ERR_INVALID;
     if (bytes == 0) return SM_OK;
     if (grid <= 0) {
@@ -1366,7 +1373,9 @@ int sm_bench_copy(const void* src, void* dst, size_t bytes, int grid, hipStream_
         if (rc != SM_OK) return rc;
         grid = 8 * dv.cus;
     }
-    hipError_t e = launch_k(reinterpret_cast<const void*>(&k_copy16), dim3(grid), dim3(256), stream,
+    const void* fn = store_scope ? reinterpret_cast<const void*>(&k_copy16<true>)
+                                 : reinterpret_cast<const void*>(&k_copy16<false>);
+    hipError_t e = launch_k(fn, dim3(grid), dim3(256), stream,
                             start_event, stop_event, reinterpret_cast<const uint4*>(src),
                             reinterpret_cast<uint4*>(dst), (int64_t)(bytes / 16));
     return e == hipSuccess ? SM_OK : hip_fail(e);

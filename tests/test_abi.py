@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert sm.sm_softmax_version() == 10000
+    assert sm.sm_softmax_version() == sm.ABI_VERSION == 10100
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert sm.sm_softmax_strerror(code) and sm.sm_softmax_strerror(code) != "unknown status"
     assert sm.sm_softmax_strerror(99) == "unknown status"

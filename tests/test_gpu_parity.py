@@ -343,10 +343,12 @@ def test_batched_views_through_python_binding():
 def test_bench_copy_and_flush():
     n = 1 << 22
     a = torch.randint(0, 1 << 30, (n // 4,), dtype=torch.int32, device=DEV)
-    b = torch.zeros_like(a)
-    assert sm.sm_bench_copy(a.data_ptr(), b.data_ptr(), n, 0, 0, None, None) == 0
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    for scope in (0, 1):  # plain and device-scope stores
+        b = torch.zeros_like(a)
+        assert sm.sm_bench_copy(a.data_ptr(), b.data_ptr(), n, 0, scope, 0, None, None) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+    assert sm.sm_bench_copy(a.data_ptr(), b.data_ptr(), n, 0, 2, 0, None, None) == -1  # bad scope
     assert sm.sm_bench_flush(b.data_ptr(), n, 0) == 0
     torch.cuda.synchronize()
     assert torch.equal(b, a)  # the sweep only reads

@@ -107,6 +107,14 @@ __device__ __forceinline__ uint32_t attn_pack2(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, e2));
 }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum; v_maximum3_f32 on gfx950). fmaxf
+// would make the compiler quiet every MFMA and permlane result first (a v_max_f32 x, x, x
+// per input: 28 of the 68 VALU instructions of a block's row maxima at d = 128). A NaN
+// score gives a NaN row either way (through its exponential and the row sum).
+__device__ __forceinline__ float attn_max(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
 // Max / sum over the 4 lane groups of a lane column (lanes l, l^16, l^32, l^48).
 // gfx950's v_permlane32_swap / v_permlane16_swap exchange lanes between two registers:
 // given two copies of x they return x and its partner lane l^32 / l^16 (position in the
@@ -118,7 +126,7 @@ __device__ __forceinline__ float attn_swap_op(float x, bool is_max, bool half32)
                           : __builtin_amdgcn_permlane16_swap(a, a, false, false);
     const uint32_t u0 = r[0], u1 = r[1];
     const float r0 = __builtin_bit_cast(float, u0), r1 = __builtin_bit_cast(float, u1);
-    return is_max ? __builtin_fmaxf(r0, r1) : r0 + r1;
+    return is_max ? attn_max(r0, r1) : r0 + r1;
 }
 __device__ __forceinline__ float attn_xgroup(float x, bool is_max) {
     return attn_swap_op(attn_swap_op(x, is_max, true), is_max, false);
@@ -314,9 +322,8 @@ k_attention_fwd(const AttnArgs a) {
                 float q4[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    q4[t] = __builtin_fmaxf(__builtin_fmaxf(s[t][u][0], s[t][u][1]),
-                                            __builtin_fmaxf(s[t][u][2], s[t][u][3]));
-                bmax[u] = __builtin_fmaxf(__builtin_fmaxf(q4[0], q4[1]), __builtin_fmaxf(q4[2], q4[3]));
+                    q4[t] = attn_max(attn_max(s[t][u][0], s[t][u][1]), attn_max(s[t][u][2], s[t][u][3]));
+                bmax[u] = attn_max(attn_max(q4[0], q4[1]), attn_max(q4[2], q4[3]));
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {

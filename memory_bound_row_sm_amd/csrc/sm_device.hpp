@@ -127,10 +127,13 @@ __device__ __forceinline__ void store_elem(unsigned char* p, const uint4 v, int 
 }
 
 // ------------------------------------------------------------ lane max
-// v_max3_f32 folds two elements per instruction.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
-}
+// Row maxima use the NaN-propagating maximum (IEEE 754-2019; v_maximum3_f32 on gfx950,
+// two elements per instruction). fmaxf would make the compiler quiet every input that
+// it cannot prove canonical first (decoded 16-bit values, DPP and LDS results): one
+// v_max_f32 x, x, x each. A NaN makes its row NaN either way (through its exponential
+// and the row sum).
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmax_nan(fmax_nan(a, b), c); }
 
 // ------------------------------------------------------------ DPP / swizzle
 template <int CTRL>
@@ -169,7 +172,7 @@ __device__ __forceinline__ float group_allreduce(float v, Op op) {
 }
 
 struct OpMax {
-    __device__ __forceinline__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmax_nan(a, b); }
 };
 struct OpAdd {
     __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
@@ -242,7 +245,7 @@ __device__ __forceinline__ CSum group_allreduce_csum(CSum c) {
 // evaluating exp(-inf - (-inf)) ("Measured optimization case studies", section
 // "Wide rows: loop in one program, or split across programs": the merge guard).
 __device__ __forceinline__ void merge_fast(float& m, float& s, float m2, float s2) {
-    const float mn = __builtin_fmaxf(m, m2);
+    const float mn = fmax_nan(m, m2);
     const float r = s * exp2_fast((m - mn) * kLog2e) + s2 * exp2_fast((m2 - mn) * kLog2e);
     s = (mn == kNegInf) ? s + s2 : r;
     m = mn;
@@ -250,7 +253,7 @@ __device__ __forceinline__ void merge_fast(float& m, float& s, float m2, float s
 
 // FP32-accurate merge: rescale factors from exp_diff_acc, compensated sums.
 __device__ __forceinline__ void merge_acc(float& m, CSum& s, float m2, CSum s2) {
-    const float mn = __builtin_fmaxf(m, m2);
+    const float mn = fmax_nan(m, m2);
     if (mn == kNegInf) {  // both parts fully masked: 0, or NaN if a NaN was seen
         s.hi = s.hi + s2.hi;
         s.lo = s.lo + s2.lo;

@@ -70,7 +70,7 @@ __device__ __forceinline__ float row_max(float m, float* lds) {
         __syncthreads();
         float r = lds[0];
 #pragma unroll
-        for (int w = 1; w < G / 64; ++w) r = __builtin_fmaxf(r, lds[w]);
+        for (int w = 1; w < G / 64; ++w) r = fmax_nan(r, lds[w]);
         return r;
     }
 }

@@ -155,7 +155,7 @@ k_attention_fwd(const AttnArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to M0 from SGPRs
     const int col = lane & 15;       // lane column: a query (S^T, O^T) or a key/d row (A ops)
     const int grp = lane >> 4;       // lane group 0..3
     const int off = a.Sk - a.Sq;     // causal: query i sees keys j <= i + off

@@ -295,10 +295,12 @@ k_attention_fwd(const AttnArgs a) {
             }
 
             // Blocks cut by the end of the keys or by a diagonal of this wave's queries
-            // are scaled and masked element by element (cc = 1 then); all others keep the
-            // raw products and fold the scale into the exponent's FMA.
+            // set their hidden scores to -inf; the scale stays folded into the
+            // exponent's FMA (-inf * c - m = -inf). With scale 0 the visible scores are
+            // set to 0 instead and the FMA scales by 1 (-inf * 0 would be NaN).
             const bool need_mask = (kb + BN > a.Sk) || (CAUSAL && kb + BN - 1 > q0 + off);
-            const float cc = need_mask ? 1.f : c;
+            const bool zero_scale = c == 0.f;
+            const float cc = (need_mask && zero_scale) ? 1.f : c;
             if (need_mask) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
@@ -306,11 +308,17 @@ k_attention_fwd(const AttnArgs a) {
                     int lim = a.Sk - 1;
                     if (CAUSAL) lim = min(lim, q0 + u * 16 + col + off);
                     lim -= kb + grp * 4;
+                    if (zero_scale) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                        for (int t = 0; t < 4; ++t)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i] * c;
+                            for (int i = 0; i < 4; ++i) s[t][u][i] = (t * 16 + i > lim) ? -kInf : 0.f;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s[t][u][i] = (t * 16 + i > lim) ? -kInf : s[t][u][i];
+                    }
                 }
             }
             // Both subtiles' statistics first (trees, not chains), then one rescale

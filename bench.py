@@ -278,6 +278,7 @@ def main(argv=None) -> int:
     # ---------------------------------------------------------------- clocks up
     # 200 ms of cache sweeps keep the GPU busy without calling the timed kernel, so
     # a profiler's per-kernel average covers only the calls below
+    sampler = GpuSampler().start(torch)  # through the burst and the cold lane
     t_end = time.perf_counter() + 0.2
     while time.perf_counter() < t_end:
         for _ in range(20):
@@ -296,10 +297,10 @@ def main(argv=None) -> int:
         call(ev.next_pair())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state = {"during_softmax_cold_lane": sampler.stop()}
     cold = stats_us(ev.samples_ms(torch))
     ev.close()
     log(f"[bench] timed {args.steps} cold steps in {wall:.3f} s wall (flush sweeps included)")
-    state = {"after_softmax_cold_lane": gpu_state()}
 
     # ---------------------------------------------------------------- warm lane (diagnostic)
     warm = None
@@ -353,8 +354,9 @@ def main(argv=None) -> int:
     # ---------------------------------------------------------------- attention forward
     attn = None
     if not args.no_attention:
+        sampler = GpuSampler().start(torch)
         attn = bench_attention(torch, sm, s_handle, args.steps, args.warmup, log)
-        state["after_attention"] = gpu_state()
+        state["during_attention"] = sampler.stop()
 
     # ---------------------------------------------------------------- sweep (stderr)
     if args.sweep:
@@ -850,35 +852,85 @@ def bench_backward(torch, sm, workloads, y, flush, s_handle, steps, warmup, log)
     return res
 
 
-def gpu_state() -> dict | None:
-    """Clock, power and temperature of GPU 0 from `amd-smi metric` (a child process;
-    None where the tool is missing or fails): the mean and range of the XCDs' current
-    graphics clocks, socket power, hotspot and memory temperature."""
-    import subprocess
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "-t", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)
-        g = d["gpu_data"] if isinstance(d, dict) else d
-        g = g[0] if isinstance(g, list) else g
+class GpuSampler:
+    """Clock, power and temperature of the GPU while a lane runs: a thread of this
+    process polls amdsmi's GPU metrics in-process (no child process) every `period`
+    seconds between start() and stop(). stop() returns the mean and range of the
+    XCDs' graphics clocks, the memory clock, socket power and the hottest readings, or
+    None where amdsmi is missing or fails: the readings are a diagnostic and never
+    fail the bench."""
+    _handle = None
 
-        def val(x):
-            return x.get("value") if isinstance(x, dict) else None
+    def __init__(self, period: float = 0.005):
+        self.period = period
+        self.samples = []
+        self._thread = None
+        self._stop = None
 
-        clocks = [val(v.get("clk")) for k, v in g.get("clock", {}).items()
-                  if k.startswith("gfx") and isinstance(v, dict)]
-        clocks = [c for c in clocks if isinstance(c, (int, float))]
-        mem = [val(v.get("clk")) for k, v in g.get("clock", {}).items()
-               if k.startswith("mem") and isinstance(v, dict)]
-        return {"gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
+    @classmethod
+    def _device(cls, torch):
+        if cls._handle is None:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            h = hs[0]
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for cand in hs:  # the handle of torch's device 0, by PCI bus, where known
+                try:
+                    if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(cand).split(":")[1], 16) == bus:
+                        h = cand
+                except Exception:
+                    pass
+            cls._handle = h
+        return cls._handle
+
+    def start(self, torch):
+        import threading
+        try:
+            import amdsmi
+            h = self._device(torch)
+        except Exception:
+            return self
+        self._stop = threading.Event()
+
+        def poll():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(amdsmi.amdsmi_get_gpu_metrics_info(h))
+                except Exception:
+                    pass
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=poll, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self) -> dict | None:
+        if self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        num = lambda x: x if isinstance(x, (int, float)) and 0 < x < 100000 else None
+        clocks = [c for m in self.samples for c in (m.get("current_gfxclks") or []) if num(c)]
+        power = [num(m.get("current_socket_power")) for m in self.samples]
+        power = [p for p in power if p]
+        hot = [num(m.get("temperature_hotspot")) for m in self.samples]
+        hot = [t for t in hot if t]
+        memt = [num(m.get("temperature_mem")) for m in self.samples]
+        memt = [t for t in memt if t]
+        uclk = [num(m.get("current_uclk")) for m in self.samples]
+        uclk = [u for u in uclk if u]
+        if not self.samples:
+            return None
+        return {"samples": len(self.samples),
+                "gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
                 "gfx_clk_mhz_min": min(clocks) if clocks else None,
                 "gfx_clk_mhz_max": max(clocks) if clocks else None,
-                "mem_clk_mhz": mem[0] if mem else None,
-                "socket_power_w": val(g.get("power", {}).get("socket_power")),
-                "hotspot_c": val(g.get("temperature", {}).get("hotspot")),
-                "mem_temp_c": val(g.get("temperature", {}).get("mem"))}
-    except Exception:  # the snapshot is a diagnostic: never fail the bench for it
-        return None
+                "mem_clk_mhz": max(uclk) if uclk else None,
+                "socket_power_w_mean": round(sum(power) / len(power), 1) if power else None,
+                "socket_power_w_max": max(power) if power else None,
+                "hotspot_c_max": max(hot) if hot else None,
+                "mem_temp_c_max": max(memt) if memt else None}
 
 
 def attention_pairs(Sq: int, Sk: int, causal: bool) -> int:

@@ -910,16 +910,20 @@ class GpuSampler:
             return None
         self._stop.set()
         self._thread.join()
-        num = lambda x: x if isinstance(x, (int, float)) and 0 < x < 100000 else None
-        clocks = [c for m in self.samples for c in (m.get("current_gfxclks") or []) if num(c)]
-        power = [num(m.get("current_socket_power")) for m in self.samples]
-        power = [p for p in power if p]
-        hot = [num(m.get("temperature_hotspot")) for m in self.samples]
-        hot = [t for t in hot if t]
-        memt = [num(m.get("temperature_mem")) for m in self.samples]
-        memt = [t for t in memt if t]
-        uclk = [num(m.get("current_uclk")) for m in self.samples]
-        uclk = [u for u in uclk if u]
+        # unavailable fields read "N/A" or an all-ones 16-bit value (65535): keep numbers
+        # in a plausible range only (MHz, W, degrees C)
+        def vals(key, hi, many=False):
+            out = []
+            for m in self.samples:
+                xs = (m.get(key) or []) if many else [m.get(key)]
+                out += [x for x in xs if isinstance(x, (int, float)) and 0 < x < hi]
+            return out
+
+        clocks = vals("current_gfxclks", 10000, many=True)
+        power = vals("current_socket_power", 10000)
+        hot = vals("temperature_hotspot", 200)
+        memt = vals("temperature_mem", 200)
+        uclk = vals("current_uclk", 10000)
         if not self.samples:
             return None
         return {"samples": len(self.samples),

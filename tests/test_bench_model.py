@@ -67,3 +67,23 @@ def test_attention_pair_count(Sq, Sk):
     assert bench.attention_pairs(Sq, Sk, False) == Sq * Sk
     if Sq == Sk:
         assert bench.attention_pairs(Sq, Sk, True) == Sq * (Sq + 1) // 2
+
+
+def test_gpu_sampler_is_a_diagnostic_only():
+    """The clock/power sampler returns None, not an error, when no device can be queried
+    (no GPU or no amdsmi here); with readings it summarises the per-XCD clocks and
+    ignores unavailable fields."""
+    import torch
+    s = bench.GpuSampler()
+    if not torch.cuda.is_available():
+        assert s.start(torch).stop() is None
+    fake = bench.GpuSampler()
+    fake._thread = type("T", (), {"join": lambda self: None})()
+    fake._stop = type("E", (), {"set": lambda self: None})()
+    fake.samples = [{"current_gfxclks": [2100, 2000, "N/A"], "current_socket_power": 900,
+                     "temperature_hotspot": 60, "temperature_mem": "N/A", "current_uclk": 2000},
+                    {"current_gfxclks": [2200, 65535], "current_socket_power": "N/A"}]
+    st = fake.stop()
+    assert st["samples"] == 2
+    assert (st["gfx_clk_mhz_min"], st["gfx_clk_mhz_max"], st["gfx_clk_mhz_mean"]) == (2000, 2200, 2100.0)
+    assert st["socket_power_w_max"] == 900 and st["hotspot_c_max"] == 60 and st["mem_temp_c_max"] is None

@@ -9,8 +9,10 @@ Protocol (the pages' methodology, restated):
     paragraph): output properties on the GPU first, then, in the CPU-baseline leg,
     the FP64 oracle's result on the same input compared element by element with
     the timed call's output (the run fails if they disagree);
-  * a 200 ms burst of calls to bring the clocks up ("Measured optimization case
-    studies", section "GPU clocks: the first calls after an idle pause");
+  * a burst of calls to bring the clocks up ("Measured optimization case studies",
+    section "GPU clocks: the first calls after an idle pause", which uses 200 ms; 1 s
+    here, so that the clock/power sampler also sees the SMU's metrics table refresh
+    under load);
   * W untimed cold steps, then K timed cold steps, each bracketed by its own pair
     of HIP events on the launch stream; median, p10, p90, MAD, min, max and mean
     are reported (Warpline README, the suite-protocol paragraph);
@@ -276,10 +278,11 @@ def main(argv=None) -> int:
             raise sm.SoftmaxError(rc, "sm_bench_flush")
 
     # ---------------------------------------------------------------- clocks up
-    # 200 ms of cache sweeps keep the GPU busy without calling the timed kernel, so
-    # a profiler's per-kernel average covers only the calls below
+    # 1 s of cache sweeps keep the GPU busy without calling the timed kernel, so a
+    # profiler's per-kernel average covers only the calls below, and long enough for the
+    # SMU's metrics table (refreshed every few hundred ms) to show the loaded clocks
     sampler = GpuSampler().start(torch)  # through the burst and the cold lane
-    t_end = time.perf_counter() + 0.2
+    t_end = time.perf_counter() + 1.0
     while time.perf_counter() < t_end:
         for _ in range(20):
             flush()
@@ -861,7 +864,7 @@ class GpuSampler:
     fail the bench."""
     _handle = None
 
-    def __init__(self, period: float = 0.005):
+    def __init__(self, period: float = 0.025):
         self.period = period
         self.samples = []
         self._thread = None
@@ -926,7 +929,8 @@ class GpuSampler:
         uclk = vals("current_uclk", 10000)
         if not self.samples:
             return None
-        return {"samples": len(self.samples),
+        distinct = len({tuple(m.get("current_gfxclks") or []) for m in self.samples})
+        return {"samples": len(self.samples), "distinct_readings": distinct,
                 "gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
                 "gfx_clk_mhz_min": min(clocks) if clocks else None,
                 "gfx_clk_mhz_max": max(clocks) if clocks else None,

@@ -147,3 +147,21 @@ def test_attention_workload_full_size_sampled(dt):
     log(f"[attn] workload sampled {dt} {rows.size} rows: {st}")
     # the first query of every head sees only key 0: o = v_0 rounded
     assert torch.equal(o[:, 0].cpu().view(torch.int16), v[:, 0].view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_maximum_grows_along_the_keys(causal):
+    """Keys scaled by 1 + 6 j / Sk, so most queries' running maximum passes the lazy margin
+    block after block; then one late key aligned with every query, whose score lies about
+    a hundred binades above the others (the accumulated O and l are rescaled by ~2^-100)."""
+    BH, S, d = 2, 700, 128
+    q, k, v = qkv(BH, S, S, d, "bf16", seed=31)
+    ramp = (1 + 6 * torch.arange(S, dtype=torch.float32) / S).view(1, S, 1)
+    k2 = (k.float() * ramp).to(torch.bfloat16)
+    o, ls = run(q, k2, v, causal, scale=0.3, lse=True)
+    compare_attn(o, q, k2, v, 0.3, causal, lse_gpu=ls, what=f"ramped keys causal={causal}")
+    q3, k3 = q.clone(), k.clone()
+    q3[:, :, 0] = 4.0
+    k3[:, S - 40, 0] = 60.0  # score +240 (x 0.3 scale: ~104 binades) for every query that sees it
+    o, ls = run(q3, k3, v, causal, scale=0.3, lse=True)
+    compare_attn(o, q3, k3, v, 0.3, causal, lse_gpu=ls, what=f"one dominant key causal={causal}")

@@ -195,3 +195,19 @@ def test_against_torch_rms_norm():
     assert torch.equal(s.cpu().view(torch.int16), st.view(torch.int16))
     want = torch.nn.functional.rms_norm(st.float(), (4096,), weight=w.float(), eps=1e-6)
     assert float((y.float().cpu() - want).abs().max()) <= 2 ** -7 * float(want.abs().max())
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_widest_rows_automatic_launch_count(M):
+    """Width 2^20 (FP16): one row fits one round of resident slices (one fused launch);
+    eight rows need several rounds of more than 64 slices each, where the automatic plan
+    takes the two-launch form (publish, then gather and apply) — both against the oracle,
+    with a residual and residual_out."""
+    N = 1 << 20
+    x, r, w = inputs(M, N, "f16", seed=M + 17)
+    info = sm.plan_for_rmsnorm(x.to(DEV), w.to(DEV), residual=r.to(DEV))
+    log(f"[rms] {M}x{N}: plan {info['plan_name']} launches {info['launches']} "
+        f"P={info['waves_per_row']} grid={info['grid']}")
+    assert info["launches"] == (2 if M == 8 else 1)
+    y, s = run(x, r, w, s_out=True)
+    compare_rms(y, x, r, w, 1e-6, s_gpu=s, what=f"widest {M}x{N}")

@@ -328,7 +328,7 @@ def main(argv=None) -> int:
     # the ceiling is the best of a few launch shapes under either store policy
     copy_cold, copy_grid, copy_scope = None, None, None
     for scope in (0, 1):
-        for grid in (512, 1024, 2048):
+        for grid in (512, 1024, 2048, 4096, 8192):  # 8192: one vector per thread at 32 MiB
             for _ in range(args.warmup):
                 flush()
                 copy(grid, scope)

@@ -186,6 +186,7 @@ def main(argv=None) -> int:
     ap.add_argument("--grid-runs", type=int, default=2, help="repeat runs of the plan grid")
     ap.add_argument("--grid-steps", type=int, default=10, help="timed cold calls per plan and cell")
     ap.add_argument("--grid-op", default="fwd", choices=["fwd", "bwd", "rms"])
+    ap.add_argument("--grid-dtype", default="bf16", choices=["bf16", "f16", "f32"])
     ap.add_argument("--score-grid", metavar="GRID_JSON",
                     help="print the regret summary of a plan-grid file and exit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -568,35 +569,37 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
 
     bwd = args.grid_op == "bwd"
     rms = args.grid_op == "rms"
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[args.grid_dtype]
+    code = {"bf16": sm.SM_BF16, "f16": sm.SM_F16, "f32": sm.SM_F32}[args.grid_dtype]
     runs = []
     for run in range(args.grid_runs):
         cells = []
         gen = torch.Generator(device="cuda").manual_seed(2026)
         for N in GRID_WIDTHS:
             for M in GRID_ROWS:
-                x = (torch.randn(M, N, device=dev, generator=gen) * 3).to(torch.bfloat16)
+                x = (torch.randn(M, N, device=dev, generator=gen) * 3).to(tdt)
                 out = torch.empty_like(x)
                 dy = w = None
                 if bwd:
                     sm.softmax(x, out=x)  # y
-                    dy = torch.randn(M, N, device=dev, generator=gen).to(torch.bfloat16)
+                    dy = torch.randn(M, N, device=dev, generator=gen).to(tdt)
                 if rms:  # residual and weight
-                    dy = torch.randn(M, N, device=dev, generator=gen).to(torch.bfloat16)
-                    w = (1 + 0.5 * torch.randn(N, device=dev, generator=gen)).to(torch.bfloat16)
+                    dy = torch.randn(M, N, device=dev, generator=gen).to(tdt)
+                    w = (1 + 0.5 * torch.randn(N, device=dev, generator=gen)).to(tdt)
                 keys, times, model = {}, {}, {}
                 for key, o in GRID_PLANS.items():
                     opts = sm._opts(o)
                     if bwd:
                         rc, info = sm.sm_softmax_bwd_plan_query(
-                            x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N, N, N, N, sm.SM_BF16,
+                            x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N, N, N, N, code,
                             opts, 0)
                     elif rms:
                         rc, info = sm.sm_rmsnorm_plan_query(
                             x.data_ptr(), dy.data_ptr(), w.data_ptr(), out.data_ptr(), 0, M, N, N, N,
-                            N, 0, 1e-6, sm.SM_BF16, opts, 0)
+                            N, 0, 1e-6, code, opts, 0)
                     else:
                         rc, info = sm.sm_softmax_plan_query(x.data_ptr(), out.data_ptr(), M, N, N, N,
-                                                            sm.SM_BF16, opts, 0)
+                                                            code, opts, 0)
                     if rc != 0:
                         continue
                     sig = _signature(info)
@@ -608,14 +611,14 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                         opts.start_event, opts.stop_event = events
                         if bwd:
                             r = sm.sm_softmax_bwd_ex(x.data_ptr(), dy.data_ptr(), out.data_ptr(), M, N,
-                                                     N, N, N, sm.SM_BF16, opts, 0, 0, s_handle)
+                                                     N, N, N, code, opts, 0, 0, s_handle)
                         elif rms:
                             r = sm.sm_rmsnorm_fwd_ex(x.data_ptr(), dy.data_ptr(), w.data_ptr(),
                                                      out.data_ptr(), 0, M, N, N, N, N, 0, 1e-6,
-                                                     sm.SM_BF16, opts, 0, 0, s_handle)
+                                                     code, opts, 0, 0, s_handle)
                         else:
                             r = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N,
-                                                     sm.SM_BF16, opts, 0, 0, s_handle)
+                                                     code, opts, 0, 0, s_handle)
                         if r != 0:
                             raise sm.SoftmaxError(r)
 
@@ -636,7 +639,7 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
         runs.append(cells)
     if sm.sync_failures() != 0:
         raise RuntimeError("SPLIT waits timed out during the grid")
-    data = {"op": args.grid_op, "dtype": "bf16", "rows": GRID_ROWS, "widths": GRID_WIDTHS,
+    data = {"op": args.grid_op, "dtype": args.grid_dtype, "rows": GRID_ROWS, "widths": GRID_WIDTHS,
             "steps": args.grid_steps, "runs": runs}
     with open(args.plan_grid, "w") as f:
         json.dump(data, f, separators=(",", ":"))

@@ -200,6 +200,25 @@ bool one_pass_rule(int64_t M, int64_t N, int64_t nw) {
     return N <= kResidentMaxCols || (nw <= kOnePassWideWindows && M >= kOnePassWideRows);
 }
 
+// FP32 forward, refitted on an FP32 row-plan grid (18 row counts x 10 widths, two runs;
+// the BF16 rule there: mean regret 6.9%, 57 of 180 cells over 10%). FP32 rows cost more
+// VALU per 16-byte window (compensated sums and exponentials), which moves three choices:
+// one-pass rows up to 8192 windows from 128 rows (the 1024 x 8 shape beat SPLIT by 27 to
+// 36% at width 32768); SPLIT slices of one vector per lane while a row's slices fit one
+// round (V = 2 lost 12 to 23% at up to 24 rows); no V = 4 preference in rounds; and the
+// two-pass WIDE plan with 8 chunks per wave for rows of at least 2^17 windows that would
+// take SPLIT 4 or more rounds (SPLIT lost 11 to 21% there). Mean regret 0.8%, p90 2.4%,
+// 2 cells over 10% on the grid it was fitted on.
+constexpr int64_t kF32OnePassWideWindows = 8192;
+constexpr int64_t kF32WideWindows = int64_t(1) << 17;
+constexpr int64_t kF32WideRounds = 4;
+constexpr int kF32WideChunksPerWave = 8;
+
+bool fwd_one_pass_rule(int64_t M, int64_t N, int64_t nw, int dtype) {
+    return one_pass_rule(M, N, nw) ||
+           (dtype == SM_F32 && nw <= kF32OnePassWideWindows && M >= kOnePassWideRows);
+}
+
 struct DeviceView {
     int cus;
     // workgroups per CU for a row-kernel instance / for the wide kernels
@@ -300,8 +319,10 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     int plan = o.plan;
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
-    if (auto_plan) plan = one_pass_rule(p.M, p.N, nw_max) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
+    if (auto_plan) plan = fwd_one_pass_rule(p.M, p.N, nw_max, p.dtype) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
     if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
+    const bool f32 = p.dtype == SM_F32;
+    int64_t wide_cpw = 0;  // preferred chunks per wave of an automatic WIDE plan (0: by the grid)
 
     if (plan == SM_PLAN_SPLIT) {
         int64_t P = 0, grid = 0;
@@ -311,8 +332,13 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
             const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
             if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
         } else {
-            V = split_auto_v(p.M, nw_max, 2, 8, 4, kSplitRoundSlices, dev.cus, dev.ctx, p.dtype, 0,
-                             dev.occ_split, P, grid);
+            V = split_auto_v(p.M, nw_max, f32 ? 1 : 2, 8, 4, f32 ? 0 : kSplitRoundSlices, dev.cus, dev.ctx,
+                             p.dtype, 0, dev.occ_split, P, grid);
+            if (V && f32 && auto_plan && o.grid <= 0 && nw_max >= kF32WideWindows &&
+                (p.M * P + grid - 1) / grid >= kF32WideRounds) {
+                V = 0;
+                wide_cpw = kF32WideChunksPerWave;
+            }
             if (V && o.grid > 0) {
                 const int64_t slots = (int64_t)std::max(1, dev.occ_split(dev.ctx, p.dtype, V, 0)) * dev.cus;
                 if (!split_geometry(p.M, nw_max, V, slots, o.grid, P, grid)) V = 0;
@@ -343,7 +369,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     if (plan == SM_PLAN_WIDE) {
         const int WPC = kChunk / E;
         const int64_t nchunks = (nw_max + WPC - 1) / WPC;
-        int64_t cpw = o.chunks_per_wave;
+        int64_t cpw = o.chunks_per_wave > 0 ? o.chunks_per_wave : wide_cpw;
         if (cpw <= 0) {
             const int64_t target = (int64_t)dev.cus * 32;  // one full wave slot set
             cpw = std::max<int64_t>(1, (p.M * nchunks + target - 1) / target);

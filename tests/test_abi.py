@@ -159,9 +159,9 @@ def test_plan_rule_split():
     assert rc == OK and p["plan_name"] == "split" and p["launches"] == 1
     assert (p["vecs_per_lane"], p["waves_per_row"], p["grid"]) == (4, 16, 1024)
     assert p["workspace_bytes"] == 64 * 16 * 32 and p["model_bytes"] == 2 * 64 * 131072 * 2
-    rc, p = plan(4, 8193, F32)  # just past the one-pass limit: 2049 windows -> 5 slices of 512
-    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 5)
-    assert p["grid"] == 20 and p["slice_windows"] == 410  # 2049 windows spread over 5 slices
+    rc, p = plan(4, 8193, BF16)  # just past the one-pass limit: 1025 windows -> 3 slices of 512
+    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 3)
+    assert p["grid"] == 12 and p["slice_windows"] == 342  # 1025 windows spread over 3 slices
     rc, p = plan(1024, 32769, BF16, {"plan": sm.SM_PLAN_SPLIT, "vecs_per_lane": 8})
     assert (p["waves_per_row"], p["slice_windows"]) == (3, 1366)  # not 2048 + 2048 + 1
     rc, p = plan(1, 1 << 20, BF16)  # V=2 would need 256 slices per row: V=4, 128 slices
@@ -196,6 +196,33 @@ def test_plan_rule_split():
     assert rc == OK and p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (2, 1)
     rc, p = plan(100, 3000, BF16, {**S, "vecs_per_lane": 1})
     assert rc == OK and p["waves_per_row"] == 2
+
+
+def test_plan_rule_fp32_forward():
+    """FP32 rows (fitted on an FP32 row-plan grid): SPLIT slices of one vector per lane
+    while a row's slices fit one round, one-pass rows up to 8192 windows from 128 rows,
+    the largest V in rounds, and WIDE with 8 chunks per wave for rows of 2^17 windows or
+    more that SPLIT would take 4 or more rounds over; BF16 keeps its own choices there."""
+    rc, p = plan(4, 8193, F32)  # 2049 windows -> 9 slices of 256
+    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (1, 9)
+    assert p["grid"] == 36 and p["slice_windows"] == 228
+    rc, p = plan(256, 32768, F32)  # 8192 windows, 256 rows: one-pass 1024 x 8
+    assert (p["plan_name"], p["lanes_per_row"], p["vecs_per_lane"]) == ("persistent", 1024, 8)
+    rc, p = plan(127, 32768, F32)  # fewer rows: SPLIT
+    assert p["plan_name"] == "split"
+    rc, p = plan(256, 65536, F32)  # 16384 windows in rounds: the largest V
+    assert p["plan_name"] == "split" and (p["vecs_per_lane"], p["waves_per_row"]) == (8, 8)
+    rc, p = plan(256, 1 << 20, F32)  # 2^18 windows, 128 slices per row, 32 rounds: WIDE
+    assert (p["plan_name"], p["chunks_per_wave"], p["launches"]) == ("wide", 8, 2)
+    rc, p = plan(4, 1 << 20, F32)  # one round of 512 slices: SPLIT
+    assert p["plan_name"] == "split" and p["vecs_per_lane"] == 8
+    rc, p = plan(256, 1 << 20, F32, {"plan": sm.SM_PLAN_SPLIT})  # forced: SPLIT in rounds
+    assert rc == OK and p["plan_name"] == "split"
+    rc, p = plan(256, 1 << 20, F32, {"grid": 1024})  # a fixed (valid) SPLIT grid keeps SPLIT
+    assert rc == OK and p["plan_name"] == "split"
+    for M, N, want in [(256, 65536, ("split", 8)), (4, 16386, ("split", 2)), (256, 1 << 21, ("split", 8))]:
+        rc, p = plan(M, N, BF16)
+        assert (p["plan_name"], p["vecs_per_lane"]) == want, (M, N, p)
 
 
 def test_plan_forcing_and_limits():

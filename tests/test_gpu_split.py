@@ -333,3 +333,25 @@ def test_widest_rows_backward():
     _widest_backward(lim, True)
     _widest_backward(lim + 1, False)
     _widest_backward((1 << 23) + 7, False)
+
+
+@pytest.mark.parametrize("M,N", [(4, 16385), (256, 32768), (64, 1 << 19)])
+def test_fp32_automatic_plans(M, N):
+    """The FP32 terms of the forward rule against the oracle: few rows split into slices
+    of one vector per lane, 8192-window rows from 128 rows one-pass (1024 lanes x 8), and
+    2^17-window rows over several SPLIT rounds on the two-pass plan (8 chunks per wave)."""
+    x = _rand(M, N, "f32", seed=N % 991 + M)
+    xd = x.to(DEV)
+    info = sm.plan_for(xd)
+    log(f"[split] fp32 {M}x{N}: plan {info['plan_name']} G={info['lanes_per_row']} "
+        f"V={info['vecs_per_lane']} P={info['waves_per_row']} cpw={info['chunks_per_wave']}")
+    if (M, N) == (4, 16385):
+        assert (info["plan_name"], info["vecs_per_lane"]) == ("split", 1)
+    if (M, N) == (256, 32768):
+        assert (info["plan_name"], info["lanes_per_row"], info["vecs_per_lane"]) == ("persistent", 1024, 8)
+    before = sm.sync_failures()  # cumulative per stream
+    out = torch.full_like(xd, float("nan"))
+    sm.softmax(xd, out=out)
+    torch.cuda.synchronize()
+    compare(out, x, what=f"fp32 auto {M}x{N} {info['plan_name']}")
+    assert sm.sync_failures() == before

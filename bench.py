@@ -499,6 +499,18 @@ def record_traffic(fetch_csv: str, write_csv: str) -> dict:
     return rec
 
 
+def cpu_model() -> str | None:
+    """The host CPU's model name (from /proc/cpuinfo), None where unavailable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
     """The FP64 oracle, as it stands, on this host's cores: repetitions of the whole
     4096 x 4096 input until the budget is spent (median per repetition), and one
@@ -525,7 +537,8 @@ def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
            "kind": "oracle",
            "sample": f"the whole 4096x4096 BF16 input, {len(times)} repetitions in "
                      f"{sum(times):.1f} s, median per repetition {med * 1e3:.1f} ms",
-           "value_1_thread": round(model_bytes / t1 / 1e9, 3)}
+           "value_1_thread": round(model_bytes / t1 / 1e9, 3), "cpu_model": cpu_model(),
+           "host_cpus_available": len(os.sched_getaffinity(0))}
     log(f"[bench] cpu oracle: {res}")
     try:
         parity = {"passed": True, **compare(gpu_out, x_cpu, what="bench output")}

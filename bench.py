@@ -326,21 +326,14 @@ def main(argv=None) -> int:
         if rc != 0:
             raise sm.SoftmaxError(rc, "sm_bench_copy")
 
-    # the ceiling is the best of a few launch shapes under either store policy
-    copy_cold, copy_grid, copy_scope = None, None, None
-    for scope in (0, 1):
-        for grid in (512, 1024, 2048, 4096, 8192):  # 8192: one vector per thread at 32 MiB
-            for _ in range(args.warmup):
-                flush()
-                copy(grid, scope)
-            ev = DispatchEvents(args.steps)
-            for _ in range(args.steps):
-                flush()
-                copy(grid, scope, ev.next_pair())
-            st = stats_us(ev.samples_ms(torch))
-            ev.close()
-            if copy_cold is None or st["mean_us"] < copy_cold["mean_us"]:
-                copy_cold, copy_grid, copy_scope = st, grid, scope
+    # the ceiling is the best of a few launch shapes under either store policy, timed in
+    # rotating order
+    shapes = [(grid, scope) for scope in (0, 1)
+              for grid in (512, 1024, 2048, 4096, 8192)]  # 8192: one vector per thread at 32 MiB
+    sts = time_rotating(torch, [lambda events=(None, None), g=g, s=s: copy(g, s, events)
+                                for g, s in shapes], flush, args.steps, args.warmup)
+    k = min(range(len(shapes)), key=lambda i: sts[i]["mean_us"])
+    copy_cold, (copy_grid, copy_scope) = sts[k], shapes[k]
     del src, dst
 
     gbps = model_bytes / (cold["mean_us"] * 1e-6) / 1e9
@@ -599,7 +592,7 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                 if rms:  # residual and weight
                     dy = torch.randn(M, N, device=dev, generator=gen).to(tdt)
                     w = (1 + 0.5 * torch.randn(N, device=dev, generator=gen)).to(tdt)
-                keys, times, model = {}, {}, {}
+                keys, calls = {}, {}
                 for key, o in GRID_PLANS.items():
                     opts = sm._opts(o)
                     if bwd:
@@ -617,7 +610,7 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                         continue
                     sig = _signature(info)
                     keys[key] = sig
-                    if sig in times:
+                    if sig in calls:
                         continue
 
                     def call(events=(None, None), opts=opts):
@@ -635,16 +628,10 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
                         if r != 0:
                             raise sm.SoftmaxError(r)
 
-                    for _ in range(2):
-                        flush()
-                        call()
-                    ev = DispatchEvents(args.grid_steps)
-                    for _ in range(args.grid_steps):
-                        flush()
-                        call(ev.next_pair())
-                    times[sig] = round(float(np.mean(ev.samples_ms(torch))) * 1e3, 3)
-                    ev.close()
-                    model[sig] = int(info.model_bytes)
+                    calls[sig] = call
+                # the distinct plans of a cell in rotating order, sample by sample
+                st = time_rotating(torch, list(calls.values()), flush, args.grid_steps, 2)
+                times = {sig: round(s["mean_us"], 3) for sig, s in zip(calls, st)}
                 cells.append({"M": M, "N": N, "keys": keys, "us": times})
                 del x, out, dy, w
             torch.cuda.empty_cache()
@@ -699,6 +686,30 @@ def score_grid(data: dict) -> dict:
     return out
 
 
+def time_rotating(torch, calls, flush, steps, warmup):
+    """Cold timing of several calls of one workload, interleaved: round i times every
+    call once, after a cache sweep each, starting from call i mod len(calls), so slow
+    drifts of clock and temperature spread over all calls alike instead of landing on
+    whichever call happened to run last. ``warmup`` untimed rounds come first. Returns
+    one stats_us() dict per call, in the order given."""
+    n = len(calls)
+    for i in range(warmup):
+        for j in range(n):
+            flush()
+            calls[(i + j) % n]()
+    evs = [DispatchEvents(steps) for _ in calls]
+    for i in range(steps):
+        for j in range(n):
+            k = (i + j) % n
+            flush()
+            calls[k](evs[k].next_pair())
+    out = []
+    for e in evs:
+        out.append(stats_us(e.samples_ms(torch)))
+        e.close()
+    return out
+
+
 def sweep(torch, sm, workloads, flush, s_handle, log, args):
     """Cold timing of every workload under every plan that can take it (softmax forward
     and backward), then the residual RMSNorm shapes."""
@@ -719,31 +730,23 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
         out = torch.empty_like(x)
         M, N = x.shape
         dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[x.dtype]
+        runs = []
         for pname, p in plans.items():
             if p in (1, 2) and N > 8192:
                 continue
-            opts = {"plan": p}
-            info = sm.plan_for(x, out, opts)
-
+            info = sm.plan_for(x, out, {"plan": p})
             o = sm.SmOpts()
             o.plan = p
 
-            def call(events=(None, None)):
+            def call(events=(None, None), o=o):
                 o.start_event, o.stop_event = events
                 rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N, dt, o, 0, 0,
                                           s_handle)
                 if rc != 0:
                     raise sm.SoftmaxError(rc)
-
-            for _ in range(5):
-                flush()
-                call()
-            t = DispatchEvents(steps)
-            for _ in range(steps):
-                flush()
-                call(t.next_pair())
-            st = stats_us(t.samples_ms(torch))
-            t.close()
+            runs.append((pname, info, call))
+        stats = time_rotating(torch, [c for _, _, c in runs], flush, steps, 10)
+        for (pname, info, _), st in zip(runs, stats):
             gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
             line = {"workload": name, "plan": pname, "resolved": info["plan_name"],
                     "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
@@ -754,18 +757,23 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
             log("[sweep] " + json.dumps(line))
         sm.softmax(x, out)
         dy = workloads.upstream_grad(x.shape, workloads.dtype_name(x), device="cuda")
+        runs = []
         for pname, p in plans.items():
             if p in (1, 2) and N > 8192:
                 continue
-            st, info = time_backward(torch, sm, out, dy, p, flush, s_handle, steps, 5)
+            runs.append((pname,) + backward_call(torch, sm, out, dy, p, s_handle))
+        stats = time_rotating(torch, [c for _, _, c, _ in runs], flush, steps, 10)
+        for (pname, info, _, dx), st in zip(runs, stats):
             gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
             line = {"workload": name, "op": "backward", "plan": pname, "resolved": info["plan_name"],
                     "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
                     "cpw": info["chunks_per_wave"], "grid": info["grid"],
                     "model_bytes": info["model_bytes"], "mean_us": round(st["mean_us"], 3),
                     "median_us": round(st["median_us"], 3), "GBps": round(gb, 1),
-                    "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
+                    "pct_peak": round(100 * gb / PEAK_GBPS, 2),
+                    "max_abs_row_sum": round(dx.float().sum(dim=1).abs().max().item(), 6)}
             log("[sweep] " + json.dumps(line))
+        del runs
         del x, out, dy
         torch.cuda.empty_cache()
 
@@ -788,6 +796,7 @@ def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
         r = torch.randn(M, N, device="cuda", generator=gen).to(tdt[dt])
         w = (1 + 0.5 * torch.randn(N, device="cuda", generator=gen)).to(tdt[dt])
         y = torch.empty_like(x)
+        runs = []
         for pname, p in plans.items():
             o = sm.SmOpts()
             o.plan = p
@@ -796,22 +805,15 @@ def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
             if rc != 0:
                 continue
 
-            def call(events=(None, None)):
+            def call(events=(None, None), o=o):
                 o.start_event, o.stop_event = events
                 rc = sm.sm_rmsnorm_fwd_ex(x.data_ptr(), r.data_ptr(), w.data_ptr(), y.data_ptr(), 0, M,
                                           N, N, N, N, 0, 1e-6, code[dt], o, 0, 0, s_handle)
                 if rc != 0:
                     raise sm.SoftmaxError(rc)
-
-            for _ in range(5):
-                flush()
-                call()
-            t = DispatchEvents(steps)
-            for _ in range(steps):
-                flush()
-                call(t.next_pair())
-            st = stats_us(t.samples_ms(torch))
-            t.close()
+            runs.append((pname, info, call))
+        stats = time_rotating(torch, [c for _, _, c in runs], flush, steps, 10)
+        for (pname, info, _), st in zip(runs, stats):
             line = {"workload": f"rmsnorm_{dt}_{M}x{N}", "op": "rmsnorm", "plan": pname,
                     "resolved": info.as_dict()["plan_name"], "G": info.lanes_per_row,
                     "V": info.vecs_per_lane, "cpw": info.waves_per_row, "grid": info.grid,
@@ -824,8 +826,9 @@ def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
     torch.cuda.empty_cache()
 
 
-def time_backward(torch, sm, y, dy, plan, flush, s_handle, steps, warmup):
-    """Cold timing of sm_softmax_bwd_ex (dx in a buffer of its own) under ``plan``."""
+def backward_call(torch, sm, y, dy, plan, s_handle):
+    """(plan info, call, dx) for sm_softmax_bwd_ex under ``plan``, dx in a buffer of its
+    own; call(events) runs one backward with the dispatch events given."""
     dx = torch.empty_like(y)
     M, N = y.shape
     o = sm.SmOpts()
@@ -839,16 +842,13 @@ def time_backward(torch, sm, y, dy, plan, flush, s_handle, steps, warmup):
                                   dy.stride(0), dx.stride(0), dt, o, 0, 0, s_handle)
         if rc != 0:
             raise sm.SoftmaxError(rc, "sm_softmax_bwd_ex")
+    return info, call, dx
 
-    for _ in range(warmup):
-        flush()
-        call()
-    t = DispatchEvents(steps)
-    for _ in range(steps):
-        flush()
-        call(t.next_pair())
-    st = stats_us(t.samples_ms(torch))
-    t.close()
+
+def time_backward(torch, sm, y, dy, plan, flush, s_handle, steps, warmup):
+    """Cold timing of sm_softmax_bwd_ex (dx in a buffer of its own) under ``plan``."""
+    info, call, dx = backward_call(torch, sm, y, dy, plan, s_handle)
+    st, = time_rotating(torch, [call], flush, steps, warmup)
     # property of every correct dx: each row sums to d * (1 - sum(y)), about 0
     rs = dx.float().sum(dim=1).abs().max().item()
     info["max_abs_row_sum"] = rs

@@ -87,3 +87,39 @@ def test_gpu_sampler_is_a_diagnostic_only():
     assert st["samples"] == 2
     assert (st["gfx_clk_mhz_min"], st["gfx_clk_mhz_max"], st["gfx_clk_mhz_mean"]) == (2000, 2200, 2100.0)
     assert st["socket_power_w_max"] == 900 and st["hotspot_c_max"] == 60 and st["mem_temp_c_max"] is None
+
+
+def test_rotating_timing_interleaves_the_calls(monkeypatch):
+    """Round i times every call once, starting from call i mod n, each after a cache
+    sweep; warm-up calls carry no events; every call gets exactly `steps` samples."""
+    log = []
+
+    class FakeEvents:
+        def __init__(self, n):
+            self.n, self.used = n, 0
+
+        def next_pair(self):
+            self.used += 1
+            return ("start", "stop")
+
+        def samples_ms(self, torch):
+            return [0.001 * (1 + i) for i in range(self.used)]
+
+        def close(self):
+            pass
+
+    monkeypatch.setattr(bench, "DispatchEvents", FakeEvents)
+
+    def make(k):
+        def call(events=(None, None)):
+            log.append((k, events != (None, None)))
+        return call
+
+    flushes = []
+    st = bench.time_rotating(None, [make(0), make(1), make(2)], lambda: flushes.append(1), 4, 2)
+    warm, timed = log[:6], log[6:]
+    assert all(not t for _, t in warm) and all(t for _, t in timed)
+    assert [k for k, _ in timed] == [0, 1, 2, 1, 2, 0, 2, 0, 1, 0, 1, 2]
+    assert len(flushes) == len(log) == 18
+    assert [s["n"] for s in st] == [4, 4, 4]
+    assert st[0]["mean_us"] == pytest.approx(2.5)

@@ -43,6 +43,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import itertools
 import json
 import os
 import statistics
@@ -162,6 +163,17 @@ class DispatchEvents:
         self.events = []
 
 
+def make_flush(torch, sm, s_handle):
+    """A cold-cache call: one read-only sweep of a 1 GiB device buffer on the stream."""
+    buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    def flush():
+        rc = sm.sm_bench_flush(buf.data_ptr(), FLUSH_BYTES, s_handle)
+        if rc != 0:
+            raise sm.SoftmaxError(rc, "sm_bench_flush")
+    return flush
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +204,14 @@ def main(argv=None) -> int:
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from the two rocprofv3 --pmc "
                          "CSVs (FETCH_SIZE run, WRITE_SIZE run) of this bench, and exit")
+    ap.add_argument("--counter-pass", metavar="MANIFEST_JSON",
+                    help="one cold call of every sweep case, each after a cache sweep (run it "
+                         "under rocprofv3 --pmc), write the calls in dispatch order, and exit")
+    ap.add_argument("--traffic-table", nargs=3, metavar=("MANIFEST_JSON", "FETCH_CSV", "WRITE_CSV"),
+                    help="HBM bytes per call of every sweep case from the counter pass's manifest "
+                         "and its FETCH_SIZE and WRITE_SIZE runs (markdown on stdout), and exit")
+    ap.add_argument("--sq-csv", help="with --traffic-table: an SQ counter run of the same pass")
+    ap.add_argument("--sweep-log", help="with --traffic-table: a --sweep log, for times and GB/s")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
@@ -202,6 +222,9 @@ def main(argv=None) -> int:
         return 0
     if args.record_traffic:
         print(json.dumps(record_traffic(*args.record_traffic), indent=1))
+        return 0
+    if args.traffic_table:
+        print(traffic_table(*args.traffic_table, sq_csv=args.sq_csv, sweep_log=args.sweep_log))
         return 0
     if args.score_grid:
         with open(args.score_grid) as f:
@@ -230,6 +253,9 @@ def main(argv=None) -> int:
 
     if args.plan_grid:
         return plan_grid(torch, sm, s_handle, log, args)
+    if args.counter_pass:
+        return counter_pass(torch, sm, workloads, make_flush(torch, sm, s_handle), s_handle,
+                            args.counter_pass, 64 << 20, log)
 
     # ---------------------------------------------------------------- input
     x_cpu = workloads.generate(WORKLOAD)
@@ -271,12 +297,7 @@ def main(argv=None) -> int:
         return 1
     log("[bench] property gate passed")
 
-    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
-
-    def flush():
-        rc = sm.sm_bench_flush(flush_buf.data_ptr(), FLUSH_BYTES, s_handle)
-        if rc != 0:
-            raise sm.SoftmaxError(rc, "sm_bench_flush")
+    flush = make_flush(torch, sm, s_handle)
 
     # ---------------------------------------------------------------- clocks up
     # 1 s of cache sweeps keep the GPU busy without calling the timed kernel, so a
@@ -492,6 +513,100 @@ def record_traffic(fetch_csv: str, write_csv: str) -> dict:
     return rec
 
 
+def counter_groups(path: str) -> list:
+    """The library's dispatches in a rocprofv3 --pmc CSV, in dispatch order, cut into
+    groups at each cache-sweep dispatch (empty groups dropped): one group per call of
+    the counter pass, each a list of (kernel, {counter: value})."""
+    import csv
+    rows = {}
+    for r in csv.DictReader(open(path)):
+        k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        d = rows.setdefault(int(r["Dispatch_Id"]), (k, {}))[1]
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    groups, cur = [], []
+    for i in sorted(rows):
+        k, c = rows[i]
+        if not k.startswith("smx::"):
+            continue
+        if k.startswith("smx::k_sweep_read16"):
+            if cur:
+                groups.append(cur)
+            cur = []
+        else:
+            cur.append((k, c))
+    if cur:
+        groups.append(cur)
+    return groups
+
+
+def traffic_table(manifest_path: str, fetch_csv: str, write_csv: str, sq_csv=None,
+                  sweep_log=None) -> str:
+    """Markdown table of the HBM bytes of one cold call per sweep case (FETCH_SIZE and
+    WRITE_SIZE summed over the call's kernels, each scaled by what it reads for the
+    calibration copy of known size), against the plan's algorithmic bytes; with sq_csv,
+    VALU busy and LDS bank conflicts; with sweep_log, the sweep's mean time and the
+    physical GB/s."""
+    with open(manifest_path) as f:
+        man = json.load(f)
+    calls = man["calls"]
+    runs = {"FETCH_SIZE": counter_groups(fetch_csv), "WRITE_SIZE": counter_groups(write_csv)}
+    if sq_csv:
+        runs["SQ"] = counter_groups(sq_csv)
+    for name, g in runs.items():
+        if len(g) != len(calls):
+            raise RuntimeError(f"{name} run: {len(g)} call groups, manifest has {len(calls)}")
+        for c, grp in zip(calls, g):
+            if c["launches"] is not None and c["launches"] != len(grp):
+                raise RuntimeError(f"{name} run: {c} has {len(grp)} dispatches: "
+                                   f"{[k for k, _ in grp]}")
+
+    def total(grp, counter):
+        return sum(v.get(counter, 0.0) for _, v in grp)
+
+    cb = man["copy_bytes"]
+    if not runs["FETCH_SIZE"][0][0][0].startswith("smx::k_copy16"):
+        raise RuntimeError("the first call is not the calibration copy")
+    ff = (cb / 2 / 1024) / total(runs["FETCH_SIZE"][0], "FETCH_SIZE")
+    wf = (cb / 2 / 1024) / total(runs["WRITE_SIZE"][0], "WRITE_SIZE")
+    times = {}
+    if sweep_log:
+        for line in open(sweep_log):
+            if line.startswith("[sweep] "):
+                d = json.loads(line[len("[sweep] "):])
+                if "plan" in d:  # row kernels only (the attention lines carry no plan)
+                    times[(d["workload"], d.get("op", "forward"), d["plan"])] = d.get("mean_us")
+    head = ["workload", "op", "plan", "resolved (G, V, cpw, grid)", "kernels", "algorithmic MB",
+            "fetched MB", "written MB", "HBM / algorithmic"]
+    if times:
+        head += ["mean µs", "physical GB/s"]
+    if sq_csv:
+        head += ["VALU busy", "LDS bank conflicts / LDS instr."]
+    out = ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for i, c in enumerate(calls):
+        if c["op"] in ("copy", "setup"):
+            continue
+        fetch = total(runs["FETCH_SIZE"][i], "FETCH_SIZE") * ff * 1024
+        write = total(runs["WRITE_SIZE"][i], "WRITE_SIZE") * wf * 1024
+        cells = [c["workload"], c["op"], c["plan"],
+                 f"{c['resolved']} ({c['G']}, {c['V']}, {c['cpw']}, {c['grid']})",
+                 str(c["launches"]), f"{c['model_bytes'] / 1e6:.3f}", f"{fetch / 1e6:.3f}",
+                 f"{write / 1e6:.3f}", f"{(fetch + write) / c['model_bytes']:.3f}"]
+        if times:
+            t = times.get((c["workload"], c["op"], c["plan"]))
+            cells += [f"{t:.3f}", f"{(fetch + write) / (t * 1e-6) / 1e9:.0f}"] if t else ["", ""]
+        if sq_csv:
+            g = runs["SQ"][i]
+            busy = total(g, "SQ_ACTIVE_INST_VALU") / max(total(g, "SQ_BUSY_CU_CYCLES"), 1.0)
+            lds = total(g, "SQ_INSTS_LDS")
+            conf = total(g, "SQ_LDS_BANK_CONFLICT") / lds if lds else 0.0
+            cells += [f"{100 * busy:.0f}%", f"{conf:.3f}"]
+        out.append("| " + " | ".join(cells) + " |")
+    out.append("")
+    out.append(f"Calibration: the 16-byte copy of {cb >> 20} MiB ({cb >> 21} MiB in, {cb >> 21} MiB out) "
+               f"gives FETCH_SIZE x {ff:.5f}, WRITE_SIZE x {wf:.5f}.")
+    return "\n".join(out)
+
+
 def cpu_model() -> str | None:
     """The host CPU's model name (from /proc/cpuinfo), None where unavailable."""
     try:
@@ -567,11 +682,7 @@ def plan_grid(torch, sm, s_handle, log, args) -> int:
     """Time every plan of every grid cell (cold calls, dispatch events), write the cell
     times, print the regret summary."""
     dev = torch.device("cuda")
-    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
-
-    def flush():
-        if sm.sm_bench_flush(flush_buf.data_ptr(), FLUSH_BYTES, s_handle) != 0:
-            raise RuntimeError("sm_bench_flush failed")
+    flush = make_flush(torch, sm, s_handle)
 
     bwd = args.grid_op == "bwd"
     rms = args.grid_op == "rms"
@@ -710,73 +821,7 @@ def time_rotating(torch, calls, flush, steps, warmup):
     return out
 
 
-def sweep(torch, sm, workloads, flush, s_handle, log, args):
-    """Cold timing of every workload under every plan that can take it (softmax forward
-    and backward), then the residual RMSNorm shapes."""
-    sweep_rmsnorm(torch, sm, flush, s_handle, log, max(100, args.steps // 2))
-    names = ["normal_f32_128x781", "normal_bf16_4096x4096",
-             *[f"spiky_f16_8192x{n}" for n in workloads.SPIKE_WIDTHS],
-             "offset_bf16_64x131072", "causal_bf16_524288x2048"]
-    plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
-    steps = max(100, args.steps // 2)  # at least 100 timed samples per (workload, plan)
-    for name in names:
-        x = workloads.generate(name).to("cuda")
-        # the GPU idled while the input was built on the host: bring the clocks back up
-        t_end = time.perf_counter() + 0.2
-        while time.perf_counter() < t_end:
-            for _ in range(20):
-                flush()
-            torch.cuda.synchronize()
-        out = torch.empty_like(x)
-        M, N = x.shape
-        dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[x.dtype]
-        runs = []
-        for pname, p in plans.items():
-            if p in (1, 2) and N > 8192:
-                continue
-            info = sm.plan_for(x, out, {"plan": p})
-            o = sm.SmOpts()
-            o.plan = p
-
-            def call(events=(None, None), o=o):
-                o.start_event, o.stop_event = events
-                rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N, dt, o, 0, 0,
-                                          s_handle)
-                if rc != 0:
-                    raise sm.SoftmaxError(rc)
-            runs.append((pname, info, call))
-        stats = time_rotating(torch, [c for _, _, c in runs], flush, steps, 10)
-        for (pname, info, _), st in zip(runs, stats):
-            gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
-            line = {"workload": name, "plan": pname, "resolved": info["plan_name"],
-                    "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
-                    "cpw": info["chunks_per_wave"], "grid": info["grid"],
-                    "model_bytes": info["model_bytes"], "mean_us": round(st["mean_us"], 3),
-                    "median_us": round(st["median_us"], 3), "GBps": round(gb, 1),
-                    "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
-            log("[sweep] " + json.dumps(line))
-        sm.softmax(x, out)
-        dy = workloads.upstream_grad(x.shape, workloads.dtype_name(x), device="cuda")
-        runs = []
-        for pname, p in plans.items():
-            if p in (1, 2) and N > 8192:
-                continue
-            runs.append((pname,) + backward_call(torch, sm, out, dy, p, s_handle))
-        stats = time_rotating(torch, [c for _, _, c, _ in runs], flush, steps, 10)
-        for (pname, info, _, dx), st in zip(runs, stats):
-            gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
-            line = {"workload": name, "op": "backward", "plan": pname, "resolved": info["plan_name"],
-                    "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
-                    "cpw": info["chunks_per_wave"], "grid": info["grid"],
-                    "model_bytes": info["model_bytes"], "mean_us": round(st["mean_us"], 3),
-                    "median_us": round(st["median_us"], 3), "GBps": round(gb, 1),
-                    "pct_peak": round(100 * gb / PEAK_GBPS, 2),
-                    "max_abs_row_sum": round(dx.float().sum(dim=1).abs().max().item(), 6)}
-            log("[sweep] " + json.dumps(line))
-        del runs
-        del x, out, dy
-        torch.cuda.empty_cache()
-
+SWEEP_PLANS = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
 
 # residual RMSNorm shapes: the FP16 shapes of "Measured optimization case studies"
 # (residual RMSNorm section) and the BF16 batch x hidden shapes of the Warpline README
@@ -785,9 +830,16 @@ RMS_SHAPES = [("f16", 32, 127), ("f16", 1024, 1024), ("f16", 512, 4097), ("f16",
               ("bf16", 16, 2048), ("bf16", 32, 4096), ("bf16", 64, 4096), ("bf16", 64, 8192)]
 
 
-def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
-    """Cold timing of the residual RMSNorm (y only) under every plan that can take it."""
-    plans = {"auto": 0, "resident": 1, "persistent": 2, "wide": 3, "split": 4}
+def plan_fields(info: dict, op: str) -> dict:
+    """The plan columns of a sweep line."""
+    return {"resolved": info["plan_name"], "G": info["lanes_per_row"], "V": info["vecs_per_lane"],
+            "cpw": info["waves_per_row"] if op == "rmsnorm" else info["chunks_per_wave"],
+            "grid": info["grid"], "model_bytes": info["model_bytes"]}
+
+
+def rmsnorm_groups(torch, sm, s_handle):
+    """The residual RMSNorm cases (y only), one shape at a time: yields (workload, op,
+    setup, runs) as softmax_groups does."""
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
     code = {"f16": sm.SM_F16, "bf16": sm.SM_BF16}
     gen = torch.Generator(device="cuda").manual_seed(2026)
@@ -797,7 +849,7 @@ def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
         w = (1 + 0.5 * torch.randn(N, device="cuda", generator=gen)).to(tdt[dt])
         y = torch.empty_like(x)
         runs = []
-        for pname, p in plans.items():
+        for pname, p in SWEEP_PLANS.items():
             o = sm.SmOpts()
             o.plan = p
             rc, info = sm.sm_rmsnorm_plan_query(x.data_ptr(), r.data_ptr(), w.data_ptr(), y.data_ptr(),
@@ -811,19 +863,120 @@ def sweep_rmsnorm(torch, sm, flush, s_handle, log, steps):
                                           N, N, N, N, 0, 1e-6, code[dt], o, 0, 0, s_handle)
                 if rc != 0:
                     raise sm.SoftmaxError(rc)
-            runs.append((pname, info, call))
-        stats = time_rotating(torch, [c for _, _, c in runs], flush, steps, 10)
-        for (pname, info, _), st in zip(runs, stats):
-            line = {"workload": f"rmsnorm_{dt}_{M}x{N}", "op": "rmsnorm", "plan": pname,
-                    "resolved": info.as_dict()["plan_name"], "G": info.lanes_per_row,
-                    "V": info.vecs_per_lane, "cpw": info.waves_per_row, "grid": info.grid,
-                    "model_bytes": info.model_bytes, "mean_us": round(st["mean_us"], 3),
-                    "median_us": round(st["median_us"], 3),
-                    "GBps": round(info.model_bytes / (st["mean_us"] * 1e-6) / 1e9, 1),
-                    "pct_peak": round(100 * info.model_bytes / (st["mean_us"] * 1e-6) / 1e9 / PEAK_GBPS, 2)}
-            log("[sweep] " + json.dumps(line))
-        del x, r, w, y
+            runs.append((pname, info.as_dict(), call, None))
+        yield f"rmsnorm_{dt}_{M}x{N}", "rmsnorm", None, runs
+        del runs, x, r, w, y
     torch.cuda.empty_cache()
+
+
+def softmax_groups(torch, sm, workloads, s_handle, clocks_up=None):
+    """The softmax cases of the sweep, one workload at a time: yields (workload, op,
+    setup, runs) for op "forward", then "backward", with runs = [(plan name, plan info,
+    call, check)]: call(events) runs one call under that plan, check() (or None) returns
+    fields that describe its output, and setup() (or None) must run before the group's
+    calls (the backward's y is the forward's output). A workload's tensors live until
+    the generator moves on; clocks_up() runs after each input reaches the device."""
+    names = ["normal_f32_128x781", "normal_bf16_4096x4096",
+             *[f"spiky_f16_8192x{n}" for n in workloads.SPIKE_WIDTHS],
+             "offset_bf16_64x131072", "causal_bf16_524288x2048"]
+    for name in names:
+        x = workloads.generate(name).to("cuda")
+        if clocks_up is not None:
+            clocks_up()
+        out = torch.empty_like(x)
+        M, N = x.shape
+        dt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[x.dtype]
+        plans = {k: p for k, p in SWEEP_PLANS.items() if not (p in (1, 2) and N > 8192)}
+        runs = []
+        for pname, p in plans.items():
+            o = sm.SmOpts()
+            o.plan = p
+
+            def call(events=(None, None), o=o):
+                o.start_event, o.stop_event = events
+                rc = sm.sm_softmax_fwd_ex(x.data_ptr(), out.data_ptr(), M, N, N, N, dt, o, 0, 0,
+                                          s_handle)
+                if rc != 0:
+                    raise sm.SoftmaxError(rc)
+            runs.append((pname, sm.plan_for(x, out, {"plan": p}), call, None))
+        yield name, "forward", None, runs
+        dy = workloads.upstream_grad(x.shape, workloads.dtype_name(x), device="cuda")
+        runs = []
+        for pname, p in plans.items():
+            info, call, dx = backward_call(torch, sm, out, dy, p, s_handle)
+            # property of every correct dx: each row sums to about 0
+            runs.append((pname, info, call, lambda dx=dx: {
+                "max_abs_row_sum": round(dx.float().sum(dim=1).abs().max().item(), 6)}))
+        yield name, "backward", lambda: sm.softmax(x, out), runs
+        del runs, x, out, dy
+        torch.cuda.empty_cache()
+
+
+def sweep(torch, sm, workloads, flush, s_handle, log, args):
+    """Cold timing of every workload under every plan that can take it (residual
+    RMSNorm, then softmax forward and backward), the plans of a workload in rotating
+    order."""
+    steps = max(100, args.steps // 2)  # at least 100 timed samples per (workload, plan)
+
+    def clocks_up():  # the GPU idled while the input was built on the host
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                flush()
+            torch.cuda.synchronize()
+
+    groups = itertools.chain(rmsnorm_groups(torch, sm, s_handle),
+                             softmax_groups(torch, sm, workloads, s_handle, clocks_up))
+    for name, op, setup, runs in groups:
+        if setup is not None:
+            setup()
+        stats = time_rotating(torch, [r[2] for r in runs], flush, steps, 10)
+        for (pname, info, _, check), st in zip(runs, stats):
+            gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
+            line = {"workload": name, "plan": pname, **plan_fields(info, op),
+                    "mean_us": round(st["mean_us"], 3), "median_us": round(st["median_us"], 3),
+                    "GBps": round(gb, 1), "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
+            if op != "forward":
+                line = {"workload": name, "op": op, **{k: v for k, v in line.items() if k != "workload"}}
+            if check is not None:
+                line.update(check())
+            log("[sweep] " + json.dumps(line))
+
+
+def counter_pass(torch, sm, workloads, flush, s_handle, manifest_path, copy_bytes, log) -> int:
+    """One cold call of every sweep case (residual RMSNorm, softmax forward and
+    backward, every plan), each right after a cache sweep, for rocprofv3 --pmc runs of
+    their own; first a 16-byte copy of copy_bytes, the calibration of the byte counters.
+    Writes the calls in dispatch order to manifest_path: the cache-sweep kernel's
+    dispatches cut the counter rows of the library's kernels into these calls."""
+    src = torch.ones(copy_bytes // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    flush()
+    rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), src.numel(), 0, 0, s_handle, None, None)
+    if rc != 0:
+        raise sm.SoftmaxError(rc, "sm_bench_copy")
+    del src, dst
+    calls = [{"op": "copy", "bytes": copy_bytes, "launches": 1}]
+    failures = sm.sync_failures()
+    groups = itertools.chain(rmsnorm_groups(torch, sm, s_handle),
+                             softmax_groups(torch, sm, workloads, s_handle))
+    for name, op, setup, runs in groups:
+        if setup is not None:
+            flush()
+            setup()
+            calls.append({"op": "setup", "workload": name, "launches": None})
+        for pname, info, call, _ in runs:
+            flush()
+            call()
+            calls.append({"workload": name, "op": op, "plan": pname, **plan_fields(info, op),
+                          "launches": info["launches"]})
+    torch.cuda.synchronize()
+    if sm.sync_failures() != failures:
+        raise RuntimeError("SPLIT waits timed out during the counter pass")
+    with open(manifest_path, "w") as f:
+        json.dump({"copy_bytes": copy_bytes, "calls": calls}, f, indent=0)
+    log(f"[counters] {len(calls)} calls written to {manifest_path}")
+    return 0
 
 
 def backward_call(torch, sm, y, dy, plan, s_handle):

@@ -138,14 +138,21 @@ struct RowShape {
 // narrowest first, measured on MI355X with cold calls. Rows of up to 64 windows
 // take one vector per lane in a sub-wave or wave. Wider rows spread over 2-16
 // waves with 2-4 vectors per lane, which beat 4-8 vectors per lane in one wave
-// (fewer registers, more waves in flight, shorter per-row latency). With many
-// rows (resident plan) 256-lane rows won from 256 windows up (524288 x 2048 BF16:
-// 659 us for 256 x 2 against 685 us for 128 x 2); with few rows (persistent
-// plan) the narrower 128-lane rows did (8192 x 2048 FP16: 11.8 us against 12.7).
-constexpr RowShape kShapesPersistent[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {128, 2},
-                                          {256, 2}, {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
-constexpr RowShape kShapesResident[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {256, 2},
-                                        {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+// (fewer registers, more waves in flight, shorter per-row latency). Rows of
+// 129-256 windows take 128 x 2: at the same occupancy a CU then holds twice the
+// rows, and so twice the loads, in flight that 256 x 1 holds, and 256 x 2 would
+// spend half of its lanes' arithmetic on padding (16384 x 1024 FP32: 21.4 us
+// against 25.5 for 256 x 1 and 33.5 for 256 x 2; 65536 x 2048 BF16: 75.4, 77.7
+// and 80.0 us; 65536 x 1500 FP16: 60.1 against 76.5 and 91.6 us).
+constexpr RowShape kShapes[] = {{16, 1},  {32, 1},  {64, 1},   {64, 2},   {128, 2},
+                                {256, 2}, {256, 4}, {512, 4}, {1024, 4}, {1024, 8}};
+// ... except in 16-bit calls of at least this many bytes, where one workgroup
+// per row takes 256 x 1: with that many rows HBM is saturated with fewer rows in
+// flight, and fewer was faster (524288 rows of BF16, N = 2048: 606 against 639
+// us; N = 2000: 758 against 928; 262144 x 2048: 307 against 311), while FP32
+// rows (262144 x 1024: 356 against 312 us) and smaller calls (131072 x 2048
+// BF16: 148 against 145 us) kept 128 x 2.
+constexpr int64_t kLongCallBytes = int64_t(2) << 30;
 // Calls that move at least this many bytes stream their input past the MALL
 // (524288 x 2048 BF16, 4 GiB: 639 against 659 us; below 1 GiB streaming loads
 // cost 1-3%).
@@ -410,7 +417,7 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
         // workgroup per row group kept memory streaming better (524288 x 2048
         // BF16: 659 against 909 us).
         int gp = G, vp = V;
-        if (auto_shape && !pick_shape(kShapesPersistent, nw_max, fixG, fixV, gp, vp)) return SM_ERR_PLAN;
+        if (auto_shape && !pick_shape(kShapes, nw_max, fixG, fixV, gp, vp)) return SM_ERR_PLAN;
         const int gpb = row_block(gp) / gp;
         const int occ = std::max(1, dev.occ_row(dev.ctx, p.dtype, gp, vp, prefetch_for(gp, vp)));
         slots = (int64_t)occ * dev.cus;
@@ -418,14 +425,16 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
             plan = SM_PLAN_PERSISTENT;
             G = gp;
             V = vp;
-        } else if (auto_shape && !pick_shape(kShapesResident, nw_max, fixG, fixV, G, V)) {
+        } else if (auto_shape && !pick_shape(kShapes, nw_max, fixG, fixV, G, V)) {
             return SM_ERR_PLAN;
         }
-    } else if (auto_shape) {
-        const bool ok = plan == SM_PLAN_PERSISTENT
-                            ? pick_shape(kShapesPersistent, nw_max, fixG, fixV, G, V)
-                            : pick_shape(kShapesResident, nw_max, fixG, fixV, G, V);
-        if (!ok) return SM_ERR_PLAN;
+    } else if (auto_shape && !pick_shape(kShapes, nw_max, fixG, fixV, G, V)) {
+        return SM_ERR_PLAN;
+    }
+    if (plan == SM_PLAN_RESIDENT && !fixG && !fixV && G == 128 && V == 2 &&
+        p.dtype != SM_F32 && model >= kLongCallBytes) {
+        G = 256;
+        V = 1;
     }
     if (!built_shape(G, V, 0) || (int64_t)G * V < nw_max) return SM_ERR_PLAN;
     const int block = row_block(G);

@@ -103,7 +103,12 @@ def test_plan_rule_one_pass_shapes():
         (4096, 4096, BF16): (256, 2, "persistent"),   # 4096 groups = 2 rounds of 2048
         (8192, 4096, F16): (256, 2, "resident"),      # 8192 groups: 4 rounds
         (8192, 8192, F16): (256, 4, "resident"),
-        (524288, 2048, BF16): (256, 2, "resident"),    # many rows: the resident table
+        (524288, 2048, BF16): (256, 1, "resident"),    # 16-bit, 4 GiB: one vector per lane
+        (262144, 2048, BF16): (256, 1, "resident"),    # exactly 2 GiB
+        (262143, 2048, BF16): (128, 2, "resident"),    # one row short of 2 GiB
+        (65536, 2048, BF16): (128, 2, "resident"),
+        (262144, 1024, F32): (128, 2, "resident"),     # FP32 keeps 128 x 2 at 2 GiB
+        (16384, 1024, F32): (128, 2, "resident"),
         (128, 781, F32): (128, 2, "persistent"),      # 3124-byte rows: 196 windows
         (16, 8192, F32): (512, 4, "persistent"),
     }
@@ -236,9 +241,14 @@ def test_plan_forcing_and_limits():
     rc, p = plan(100, 40000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
     assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (1024, 8)
     rc, p = plan(100, 2000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
-    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 2)   # resident table
+    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (128, 2)   # one table for both plans
     rc, p = plan(100, 2000, BF16, {"plan": sm.SM_PLAN_PERSISTENT})
-    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (128, 2)   # persistent table
+    assert (p["lanes_per_row"], p["vecs_per_lane"]) == (128, 2)
+    # the 16-bit long-call shape applies to automatic shapes only
+    rc, p = plan(524288, 2048, BF16, {"lanes_per_row": 128})
+    assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (128, 2)
+    rc, p = plan(524288, 2048, BF16, {"plan": sm.SM_PLAN_PERSISTENT})
+    assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (128, 2)
     rc, p = plan(100, 70000, BF16, {"plan": sm.SM_PLAN_RESIDENT})
     assert rc == PLAN
     rc, p = plan(100, 500, BF16, {"plan": 9})

@@ -123,3 +123,55 @@ def test_rotating_timing_interleaves_the_calls(monkeypatch):
     assert len(flushes) == len(log) == 18
     assert [s["n"] for s in st] == [4, 4, 4]
     assert st[0]["mean_us"] == pytest.approx(2.5)
+
+
+def _counter_csv(path, dispatches, counter):
+    """A rocprofv3 --pmc CSV with the columns the bench reads: (kernel, value) per dispatch."""
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_ALL)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (k, v) in enumerate(dispatches, 1):
+            w.writerow([i, k, counter, v])
+
+
+def test_traffic_table_groups_calls_at_cache_sweeps(tmp_path):
+    """The cache-sweep dispatches cut the library's kernels into calls; other kernels are
+    ignored; the copy of known size scales each counter; launch counts are checked."""
+    sweep, copy = "void smx::k_sweep_read16(uint4 const*, long)", "void smx::k_copy16<false>(x)"
+    fwd, wide_a, wide_b = "void smx::k_softmax_rows<2>(a)", "void smx::k_wide_stats(b)", "void smx::k_wide_norm(c)"
+    mib = 1024.0  # KiB
+    man = {"copy_bytes": 64 << 20, "calls": [
+        {"op": "copy", "bytes": 64 << 20, "launches": 1},
+        {"workload": "w", "op": "forward", "plan": "auto", "resolved": "resident", "G": 256, "V": 2,
+         "cpw": 0, "grid": 4096, "model_bytes": 64 << 20, "launches": 1},
+        {"op": "setup", "workload": "w", "launches": None},
+        {"workload": "w", "op": "backward", "plan": "wide", "resolved": "wide", "G": 0, "V": 0,
+         "cpw": 2, "grid": 2048, "model_bytes": 96 << 20, "launches": 2}]}
+    # FETCH_SIZE reads half on the copy, as on the hardware; torch kernels in between
+    fetch = [(sweep, 1e6), (copy, 16 * mib), ("void at::native::fill(x)", 5.0), (sweep, 1e6),
+             (fwd, 16.5 * mib), (sweep, 1e6), (fwd, 3.0), (sweep, 1e6), (sweep, 1e6),
+             (wide_a, 16 * mib), (wide_b, 16 * mib)]
+    write = [(sweep, 0), (copy, 32 * mib), (sweep, 0), (fwd, 32 * mib), (sweep, 0), (fwd, 1.0),
+             (sweep, 0), (wide_a, 0.0), (wide_b, 32 * mib)]
+    for name, rows, ctr in (("f.csv", fetch, "FETCH_SIZE"), ("w.csv", write, "WRITE_SIZE")):
+        _counter_csv(tmp_path / name, rows, ctr)
+    with open(tmp_path / "m.json", "w") as f:
+        json.dump(man, f)
+    t = bench.traffic_table(str(tmp_path / "m.json"), str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    rows = [r for r in t.splitlines() if r.startswith("| w ")]
+    assert len(rows) == 2
+    fwd_cells = [c.strip() for c in rows[0].strip("|").split("|")]
+    bwd_cells = [c.strip() for c in rows[1].strip("|").split("|")]
+    assert fwd_cells[1:3] == ["forward", "auto"] and bwd_cells[1:3] == ["backward", "wide"]
+    # forward: 33 MiB fetched (x2 scale) + 32 MiB written over 64 MiB algorithmic
+    assert float(fwd_cells[8]) == pytest.approx(65 / 64, abs=1e-3)
+    # backward: 2 x 32 MiB fetched + 32 MiB written = the 96 MiB model
+    assert float(bwd_cells[8]) == pytest.approx(1.0, abs=1e-3)
+    assert "FETCH_SIZE x 2.00000" in t
+    # a call whose kernel count differs from its plan's launch count is refused
+    man["calls"][3]["launches"] = 1
+    with open(tmp_path / "m.json", "w") as f:
+        json.dump(man, f)
+    with pytest.raises(RuntimeError, match="dispatches"):
+        bench.traffic_table(str(tmp_path / "m.json"), str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))

@@ -701,6 +701,14 @@ constexpr RowShape kShapesBwd[] = {{16, 1},  {32, 1},  {64, 1},  {64, 2},   {128
 // FP16 8192 x 4096 31.3 against 32.4 us, 8192 x 8192 59.7 against 63.7 us,
 // BF16 524288 x 2048 1035 against 1359 us.
 
+// One-pass backward rows stream y and dy past the MALL from this much traffic up:
+// two inputs per output made the streaming loads pay much earlier than in the
+// forward (cold, MI355X, dx identical: 65536 x 2048 BF16 (768 MiB) 110.6 against
+// 127.2 us; 16384 x 4096 BF16 (384 MiB) 56.7 against 60.5; 4096 x 4096 BF16 (96
+// MiB) 16.8 against 17.0; 2048 x 4096 BF16 (48 MiB) 9.85 against 10.0; at 24 MiB
+// -1.8% to +1.2%).
+constexpr int64_t kBwdNtLoadBytes = int64_t(32) << 20;
+
 int occ_bwd_live(int dtype, int G, int V) {
     BwdRowKernelFn fn = bwd_row_kernel(dtype, G, V, 0);
     return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
@@ -792,7 +800,7 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
     const int occ = live ? std::max(1, occ_bwd_live(p.dtype, G, V)) : std::max(1, 2048 / block);
     const int64_t slots = (int64_t)occ * cus;
     const int64_t model = 3 * p.M * p.N * es;
-    const bool want_nt = o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes);
+    const bool want_nt = o.nontemporal == 1 || (o.nontemporal == 0 && model >= kBwdNtLoadBytes);
     int64_t grid = o.grid > 0 ? o.grid : (plan == SM_PLAN_PERSISTENT ? slots : groups);
     grid = std::max<int64_t>(1, std::min<int64_t>(std::min(grid, groups),
                                                   kMaxThreadsPerLaunch / block));
@@ -929,6 +937,12 @@ int validate_rms(const RmsProblem& p) {
 
 constexpr int64_t kRmsTwoLaunchSlices = 64;
 
+// One-pass RMSNorm rows stream x and the residual past the MALL from the MALL's
+// size of traffic up (cold, MI355X, y identical: 65536 x 2048 BF16 (768 MiB)
+// 114.1 against 128.4 us; 16384 x 4096 FP16 (384 MiB) 59.8 against 60.1; 4096 x
+// 4096 BF16 (96 MiB) 18.7 against 18.5; 24-48 MiB within 0.2%).
+constexpr int64_t kRmsNtLoadBytes = int64_t(256) << 20;
+
 int occ_rms_live(int dtype, int G, int V) {
     RmsRowKernelFn fn = rms_row_kernel(dtype, G, V, 0);
     return fn ? occ_of(reinterpret_cast<const void*>(fn), row_block(G)) : 1;
@@ -1021,7 +1035,7 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
     pi->plan = plan;
     pi->lanes_per_row = G;
     pi->vecs_per_lane = V;
-    pi->nt_loads = ((o.nontemporal == 1 || (o.nontemporal == 0 && model >= kNtLoadBytes)) && G >= 128) ? 1 : 0;
+    pi->nt_loads = ((o.nontemporal == 1 || (o.nontemporal == 0 && model >= kRmsNtLoadBytes)) && G >= 128) ? 1 : 0;
     pi->block = block;
     pi->grid = grid;
     pi->launches = 1;

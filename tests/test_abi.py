@@ -297,8 +297,16 @@ def test_backward_plan_rule():
     rc, p = q(4096, 4096, BF16)
     assert rc == OK and (p["lanes_per_row"], p["vecs_per_lane"]) == (256, 2)
     assert p["model_bytes"] == 3 * 4096 * 4096 * 2 and p["plan_name"] == "resident"
-    assert p["grid"] == 4096 and p["nt_loads"] == 0
+    assert p["grid"] == 4096 and p["nt_loads"] == 1  # 96 MiB moved: streaming loads
     assert p["dy_same_phase"] == 1 and p["same_phase"] == 1
+    # one-pass backward rows stream from 32 MiB of traffic up, on 128- to 1024-lane rows
+    for (M, N, dt), nt in {(1024, 4096, BF16): 0, (1366, 4096, BF16): 1, (1365, 4096, BF16): 0,
+                           (4096, 1024, BF16): 0, (2048, 4096, BF16): 1}.items():
+        rc, p = q(M, N, dt)
+        assert rc == OK and p["nt_loads"] == nt, (M, N, p)
+        assert p["nt_loads"] == (1 if 3 * M * N * 2 >= 32 << 20 and p["lanes_per_row"] >= 128 else 0)
+    rc, p = q(4096, 4096, BF16, {"nontemporal": -1})
+    assert p["nt_loads"] == 0
     rc, p = q(524288, 2048, BF16)  # 6 GiB moved: streaming loads
     assert rc == OK and p["plan_name"] == "resident" and p["nt_loads"] == 1
     rc, p = q(4096, 4096, BF16, {"plan": 2})
@@ -387,6 +395,15 @@ def test_rmsnorm_plan_rule():
     assert rc == PLAN                   # rows hold at most 4 vectors per lane
     rc, p = rms_q(8, 1000, F16, r=R + 2)  # residual at another 16-byte phase
     assert p["dy_same_phase"] == 0
+    # one-pass rows stream x and the residual from 256 MiB of traffic up (128+ lanes)
+    rc, p = rms_q(16384, 4096, F16)     # 384 MiB
+    assert p["plan_name"] == "resident" and p["nt_loads"] == 1
+    rc, p = rms_q(4096, 4096, BF16)     # 96 MiB
+    assert p["nt_loads"] == 0
+    rc, p = rms_q(4096, 4096, BF16, {"nontemporal": 1})
+    assert p["nt_loads"] == 1
+    rc, p = rms_q(16384, 4096, F16, {"nontemporal": -1})
+    assert p["nt_loads"] == 0
 
 
 # ------------------------------------------------------------------ fused attention

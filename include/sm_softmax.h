@@ -115,9 +115,11 @@ typedef struct sm_softmax_opts {
     int chunks_per_wave; /* WIDE: 1024-element chunks per wave; 0 = auto */
     int prefetch;        /* PERSISTENT: 1 = load the next row early, -1 = no; 0 = auto */
     int nontemporal;     /* streaming (nontemporal) loads of the input: 1 = yes, -1 = no,
-                            0 = auto (yes when the call moves at least 1 GiB, four times the
-                            MI355X MALL); one-pass plans have them on 128- to 1024-lane
-                            rows without prefetch, the WIDE plan on both passes */
+                            0 = auto: yes when the call moves at least 1 GiB (four times
+                            the MI355X MALL) in the forward and in SPLIT and WIDE plans,
+                            32 MiB in one-pass backward rows, 256 MiB in one-pass RMSNorm
+                            rows; one-pass plans have them on 128- to 1024-lane rows
+                            without prefetch, the WIDE plan on both passes */
     int spin_limit;      /* SPLIT: polls a workgroup may spend waiting for the other
                             slices of a row; 0 = default (2^20, about a second) */
     /* Optional timing events (created by the caller with hipEventCreate), or NULL.

@@ -231,6 +231,9 @@ __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigne
 // Workgroup shape: rows that fit in a wave share 256-thread workgroups (several
 // row groups per workgroup, no barriers); a row spread over several waves gets
 // a workgroup of exactly its G lanes, so its barriers are uniform.
+// XCDs of an MI355X; the workgroups of a launch are dealt to them in turn.
+constexpr int kXcds = 8;
+
 template <int G>
 struct RowLaunch {
     static constexpr int block = G > 64 ? G : 256;
@@ -241,7 +244,7 @@ struct RowLaunch {
 template <int DT, int G, int V, bool PF, bool NT>
 __global__ void __launch_bounds__(RowLaunch<G>::block)
 k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, int64_t in_sb,
-               int64_t out_sb, int same_phase) {
+               int64_t out_sb, int same_phase, int xcd_order) {
     constexpr int GPB = RowLaunch<G>::groups;
     constexpr int NW = G > 64 ? G / 64 : 1;
     __shared__ float lds_a[NW], lds_b[NW], lds_c[NW];
@@ -250,7 +253,16 @@ k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, in
     const int lane = (GPB == 1) ? tid : (tid % G);
     const int grp = (GPB == 1) ? 0 : (tid / G);
     const int64_t rstep = (int64_t)gridDim.x * GPB;
-    int64_t row = (int64_t)blockIdx.x * GPB + grp;
+    // Workgroups are dealt to the XCDs in turn. With xcd_order they are renumbered
+    // (a permutation of the grid) so that each XCD takes a contiguous range of row
+    // groups: rows that share a cache line at their boundary then meet in one L2.
+    int64_t b = blockIdx.x;
+    if (xcd_order) {
+        const int64_t bx = b % kXcds, bj = b / kXcds;
+        const int64_t bq = (int64_t)gridDim.x / kXcds, br = (int64_t)gridDim.x % kXcds;
+        b = bx < br ? bx * (bq + 1) + bj : br * (bq + 1) + (bx - br) * bq + bj;
+    }
+    int64_t row = b * GPB + grp;
 
     uint4 cur[V];
     load_row<DT, G, V, NT>(cur, in, row, M, N, in_sb, lane);

@@ -7,7 +7,7 @@
 namespace smx {
 
 using RowKernelFn = void (*)(const unsigned char*, unsigned char*, int64_t, int, int64_t, int64_t,
-                             int);
+                             int, int);
 using StatsKernelFn = void (*)(const unsigned char*, float2*, int64_t, int, int64_t, int, int64_t);
 using NormKernelFn = void (*)(const unsigned char*, unsigned char*, const float2*, int64_t, int,
                               int64_t, int64_t, int, int64_t, int);

@@ -239,7 +239,8 @@ __device__ __forceinline__ void decode_words(const uint32_t (&w)[4], float (&f)[
 template <int DT, int G, int V, bool NT>
 __global__ void __launch_bounds__(RowLaunch<G>::block)
 k_softmax_bwd_rows(const unsigned char* y, const unsigned char* dy, unsigned char* dx, int64_t M,
-                   int N, int64_t y_sb, int64_t dy_sb, int64_t dx_sb, int dy_phase, int dx_phase) {
+                   int N, int64_t y_sb, int64_t dy_sb, int64_t dx_sb, int dy_phase, int dx_phase,
+                   int xcd_order) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int GPB = RowLaunch<G>::groups;
     constexpr int NW = G > 64 ? G / 64 : 1;
@@ -252,7 +253,7 @@ k_softmax_bwd_rows(const unsigned char* y, const unsigned char* dy, unsigned cha
     const int grp = (GPB == 1) ? 0 : (tid / G);
     const int64_t rstep = (int64_t)gridDim.x * GPB;
     int parity = 0;
-    for (int64_t row = (int64_t)blockIdx.x * GPB + grp; row < M; row += rstep, parity ^= 1) {
+    for (int64_t row = xcd_block(xcd_order) * GPB + grp; row < M; row += rstep, parity ^= 1) {
         const RowGeom<DT> g(y + row * y_sb, N);
         uint32_t ry[V][4], rd[V][4];
 #pragma unroll

@@ -234,6 +234,19 @@ __device__ __forceinline__ void process_row(const uint4 (&raw)[V], const unsigne
 // XCDs of an MI355X; the workgroups of a launch are dealt to them in turn.
 constexpr int kXcds = 8;
 
+// This workgroup's index, or with xcd_order a permutation of the grid under which
+// each XCD takes a contiguous range of indices: rows that share a cache line at
+// their boundary then meet in one L2.
+__device__ __forceinline__ int64_t xcd_block(int xcd_order) {
+    int64_t b = blockIdx.x;
+    if (xcd_order) {
+        const int64_t bx = b % kXcds, bj = b / kXcds;
+        const int64_t bq = (int64_t)gridDim.x / kXcds, br = (int64_t)gridDim.x % kXcds;
+        b = bx < br ? bx * (bq + 1) + bj : br * (bq + 1) + (bx - br) * bq + bj;
+    }
+    return b;
+}
+
 template <int G>
 struct RowLaunch {
     static constexpr int block = G > 64 ? G : 256;
@@ -253,16 +266,7 @@ k_softmax_rows(const unsigned char* in, unsigned char* out, int64_t M, int N, in
     const int lane = (GPB == 1) ? tid : (tid % G);
     const int grp = (GPB == 1) ? 0 : (tid / G);
     const int64_t rstep = (int64_t)gridDim.x * GPB;
-    // Workgroups are dealt to the XCDs in turn. With xcd_order they are renumbered
-    // (a permutation of the grid) so that each XCD takes a contiguous range of row
-    // groups: rows that share a cache line at their boundary then meet in one L2.
-    int64_t b = blockIdx.x;
-    if (xcd_order) {
-        const int64_t bx = b % kXcds, bj = b / kXcds;
-        const int64_t bq = (int64_t)gridDim.x / kXcds, br = (int64_t)gridDim.x % kXcds;
-        b = bx < br ? bx * (bq + 1) + bj : br * (bq + 1) + (bx - br) * bq + bj;
-    }
-    int64_t row = b * GPB + grp;
+    int64_t row = xcd_block(xcd_order) * GPB + grp;
 
     uint4 cur[V];
     load_row<DT, G, V, NT>(cur, in, row, M, N, in_sb, lane);

@@ -33,7 +33,7 @@ inline RowKernelFn row_kernel(int dtype, int G, int V, int PF, int NT) {
 // Softmax backward (sm_bwd.hip): one-pass rows for G in {16 ... 1024}, V in
 // {1, 2, 4}; two-pass wide rows.
 using BwdRowKernelFn = void (*)(const unsigned char*, const unsigned char*, unsigned char*, int64_t,
-                                int, int64_t, int64_t, int64_t, int, int);
+                                int, int64_t, int64_t, int64_t, int, int, int);
 using BwdDotKernelFn = void (*)(const unsigned char*, const unsigned char*, float2*, int64_t, int,
                                 int64_t, int64_t, int, int64_t, int);
 using BwdApplyKernelFn = void (*)(const unsigned char*, const unsigned char*, unsigned char*,

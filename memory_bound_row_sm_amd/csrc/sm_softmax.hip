@@ -587,6 +587,13 @@ hipError_t launch_k(const void* fn, dim3 grid, dim3 block, hipStream_t s, hipEve
     return hipLaunchKernel(fn, grid, block, argv, 0, s);
 }
 
+// Whether a one-pass launch renumbers its workgroups XCD-contiguously: resident
+// rows that own their workgroup (128 lanes and up) and share cache lines with
+// their neighbours (a row stride that is not a whole number of 128-byte lines).
+int xcd_order(const sm_plan_info& pi, bool rows_share_lines) {
+    return (pi.plan == SM_PLAN_RESIDENT && pi.lanes_per_row > 64 && rows_share_lines) ? 1 : 0;
+}
+
 int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_opts& o,
            hipStream_t stream) {
     const hipEvent_t ev0 = o.start_event, ev1 = o.stop_event;
@@ -623,13 +630,15 @@ int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_
     RowKernelFn fn =
         row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.prefetch, pi.nt_loads);
     if (!fn) return SM_ERR_PLAN;
-    // Resident rows whose stride is not a whole number of 128-byte lines share a
-    // line with the next row: XCD-contiguous order lets one L2 merge both halves of
-    // it (cold, MI355X: 524288 x 2000 BF16 691 against 764 us, 131072 x 2000 172
-    // against 194 us, 16384 x 4000 38.4 against 38.9 us); on line-aligned rows
-    // (524288 x 2048: 649 against 636 us) and persistent grids (8192 x 1000 FP16:
-    // 9.8 against 6.9 us) the hardware's order was faster.
-    const int xcd = (pi.plan == SM_PLAN_RESIDENT && (isb % 128 != 0 || osb % 128 != 0)) ? 1 : 0;
+    // Resident rows of their own workgroup whose stride is not a whole number of
+    // 128-byte lines share a line with the next row: XCD-contiguous order lets one
+    // L2 merge both halves of it (cold, MI355X: 524288 x 2000 BF16 691 against 764
+    // us, 131072 x 2000 172 against 194 us, 16384 x 4000 38.4 against 38.9 us); on
+    // line-aligned rows (524288 x 2048: 649 against 636 us), persistent grids (8192
+    // x 1000 FP16: 9.8 against 6.9 us) and rows that share a workgroup (whose
+    // consecutive rows already meet in one L2) the hardware's order was as fast or
+    // faster.
+    const int xcd = xcd_order(pi, isb % 128 != 0 || osb % 128 != 0);
     e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(pi.block), stream,
                  ev0, ev1, in, out, p.M, N, isb, osb, (int)pi.same_phase, xcd);
     return e == hipSuccess ? SM_OK : hip_fail(e);
@@ -860,9 +869,13 @@ int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, const sm_s
     }
     BwdRowKernelFn fn = bwd_row_kernel(p.dtype, pi.lanes_per_row, pi.vecs_per_lane, pi.nt_loads);
     if (!fn) return SM_ERR_PLAN;
+    // XCD-contiguous order as in the forward (262144 x 2000 BF16 526 against 596 us,
+    // 65536 x 2000 114 against 122 us; 64-lane rows 65536 x 1000 FP16 65.2 against
+    // 61.7 us: not for rows that share a workgroup)
+    const int xcd = xcd_order(pi, ysb % 128 != 0 || dysb % 128 != 0 || dxsb % 128 != 0);
     e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(pi.block), stream,
                  ev0, ev1, y, dy, dx, p.M, N, ysb, dysb, dxsb, (int)pi.dy_same_phase,
-                 (int)pi.same_phase);
+                 (int)pi.same_phase, xcd);
     return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 

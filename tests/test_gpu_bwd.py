@@ -77,6 +77,16 @@ def test_phase_shifted_and_strided(dt, plan):
         assert torch.isnan(bx[ox + M * sx:].float()).all()
 
 
+@pytest.mark.parametrize("M,N,dt", [(1, 1500, "f16"), (9, 2000, "bf16"), (1001, 1500, "f16"),
+                                     (4099, 2000, "bf16"), (2053, 1000, "f32"), (517, 4000, "bf16")])
+def test_resident_rows_sharing_lines(M, N, dt):
+    """Resident backward rows of 128+ lanes whose stride is not a whole number of
+    128-byte lines run in XCD-contiguous order: every row written as the oracle says."""
+    y, dy = inputs(M, N, dt, seed=M + N)
+    g = run_bwd(y.to(DEV), dy.to(DEV), "resident")
+    compare_bwd(g, y, dy, what=f"bwd {dt} {M}x{N} resident, XCD-contiguous order")
+
+
 @pytest.mark.parametrize("plan", ["resident", "persistent", "wide", "split"])
 def test_in_place(plan):
     for M, N in [(33, 4096), (5, 20000)]:

@@ -177,12 +177,13 @@ def test_misaligned_strided_and_phase_shifted(dt, plan):
         assert torch.isnan(ob[off_out + M * stride_out:].float()).all()
 
 
-@pytest.mark.parametrize("M,N,dt", [(1, 1000, "f16"), (7, 1000, "f16"), (8, 2000, "bf16"),
-                                     (9, 2000, "bf16"), (1001, 1000, "f16"), (4099, 2000, "bf16"),
-                                     (2053, 100, "f32"), (517, 4000, "bf16")])
+@pytest.mark.parametrize("M,N,dt", [(1, 1500, "f16"), (7, 1500, "f16"), (8, 2000, "bf16"),
+                                     (9, 2000, "bf16"), (1001, 1500, "f16"), (4099, 2000, "bf16"),
+                                     (2053, 1000, "f32"), (517, 4000, "bf16"), (300, 1000, "f16")])
 def test_resident_rows_sharing_lines(M, N, dt):
-    """Resident rows whose stride is not a whole number of 128-byte lines run in
-    XCD-contiguous order (the workgroups renumbered by a permutation): every row,
+    """Resident rows of 128+ lanes whose stride is not a whole number of 128-byte
+    lines run in XCD-contiguous order (the workgroups renumbered by a permutation;
+    the last case, 64-lane rows, keeps the hardware's order): every row,
     row group and grid size (multiple of the XCD count or not) is written exactly as
     the oracle says, and nothing else is."""
     x = _rand(M, N, dt, seed=M + N)

@@ -30,7 +30,8 @@ enum RmsFlags : int {
     kRmsResPhase = 2,  // r rows share x rows' 16-byte phase (vector loads)
     kRmsOutPhase = 4,  // y rows share x rows' phase (16-byte stores)
     kRmsSumOut = 8,    // write s
-    kRmsSumPhase = 16  // s rows share x rows' phase
+    kRmsSumPhase = 16,  // s rows share x rows' phase
+    kRmsXcdOrder = 32   // one-pass rows: workgroups renumbered XCD-contiguously
 };
 
 // Store one encoded window of a row (16-byte when inside the row and in phase,
@@ -162,7 +163,7 @@ k_rmsnorm_rows(const unsigned char* x, const unsigned char* r, const unsigned ch
     const int grp = (GPB == 1) ? 0 : (tid / G);
     const int64_t rstep = (int64_t)gridDim.x * GPB;
     int parity = 0;
-    for (int64_t row = (int64_t)blockIdx.x * GPB + grp; row < M; row += rstep, parity ^= 1) {
+    for (int64_t row = xcd_block(flags & kRmsXcdOrder) * GPB + grp; row < M; row += rstep, parity ^= 1) {
         const unsigned char* xrow = x + row * x_sb;
         const RowGeom<DT> g(xrow, N);
         uint32_t rs[V][4], rw[V][4];

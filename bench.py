@@ -627,7 +627,7 @@ def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
     import oracle
     import workloads
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from parity import compare
+    from parity import compare, rel_thr_bound
     s = workloads.storage_numpy(x_cpu)
     threads = oracle.max_threads()
     oracle.softmax_f64(s, "bf16", threads=threads)  # warm-up
@@ -650,6 +650,11 @@ def cpu_baseline(x_cpu, gpu_out, model_bytes: int, budget_s: float, log):
     log(f"[bench] cpu oracle: {res}")
     try:
         parity = {"passed": True, **compare(gpu_out, x_cpu, what="bench output")}
+        # the thresholded relative error (|y| > 1e-3) is gated as well: one rounding
+        # plus the one-ulp neighbour, 2^-6 relative in BF16
+        parity["max_rel_thr_bound"] = rel_thr_bound("bf16")
+        if parity["max_rel_thr"] > parity["max_rel_thr_bound"]:
+            parity["passed"] = False
     except AssertionError as e:
         parity = {"passed": False, "error": str(e)[:500]}
     log(f"[bench] oracle parity: {parity}")

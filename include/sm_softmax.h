@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SM_SOFTMAX_VERSION 10100 /* 1.1.0 */
+#define SM_SOFTMAX_VERSION 10200 /* 1.2.0 */
 
 typedef enum sm_dtype { SM_F32 = 0, SM_F16 = 1, SM_BF16 = 2 } sm_dtype;
 
@@ -88,9 +88,20 @@ typedef enum sm_status {
  *                 (further rows are taken in rounds), so a row's slices are
  *                 resident together unless the device is filled by other
  *                 work; more than two SPLIT calls running at once on different
- *                 streams of one device can exceed it. A wait that exceeds
- *                 spin_limit polls writes NaN over its slice and is counted
- *                 (sm_softmax_sync_failures), so every call ends.
+ *                 streams of one device can exceed it. Every wait is bounded
+ *                 (spin_limit polls), so every call ends. A wait that runs out
+ *                 is counted (sm_softmax_sync_failures); out of place, its
+ *                 workgroup then reads the whole input row for the row's
+ *                 maximum and sum itself, so the output is the softmax whatever
+ *                 the scheduling; in place (out == in), where the row's other
+ *                 slices may already have overwritten their input, it writes
+ *                 NaN over its slice.
+ * Graph capture: a SPLIT call tags its exchange with an id fixed at launch, which
+ * a graph would replay unchanged. On a stream that is capturing, AUTO therefore
+ * takes WIDE where it would take SPLIT, and a forced SPLIT returns SM_ERR_PLAN
+ * (the same holds for the backward; the RMSNorm call takes its two-launch form).
+ * sm_softmax_plan_query reports the plan of a call on a stream that is not
+ * capturing.
  * AUTO takes SPLIT for N > 8192 when a row's slices fit the resident capacity
  * (WIDE otherwise). For N <= 8192 it holds the row in the narrowest
  * measured-best group (16 to 1024 lanes, 1 to 8 vectors per lane), and takes
@@ -164,11 +175,14 @@ typedef struct sm_plan_info {
  *   in_stride,
  *   out_stride  : row strides in elements, >= N when M > 1
  *   dtype       : sm_dtype of both tensors
- * The WIDE and SPLIT plans take their scratch stream-ordered from the device's
- * default memory pool (hipMallocAsync / hipFreeAsync on `stream`), so
- * concurrent calls on different streams never share scratch. The first SPLIT
- * call on a stream also allocates that stream's failure counter (hipMalloc +
- * hipMemset of 256 bytes, kept until the process ends).
+ * The WIDE and SPLIT plans take their scratch stream-ordered (hipMallocFromPoolAsync
+ * / hipFreeAsync on `stream`) from a memory pool the library creates for the device
+ * and keeps until the process ends (its release threshold keeps freed blocks for
+ * later calls; the device's default pool is not modified), so concurrent calls on
+ * different streams never share scratch; on a stream that is capturing a graph, from
+ * hipMallocAsync (a graph memory node). The first SPLIT call on a stream also
+ * allocates that stream's failure counter (hipMalloc + hipMemset of 256 bytes, kept
+ * until the process ends).
  * Returns SM_OK or a negative sm_status.
  */
 int sm_softmax_fwd(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,
@@ -210,9 +224,14 @@ int sm_softmax_plan_query(const void *in, const void *out, int64_t M, int64_t N,
  *                 overlap each other: both are only read)
  *   strides     : row strides in elements, >= N when M > 1
  * Plans as for the forward call: one-pass RESIDENT/PERSISTENT for N <= 8192
- * (3*M*N*elem bytes); WIDE above, in two passes (a partial dot per wave, then
- * merge and apply: 5*M*N*elem bytes) with stream-ordered scratch of
- * M * waves_per_row * 8 bytes, or caller workspace through the _ex form.
+ * (3*M*N*elem bytes); wider rows SPLIT (one launch, the slices' partial dots
+ * exchanged as the forward exchanges its (max, sum) pairs: 3*M*N*elem bytes; a
+ * wait that runs out is counted, and its workgroup then re-reads the row's y and
+ * dy for the dot when dx aliases neither, or writes NaN over its slice), or WIDE
+ * where a row's slices cannot be resident together or the stream is capturing a
+ * graph (two passes, a partial dot per wave, then merge and apply: 5*M*N*elem
+ * bytes). SPLIT and WIDE take stream-ordered scratch (M * slices * 32 or
+ * M * waves_per_row * 8 bytes), or caller workspace through the _ex form.
  * Returns SM_OK or a negative sm_status; validation as for sm_softmax_fwd.
  */
 int sm_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
@@ -256,8 +275,12 @@ int sm_softmax_bwd_plan_query(const void *y, const void *dy, const void *dx, int
  * RESIDENT/PERSISTENT rows (up to 4 vectors per lane), SPLIT for wide rows (one
  * launch, partial sums of squares exchanged between the row's workgroups), and
  * WIDE as two launches of the split kernel (publish, then gather and apply) when
- * a row's slices cannot be resident together, or when rows need more than 32
- * slices and several rounds (measured faster). model_bytes counts the compulsory
+ * a row's slices cannot be resident together, when rows need more than 64
+ * slices and several rounds (measured faster), or on a stream that is capturing a
+ * graph. A SPLIT wait that runs out is counted as for the softmax; the workgroup
+ * then re-reads its row's x (and residual) for the sum of squares when neither y
+ * nor residual_out aliases x or the residual, and writes NaN over its slice
+ * otherwise. model_bytes counts the compulsory
  * HBM bytes: x, y and, when present, the residual and residual_out once per element,
  * w once (N elements); WIDE reads x and the residual twice. (The pages' requested-
  * byte convention counts w once per row in addition.)
@@ -334,8 +357,9 @@ int sm_softmax_last_hip_error(void);
 
 /*
  * SPLIT-plan waits that ran out of polls on `stream` since its counter was
- * created (each wrote NaN over one row slice). Synchronises `stream`, then
- * reads the count into *count (0 if no SPLIT call ran on that stream).
+ * created (each one re-read its whole input row, or, in place, wrote NaN over
+ * its row slice). Synchronises `stream`, then reads the count into *count (0 if
+ * no SPLIT call ran on that stream).
  * Returns SM_OK, SM_ERR_INVALID for a NULL count, or SM_ERR_HIP.
  */
 int sm_softmax_sync_failures(hipStream_t stream, unsigned int *count);

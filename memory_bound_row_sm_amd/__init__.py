@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = (
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsm_softmax.so")
-ABI_VERSION = 10100  # SM_SOFTMAX_VERSION of the signatures declared below
+ABI_VERSION = 10200  # SM_SOFTMAX_VERSION of the signatures declared below
 
 
 class SmOpts(ctypes.Structure):

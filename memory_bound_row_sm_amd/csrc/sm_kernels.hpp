@@ -34,7 +34,9 @@ struct RowGeom {
         const uintptr_t a = reinterpret_cast<uintptr_t>(row);
         head = (int)((a & 15u) / ES);
         base = row - (a & 15u);
-        nwin = (head + N + E - 1) / E;
+        // head + N + E - 1 exceeds INT32_MAX for N within 14 of it: sum in 64 bits
+        // (the quotient, at most 2^30 + 4, fits)
+        nwin = (int)(((int64_t)head + N + E - 1) / E);
     }
 };
 

@@ -44,10 +44,10 @@ BwdRowKernelFn bwd_row_kernel(int dtype, int G, int V, int NT);
 // One-launch split kernels (sm_split.hip): 256-lane workgroups, one row slice
 // each; the slot and sync pointers are SplitSlot* and SplitSync*.
 using SplitKernelFn = void (*)(const unsigned char*, unsigned char*, void*, void*, int64_t, int,
-                               int64_t, int64_t, int, int, uint32_t, int, int);
+                               int64_t, int64_t, int, int, uint32_t, int, int, int);
 using BwdSplitKernelFn = void (*)(const unsigned char*, const unsigned char*, unsigned char*, void*,
                                   void*, int64_t, int, int64_t, int64_t, int64_t, int, int,
-                                  uint32_t, int, int, int);
+                                  uint32_t, int, int, int, int);
 SplitKernelFn split_kernel(int dtype, int V, int NT);
 BwdSplitKernelFn bwd_split_kernel(int dtype, int V, int NT);
 

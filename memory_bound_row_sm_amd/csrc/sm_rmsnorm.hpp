@@ -31,7 +31,9 @@ enum RmsFlags : int {
     kRmsOutPhase = 4,  // y rows share x rows' phase (16-byte stores)
     kRmsSumOut = 8,    // write s
     kRmsSumPhase = 16,  // s rows share x rows' phase
-    kRmsXcdOrder = 32   // one-pass rows: workgroups renumbered XCD-contiguously
+    kRmsXcdOrder = 32,  // one-pass rows: workgroups renumbered XCD-contiguously
+    kRmsRecompute = 64  // split: neither output aliases x or r, so a slice whose wait
+                        // ran out may re-read the whole row
 };
 
 // Store one encoded window of a row (16-byte when inside the row and in phase,
@@ -183,8 +185,35 @@ k_rmsnorm_rows(const unsigned char* x, const unsigned char* r, const unsigned ch
     }
 }
 
+// Split fallback after a wait ran out: the workgroup forms the row's whole sum of
+// squares from x (and r, rounded in as in the slices), 256 windows per step, and
+// returns it on every lane as (hi, lo).
+template <int DT, bool NT>
+__device__ __noinline__ void rms_row_sq(const RowGeom<DT> g, const unsigned char* rrow,
+                                        const unsigned char* wvec, const unsigned char* xrow, int N,
+                                        int flags, float* lds_hi, float* lds_lo, float& hi,
+                                        float& lo) {
+    constexpr int B = kSplitBlock;
+    float acc = 0.f;
+    CSum cs;
+    for (int64_t w = threadIdx.x; w < g.nwin; w += B) {
+        uint32_t rs[1][4], rw[1][4];
+        rms_load<DT, 1, NT>(rs, rw, g, rrow, wvec, xrow, N, w, 0, g.nwin, flags);
+        rms_lane_sq<DT, 1>(rs, acc, cs);
+    }
+    if constexpr (DT == kF32) {
+        cs = row_csum<B>(cs, lds_hi, lds_lo);
+    } else {
+        cs.hi = row_sum<B>(acc, lds_hi);
+        cs.lo = 0.f;
+    }
+    hi = cs.hi;
+    lo = cs.lo;
+}
+
 // mode 0: publish, wait for the row's slices, apply (one launch); mode 1: publish
-// only; mode 2: gather the partials published by an earlier launch and apply.
+// only; mode 2: gather the partials published by an earlier launch and apply (every
+// word already carries the tag, so no wait can run out; `sync` may be null).
 template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
 k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned char* wvec,
@@ -229,11 +258,17 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
         }
         split_gather_sum<DT == kF32>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
-        const bool ok = lds_stat[3] != 0.f;
+        const bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
         float rstd = rms_scale(lds_stat[1], lds_stat[2], N, eps);
         if (!ok) {
-            rstd = __builtin_nanf("");
-            if (lane == 0) atomicAdd(&sync->failures, 1u);
+            if (lane == 0 && sync) atomicAdd(&sync->failures, 1u);
+            if (flags & kRmsRecompute) {
+                float hi, lo;
+                rms_row_sq<DT, NT>(g, r + row * r_sb, wvec, xrow, N, flags, lds_hi, lds_lo, hi, lo);
+                rstd = rms_scale(hi, lo, N, eps);
+            } else {
+                rstd = __builtin_nanf("");
+            }
         }
         rms_store<DT, V>(rs, rw, rstd, y + row * y_sb, s_out + row * s_sb, g, N, w0, B, wend, flags);
         __syncthreads();  // lds_stat is rewritten by the next item's gather

@@ -313,7 +313,12 @@ int split_auto_v(int64_t M, int64_t nw, int vmin, int vmax, int vround, int64_t 
     return 0;
 }
 
-int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev, sm_plan_info* pi) {
+// no_split: the call is being captured into a graph. SPLIT tags its slots with a
+// per-call id fixed at launch, which a graph would replay unchanged, so a replay could
+// read the previous replay's statistics before its own peers publish: AUTO takes the
+// two-pass WIDE plan instead, and a forced SPLIT is refused.
+int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev, bool no_split,
+              sm_plan_info* pi) {
     *pi = sm_plan_info{};
     const int es = elem_bytes(p.dtype);
     const int E = 16 / es;
@@ -330,6 +335,10 @@ int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev,
     if (o.nontemporal < -1 || o.nontemporal > 1) return SM_ERR_PLAN;
     const bool f32 = p.dtype == SM_F32;
     int64_t wide_cpw = 0;  // preferred chunks per wave of an automatic WIDE plan (0: by the grid)
+    if (plan == SM_PLAN_SPLIT && no_split) {
+        if (!auto_plan) return SM_ERR_PLAN;
+        plan = SM_PLAN_WIDE;
+    }
 
     if (plan == SM_PLAN_SPLIT) {
         int64_t P = 0, grid = 0;
@@ -609,9 +618,12 @@ int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_
         SplitKernelFn fn = split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
         if (!fn) return SM_ERR_PLAN;
         const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
+        // out of place (validation admits only disjoint rows or exactly in place), a
+        // slice whose wait runs out can re-read its whole input row
+        const int recompute = p.in != p.out ? 1 : 0;
         e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
                      stream, ev0, ev1, in, out, ws, sync, p.M, N, isb, osb, (int)pi.waves_per_row,
-                     pi.slice_windows, next_tag(), spin, (int)pi.same_phase);
+                     pi.slice_windows, next_tag(), spin, (int)pi.same_phase, recompute);
         return e == hipSuccess ? SM_OK : hip_fail(e);
     }
     if (pi.plan == SM_PLAN_WIDE) {
@@ -644,17 +656,71 @@ int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_
     return e == hipSuccess ? SM_OK : hip_fail(e);
 }
 
-void keep_pool_memory(int dev) {
-    static std::mutex mu;
-    static std::map<int, bool> done;
-    std::lock_guard<std::mutex> lk(mu);
-    if (done[dev]) return;
-    done[dev] = true;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-        uint64_t thr = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+// ------------------------------------------------------------ scratch memory
+// WIDE and SPLIT scratch is taken stream-ordered from a memory pool the library
+// creates per device (kept until the process ends, with a release threshold that
+// keeps freed blocks for the next call), so repeated calls do not return memory to
+// the driver and the device's default pool is left as the application set it. Under
+// graph capture the allocation comes from hipMallocAsync (a graph memory node).
+std::mutex g_pool_mu;
+std::map<int, hipMemPool_t> g_pool;
+
+hipError_t scratch_pool(int dev, hipMemPool_t* out) {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    auto it = g_pool.find(dev);
+    if (it != g_pool.end()) {
+        *out = it->second;
+        return hipSuccess;
     }
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    hipError_t e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t thr = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    if (e != hipSuccess) {
+        (void)hipMemPoolDestroy(pool);
+        return e;
+    }
+    g_pool[dev] = pool;
+    *out = pool;
+    return hipSuccess;
+}
+
+// Whether `stream` is being captured into a graph (the legacy null stream cannot be,
+// and is not asked).
+hipError_t stream_capturing(hipStream_t stream, bool* capturing) {
+    *capturing = false;
+    if (!stream) return hipSuccess;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &st);
+    *capturing = e == hipSuccess && st == hipStreamCaptureStatusActive;
+    return e;
+}
+
+// Run `go(ws)` with stream-ordered scratch of `bytes` (released after the launches).
+template <class Go>
+int with_scratch(size_t bytes, bool capturing, hipStream_t stream, Go go) {
+    void* tmp = nullptr;
+    hipError_t e;
+    if (capturing) {
+        e = hipMallocAsync(&tmp, bytes, stream);
+    } else {
+        int dev = 0;
+        hipMemPool_t pool = nullptr;
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = scratch_pool(dev, &pool);
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&tmp, bytes, pool, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    int rc = go(tmp);
+    e = hipFreeAsync(tmp, stream);
+    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
+    return rc;
 }
 
 int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes,
@@ -666,7 +732,10 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     if (rc != SM_OK) return rc;
     sm_plan_info pi;
     const sm_softmax_opts o = opts_or_default(opts);
-    rc = make_plan(p, o, dv, &pi);
+    bool capturing = false;
+    hipError_t e = stream_capturing(stream, &capturing);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = make_plan(p, o, dv, capturing, &pi);
     if (rc != SM_OK) return rc;
     if (pi.workspace_bytes == 0) return launch(p, pi, nullptr, o, stream);
 
@@ -675,17 +744,8 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
             return SM_ERR_WORKSPACE;
         return launch(p, pi, ws, o, stream);
     }
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    keep_pool_memory(dev);
-    void* tmp = nullptr;
-    e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    rc = launch(p, pi, tmp, o, stream);
-    e = hipFreeAsync(tmp, stream);
-    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
-    return rc;
+    return with_scratch((size_t)pi.workspace_bytes, capturing, stream,
+                        [&](void* tmp) { return launch(p, pi, tmp, o, stream); });
 }
 
 // ------------------------------------------------------------ backward
@@ -731,7 +791,7 @@ int occ_bwd_live(int dtype, int G, int V) {
 }
 
 int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool live,
-                  sm_plan_info* pi) {
+                  bool no_split, sm_plan_info* pi) {
     *pi = sm_plan_info{};
     const int es = elem_bytes(p.dtype);
     const int E = 16 / es;
@@ -747,6 +807,10 @@ int make_plan_bwd(const BwdProblem& p, const sm_softmax_opts& o, int cus, bool l
     if (plan < SM_PLAN_AUTO || plan > SM_PLAN_SPLIT) return SM_ERR_PLAN;
     const bool auto_plan = plan == SM_PLAN_AUTO;
     if (auto_plan) plan = one_pass_rule(p.M, p.N, nw_max) ? SM_PLAN_RESIDENT : SM_PLAN_SPLIT;
+    if (plan == SM_PLAN_SPLIT && no_split) {  // graph capture, as in the forward
+        if (!auto_plan) return SM_ERR_PLAN;
+        plan = SM_PLAN_WIDE;
+    }
     if (plan == SM_PLAN_SPLIT) {
         auto occ_fn = live ? occ_split_live : occ_split_host;
         int64_t P = 0, grid = 0;
@@ -847,10 +911,11 @@ int launch_bwd(const BwdProblem& p, const sm_plan_info& pi, void* ws, const sm_s
         BwdSplitKernelFn fn = bwd_split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
         if (!fn) return SM_ERR_PLAN;
         const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
+        const int recompute = (p.dx != p.y && p.dx != p.dy) ? 1 : 0;
         e = launch_k(reinterpret_cast<const void*>(fn), dim3((unsigned)pi.grid), dim3(kSplitLanes),
                      stream, ev0, ev1, y, dy, dx, ws, sync, p.M, N, ysb, dysb, dxsb,
                      (int)pi.waves_per_row, pi.slice_windows, next_tag(), spin,
-                     (int)pi.dy_same_phase, (int)pi.same_phase);
+                     (int)pi.dy_same_phase, (int)pi.same_phase, recompute);
         return e == hipSuccess ? SM_OK : hip_fail(e);
     }
     if (pi.plan == SM_PLAN_WIDE) {
@@ -888,7 +953,10 @@ int run_bwd(const BwdProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
     if (rc != SM_OK) return rc;
     const sm_softmax_opts o = opts_or_default(opts);
     sm_plan_info pi;
-    rc = make_plan_bwd(p, o, dv.cus, true, &pi);
+    bool capturing = false;
+    hipError_t e = stream_capturing(stream, &capturing);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = make_plan_bwd(p, o, dv.cus, true, capturing, &pi);
     if (rc != SM_OK) return rc;
     if (pi.workspace_bytes == 0) return launch_bwd(p, pi, nullptr, o, stream);
     if (ws) {
@@ -896,17 +964,8 @@ int run_bwd(const BwdProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
             return SM_ERR_WORKSPACE;
         return launch_bwd(p, pi, ws, o, stream);
     }
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    keep_pool_memory(dev);
-    void* tmp = nullptr;
-    e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    rc = launch_bwd(p, pi, tmp, o, stream);
-    e = hipFreeAsync(tmp, stream);
-    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
-    return rc;
+    return with_scratch((size_t)pi.workspace_bytes, capturing, stream,
+                        [&](void* tmp) { return launch_bwd(p, pi, tmp, o, stream); });
 }
 
 // ------------------------------------------------------------ residual RMSNorm
@@ -969,7 +1028,7 @@ int occ_rms_live(int dtype, int G, int V) {
 }
 
 int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool live,
-                  sm_plan_info* pi) {
+                  bool no_split, sm_plan_info* pi) {
     *pi = sm_plan_info{};
     const int es = elem_bytes(p.dtype);
     const int E = 16 / es;
@@ -993,7 +1052,11 @@ int make_plan_rms(const RmsProblem& p, const sm_softmax_opts& o, int cus, bool l
         int64_t P = 0, grid = 0;
         int V = o.vecs_per_lane;
         bool fused = false;
-        if (plan == SM_PLAN_SPLIT) {
+        if (plan == SM_PLAN_SPLIT && no_split) {
+            // graph capture: the two launches (publish, then gather) never wait on
+            // peers, so a replay's stale words are all rewritten before they are read
+            if (!auto_plan) return SM_ERR_PLAN;
+        } else if (plan == SM_PLAN_SPLIT) {
             if (V) {
                 if (V != 1 && V != 2 && V != 4) return SM_ERR_PLAN;
                 const int64_t slots = (int64_t)std::max(1, occ_fn(nullptr, p.dtype, V, 2)) * cus;
@@ -1084,8 +1147,15 @@ int launch_rms(const RmsProblem& p, const sm_plan_info& pi, void* ws, const sm_s
     const int N = (int)p.N;
     hipError_t e;
     if (pi.plan == SM_PLAN_SPLIT || pi.plan == SM_PLAN_WIDE) {
-        void* sync = split_sync(stream, true, &e);
-        if (!sync) return hip_fail(e);
+        // only the one-launch form waits on peers and may count a failure
+        void* sync = nullptr;
+        if (pi.plan == SM_PLAN_SPLIT) {
+            sync = split_sync(stream, true, &e);
+            if (!sync) return hip_fail(e);
+        }
+        const bool aliased = p.y == p.x || (p.r && p.y == p.r) ||
+                             (p.s && (p.s == p.x || (p.r && p.s == p.r)));
+        if (!aliased) flags |= kRmsRecompute;
         RmsSplitKernelFn fn = rms_split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
         if (!fn) return SM_ERR_PLAN;
         const int spin = o.spin_limit > 0 ? o.spin_limit : kSplitSpinDefault;
@@ -1127,7 +1197,10 @@ int run_rms(const RmsProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
     if (rc != SM_OK) return rc;
     const sm_softmax_opts o = opts_or_default(opts);
     sm_plan_info pi;
-    rc = make_plan_rms(p, o, dv.cus, true, &pi);
+    bool capturing = false;
+    hipError_t e = stream_capturing(stream, &capturing);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = make_plan_rms(p, o, dv.cus, true, capturing, &pi);
     if (rc != SM_OK) return rc;
     if (pi.workspace_bytes == 0) return launch_rms(p, pi, nullptr, o, stream);
     if (ws) {
@@ -1135,17 +1208,8 @@ int run_rms(const RmsProblem& p, const sm_softmax_opts* opts, void* ws, size_t w
             return SM_ERR_WORKSPACE;
         return launch_rms(p, pi, ws, o, stream);
     }
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e);
-    keep_pool_memory(dev);
-    void* tmp = nullptr;
-    e = hipMallocAsync(&tmp, (size_t)pi.workspace_bytes, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    rc = launch_rms(p, pi, tmp, o, stream);
-    e = hipFreeAsync(tmp, stream);
-    if (rc == SM_OK && e != hipSuccess) rc = hip_fail(e);
-    return rc;
+    return with_scratch((size_t)pi.workspace_bytes, capturing, stream,
+                        [&](void* tmp) { return launch_rms(p, pi, tmp, o, stream); });
 }
 
 // ------------------------------------------------------------ fused attention
@@ -1319,7 +1383,7 @@ int sm_rmsnorm_plan_query(const void* x, const void* residual, const void* weigh
         if (rc != SM_OK) return rc;
         cus = dv.cus;
     }
-    return make_plan_rms(p, opts_or_default(opts), cus, num_cus <= 0, info);
+    return make_plan_rms(p, opts_or_default(opts), cus, num_cus <= 0, false, info);
 }
 
 int sm_softmax_fwd(const void* in, void* out, int64_t M, int64_t N, int64_t in_stride,
@@ -1360,7 +1424,7 @@ int sm_softmax_plan_query(const void* in, const void* out, int64_t M, int64_t N,
         rc = live_device(&dv);
         if (rc != SM_OK) return rc;
     }
-    return make_plan(p, opts_or_default(opts), dv, info);
+    return make_plan(p, opts_or_default(opts), dv, false, info);
 }
 
 int sm_softmax_bwd(const void* y, const void* dy, void* dx, int64_t M, int64_t N,
@@ -1399,7 +1463,7 @@ int sm_softmax_bwd_plan_query(const void* y, const void* dy, const void* dx, int
         if (rc != SM_OK) return rc;
         cus = dv.cus;
     }
-    return make_plan_bwd(p, opts_or_default(opts), cus, num_cus <= 0, info);
+    return make_plan_bwd(p, opts_or_default(opts), cus, num_cus <= 0, false, info);
 }
 
 const char* sm_softmax_strerror(int status) {

@@ -30,8 +30,12 @@
 // the tag, and each value comes from that same single-copy-atomic load. No L2
 // write-back or invalidate is needed, and no slot is ever cleared: a stale word
 // carries another call's tag. Every wait is bounded (spin_limit polls per
-// workgroup); a workgroup that runs out writes NaN over its slice and counts the
-// failure, so a kernel always drains.
+// workgroup), so a kernel always drains. A workgroup that runs out counts the
+// failure and, when the output does not alias the input (`recompute`), derives
+// the row's statistics itself from the whole input row -- the same definition, in
+// another summation order -- so the result does not depend on scheduling; in place,
+// where the row's other slices may already have overwritten their input, it writes
+// NaN over its slice instead.
 #pragma once
 
 #include "sm_bwd.hpp"
@@ -125,11 +129,70 @@ __device__ __forceinline__ void split_gather(const SplitSlot* row_slots, int P, 
     }
 }
 
+// Fallback after a wait ran out: the whole workgroup walks the entire input row
+// (window grid as in the slice loads, 256 windows per step) twice -- the row
+// maximum, then the sum of exp(x - max) with the same exponential as the slices --
+// and returns (m, s_hi, s_lo) on every lane.
+template <int DT, bool NT>
+__device__ __noinline__ void split_row_stats(const RowGeom<DT> g, int N, float* lds_a,
+                                             float* lds_b, float* lds_c, float& m, float& s_hi,
+                                             float& s_lo) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int B = kSplitBlock;
+    const int lane = threadIdx.x;
+    auto window = [&](int64_t w, float (&x)[E]) {
+        decode<DT>(load16<NT>(g.base + 16 * (size_t)w), x);
+        const int64_t c0 = w * E - g.head;
+        if (c0 < 0 || c0 + E > N) {
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int64_t c = c0 + k;
+                if (c < 0 || c >= N) x[k] = kNegInf;
+            }
+        }
+    };
+    float lm = kNegInf;
+    for (int64_t w = lane; w < g.nwin; w += B) {
+        float x[E];
+        window(w, x);
+#pragma unroll
+        for (int k = 0; k + 1 < E; k += 2) lm = max3f(lm, x[k], x[k + 1]);
+    }
+    m = row_max<B>(lm, lds_a);
+    const float ms = (m == kNegInf) ? 0.f : m;
+    if constexpr (DT == kF32) {
+        CSum cs;
+        for (int64_t w = lane; w < g.nwin; w += B) {
+            float x[E];
+            window(w, x);
+#pragma unroll
+            for (int k = 0; k < E; ++k) cs.add(exp_diff_acc(x[k], ms));
+        }
+        cs = row_csum<B>(cs, lds_b, lds_c);
+        s_hi = cs.hi;
+        s_lo = cs.lo;
+    } else {
+        const bool fast = __builtin_fabsf(ms) <= 0x1p125f;
+        const float mL = ms * kLog2e;
+        float acc = 0.f;
+        for (int64_t w = lane; w < g.nwin; w += B) {
+            float x[E];
+            window(w, x);
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                acc += fast ? exp2_fast(__builtin_fmaf(x[k], kLog2e, -mL))
+                            : exp2_fast((x[k] - ms) * kLog2e);
+        }
+        s_hi = row_sum<B>(acc, lds_b);
+        s_lo = 0.f;
+    }
+}
+
 template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
 k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, SplitSync* sync,
                 int64_t M, int N, int64_t in_sb, int64_t out_sb, int P, int S, uint32_t tag,
-                int spin_limit, int same_phase) {
+                int spin_limit, int same_phase, int recompute) {
     // S: windows per slice (<= B * V; the host spreads a row evenly over its P slices)
     constexpr int E = Elem<DT>::per_vec;
     constexpr int ES = Elem<DT>::bytes;
@@ -213,10 +276,18 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
         }
         split_gather<DT>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
-        const float m = lds_stat[0];
-        const float s = csum_value(lds_stat[1], lds_stat[2]);
-        const bool ok = lds_stat[3] != 0.f;
-        if (!ok && lane == 0) atomicAdd(&sync->failures, 1u);
+        float m = lds_stat[0];
+        float s = csum_value(lds_stat[1], lds_stat[2]);
+        bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
+        if (!ok) {
+            if (lane == 0) atomicAdd(&sync->failures, 1u);
+            if (recompute) {
+                float hi, lo;
+                split_row_stats<DT, NT>(g, N, lds_a, lds_b, lds_c, m, hi, lo);
+                s = csum_value(hi, lo);
+                ok = true;
+            }
+        }
 
         // y = exp(x - m) / s: FP32 recomputes exp from x with the row maximum;
         // FP16/BF16 rescale the slice's exponentials by exp(mp - m) / s.
@@ -292,6 +363,32 @@ __device__ __forceinline__ void split_gather_sum(const SplitSlot* row_slots, int
     }
 }
 
+// Backward fallback after a wait ran out: the workgroup forms the row's whole dot
+// product sum(y * dy) from the inputs (256 windows per step), on every lane.
+template <int DT, bool NT>
+__device__ __noinline__ float split_row_dot(const RowGeom<DT> g, const unsigned char* dyrow, int N,
+                                            int dy_phase, float* lds_hi, float* lds_lo) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int B = kSplitBlock;
+    const int lane = threadIdx.x;
+    float acc = 0.f;
+    CSum cs;
+    for (int64_t w = lane; w < g.nwin; w += B) {
+        float fy[1][E], fd[1][E];
+        decode<DT>(load16<NT>(g.base + 16 * (size_t)w), fy[0]);
+        load_dy<DT, 1>(fd, dyrow, g.head, N, w, 0, g.nwin, dy_phase != 0);
+        zero_outside<DT, 1>(fy, g.head, N, w, 0);
+        zero_outside<DT, 1>(fd, g.head, N, w, 0);
+        lane_dot<DT, 1>(fy, fd, acc, cs);
+    }
+    if constexpr (DT == kF32) {
+        cs = row_csum<B>(cs, lds_hi, lds_lo);
+        return csum_value(cs.hi, cs.lo);
+    } else {
+        return row_sum<B>(acc, lds_hi);
+    }
+}
+
 // One-launch backward of wide rows: a slice's partial dot sum(y * dy) is
 // published and merged like the forward's (max, sum) pairs; y and dy stay in
 // registers in their stored encoding; dx = y * (dy - dot) is written from them.
@@ -300,7 +397,7 @@ __global__ void __launch_bounds__(kSplitBlock)
 k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned char* dx,
                     SplitSlot* slots, SplitSync* sync, int64_t M, int N, int64_t y_sb,
                     int64_t dy_sb, int64_t dx_sb, int P, int S, uint32_t tag, int spin_limit,
-                    int dy_phase, int dx_phase) {
+                    int dy_phase, int dx_phase, int recompute) {
     constexpr int E = Elem<DT>::per_vec;
     constexpr int B = kSplitBlock;
     __shared__ float lds_hi[B / 64], lds_lo[B / 64];
@@ -354,9 +451,12 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
         }
         split_gather_sum<DT == kF32>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
-        const bool ok = lds_stat[3] != 0.f;
-        const float dot = ok ? csum_value(lds_stat[1], lds_stat[2]) : __builtin_nanf("");
-        if (!ok && lane == 0) atomicAdd(&sync->failures, 1u);
+        const bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
+        float dot = ok ? csum_value(lds_stat[1], lds_stat[2]) : __builtin_nanf("");
+        if (!ok) {
+            if (lane == 0) atomicAdd(&sync->failures, 1u);
+            if (recompute) dot = split_row_dot<DT, NT>(g, dy + row * dy_sb, N, dy_phase, lds_hi, lds_lo);
+        }
 
         unsigned char* dxrow = dx + row * dx_sb;
 #pragma unroll

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert sm.sm_softmax_version() == sm.ABI_VERSION == 10100
+    assert sm.sm_softmax_version() == sm.ABI_VERSION == 10200
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert sm.sm_softmax_strerror(code) and sm.sm_softmax_strerror(code) != "unknown status"
     assert sm.sm_softmax_strerror(99) == "unknown status"
@@ -228,6 +228,29 @@ def test_plan_rule_fp32_forward():
     for M, N, want in [(256, 65536, ("split", 8)), (4, 16386, ("split", 2)), (256, 1 << 21, ("split", 8))]:
         rc, p = plan(M, N, BF16)
         assert (p["plan_name"], p["vecs_per_lane"]) == want, (M, N, p)
+
+
+def test_plan_at_the_width_limit():
+    """N = 2^31 - 1, the widest row the ABI takes, in each dtype and alignment: the plan
+    (SPLIT cannot hold a row's slices at once, so WIDE) has window and chunk counts that
+    cover the row exactly, the same count the kernels form in 64 bits (the 32-bit sum
+    head + N + E - 1 would overflow here); 2^31 is rejected."""
+    N = (1 << 31) - 1
+    for dt, es in ((F32, 4), (F16, 2), (BF16, 2)):
+        E = 16 // es
+        for base in (BASE, BASE + es):  # aligned, and one element past a 16-byte boundary
+            head = (base % 16) // es
+            rc, p = sm.sm_softmax_plan_query(base, BASE * 4, 1, N, N, N, dt, None, 256)
+            assert rc == OK and p.as_dict()["plan_name"] == "wide", (dt, base, rc)
+            nwin = (head + N + E - 1) // E
+            assert head + N + E - 1 > (1 << 31) - 1 or dt == F32
+            wpc = 1024 // E
+            nchunks = (nwin + wpc - 1) // wpc
+            d = p.as_dict()
+            assert d["waves_per_row"] == (nchunks + d["chunks_per_wave"] - 1) // d["chunks_per_wave"]
+            assert d["model_bytes"] == 3 * N * es
+        rc, _ = sm.sm_softmax_plan_query(BASE, BASE * 4, 1, N + 1, N + 1, N + 1, dt, None, 256)
+        assert rc == INVALID
 
 
 def test_plan_forcing_and_limits():

@@ -211,3 +211,33 @@ def test_widest_rows_automatic_launch_count(M):
     assert info["launches"] == (2 if M == 8 else 1)
     y, s = run(x, r, w, s_out=True)
     compare_rms(y, x, r, w, 1e-6, s_gpu=s, what=f"widest {M}x{N}")
+
+
+def test_split_wait_budget_runs_out():
+    """The one-launch SPLIT form with a one-poll wait budget (forced from the host):
+    slices that give up count the failure and, since neither output aliases x or the
+    residual, form the row's sum of squares from x + r themselves: oracle parity,
+    residual_out bit-exact. In place over x they write NaN over their slice instead."""
+    M, N = 24, 131072
+    x, r, w = inputs(M, N, "bf16", seed=41)
+    before = sm.sync_failures()
+    y, s = run(x, r, w, "split", s_out=True, vecs_per_lane=1, spin_limit=1)
+    n = sm.sync_failures() - before
+    compare_rms(y, x, r, w, 1e-6, s_gpu=s, what="one-poll budget, out of place")
+    log(f"[rms] one-poll budget: {n} slices fell back to the whole row")
+    assert n > 0
+    xd, rd, wd = x.to(DEV), r.to(DEV), w.to(DEV)
+    before = sm.sync_failures()
+    sm.rmsnorm(xd, wd, residual=rd, out=xd, opts={"plan": PLANS["split"], "vecs_per_lane": 1,
+                                                   "spin_limit": 1})
+    torch.cuda.synchronize()
+    n = sm.sync_failures() - before
+    P = sm.plan_for_rmsnorm(xd, wd, residual=rd, opts={"plan": PLANS["split"],
+                                                        "vecs_per_lane": 1})["waves_per_row"]
+    gc = xd.float().cpu().view(M, P, -1)
+    nan_slices = torch.isnan(gc).all(dim=2)
+    assert not (torch.isnan(gc).any(dim=2) & ~nan_slices).any()
+    assert n == int(nan_slices.sum())
+    ok_rows = [i for i in range(M) if not nan_slices[i].any()]
+    if ok_rows:
+        compare_rms(xd[ok_rows], x[ok_rows], r[ok_rows], w, 1e-6, what="in place: rows without timeouts")

@@ -1,7 +1,8 @@
 """GPU tests of the one-launch SPLIT plan (forward and backward): every slice shape,
 rounds (more row slices than the grid), rows whose slices are fully masked, the
-wait budget and its failure count, caller workspace, two streams at once, and the
-bench's wide-row workload at full size. Each result is checked against the FP64
+wait budget (its whole-row fallback out of place, NaN slices in place) and its
+failure count, caller workspace, two streams at once, and the bench's wide-row
+workload at full size. Each result is checked against the FP64
 oracle element by element."""
 import math
 
@@ -125,31 +126,73 @@ def test_repeatable_and_misaligned():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_wait_budget_failures_are_counted():
-    """A wait budget of one poll: slices whose peers are not yet published give up.
-    Each slice is then either correct or all NaN, and the failure count grows by the
-    number of NaN slices. Every kernel drains either way."""
+def test_wait_budget_runs_out_out_of_place():
+    """A wait budget of one poll (forced from the host): slices whose peers have not
+    yet published give up, count the failure, and re-read their whole input row for
+    the row statistics, so every element still matches the oracle. Every kernel drains."""
     M, N = 32, 131072
     x = _rand(M, N, "bf16", seed=3)
+    xd = x.to(DEV)
+    for dt in ("bf16", "f32"):
+        xt = x.to(TDT[dt])
+        xd = xt.to(DEV)
+        before = sm.sync_failures()
+        g = fwd(xd, vecs_per_lane=1, spin_limit=1)
+        n = sm.sync_failures() - before
+        compare(g, xt, what=f"{dt} one-poll budget, out of place")
+        log(f"[split] {dt} one-poll budget out of place: {n} slices fell back to the whole row")
+        assert n > 0
+        # the default budget then works again on the same stream and slots
+        after = sm.sync_failures()
+        g = fwd(xd, vecs_per_lane=1)
+        compare(g, xt, what=f"{dt} after timeouts")
+        assert sm.sync_failures() == after
+
+
+def test_wait_budget_runs_out_in_place():
+    """In place, a slice that gives up cannot re-read its row (its peers may already
+    have written theirs): each slice is then either correct or all NaN, and the
+    failure count grows by the number of NaN slices."""
+    M, N = 32, 131072
+    x = _rand(M, N, "bf16", seed=4)
     xd = x.to(DEV)
     info = sm.plan_for(xd, opts={"plan": SPLIT, "vecs_per_lane": 1})
     P, S = info["waves_per_row"], 256 * 8
     before = sm.sync_failures()
-    g = fwd(xd, vecs_per_lane=1, spin_limit=1)
+    fwd(xd, out=xd, vecs_per_lane=1, spin_limit=1)
     after = sm.sync_failures()
-    gc = g.float().cpu().view(M, P, S)
+    gc = xd.float().cpu().view(M, P, S)
     nan_slices = torch.isnan(gc).all(dim=2)
     partly = torch.isnan(gc).any(dim=2) & ~nan_slices
     assert not partly.any()
     assert after - before == int(nan_slices.sum())
     ok_rows = [i for i in range(M) if not nan_slices[i].any()]
     if ok_rows:
-        compare(g[ok_rows], x[ok_rows], what="rows without timeouts")
-    log(f"[split] one-poll budget: {int(nan_slices.sum())} of {M * P} slices timed out")
-    # the default budget then works again on the same stream and slots
-    g = fwd(xd, vecs_per_lane=1)
-    compare(g, x, what="after timeouts")
-    assert sm.sync_failures() == after
+        compare(xd[ok_rows], x[ok_rows], what="in place: rows without timeouts")
+    log(f"[split] one-poll budget in place: {int(nan_slices.sum())} of {M * P} slices timed out")
+
+
+def test_backward_wait_budget_runs_out():
+    """The backward with a one-poll budget: out of place, slices that give up form
+    the row's dot product from y and dy themselves (oracle parity, failures counted);
+    in place over dy, they write NaN and are counted."""
+    M, N = 24, 131072
+    y, dy = _bwd_inputs(M, N, "bf16", seed=8)
+    yd, dyd = y.to(DEV), dy.to(DEV)
+    before = sm.sync_failures()
+    g = bwd(yd, dyd, vecs_per_lane=1, spin_limit=1)
+    n = sm.sync_failures() - before
+    compare_bwd(g, y, dy, what="bwd one-poll budget, out of place")
+    log(f"[split] backward one-poll budget: {n} slices fell back to the whole row")
+    assert n > 0
+    before = sm.sync_failures()
+    bwd(yd, dyd, dx=dyd, vecs_per_lane=1, spin_limit=1)
+    n = sm.sync_failures() - before
+    P = sm.plan_for_backward(yd, dyd, opts={"plan": SPLIT, "vecs_per_lane": 1})["waves_per_row"]
+    gc = dyd.float().cpu().view(M, P, -1)
+    nan_slices = torch.isnan(gc).all(dim=2)
+    assert not (torch.isnan(gc).any(dim=2) & ~nan_slices).any()
+    assert n == int(nan_slices.sum())
 
 
 def test_two_streams_at_once():

@@ -201,6 +201,26 @@ int sm_softmax_fwd_ex(const void *in, void *out, int64_t M, int64_t N, int64_t i
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory -- code under graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: sm_softmax_fwd with the same
+ * arguments and result, making no allocation (no hipMalloc, hipFree or stream-ordered
+ * pool call). The WIDE and SPLIT plans take their scratch, and SPLIT its failure
+ * counter, from one array of the library's own per device (SM_NOALLOC_SCRATCH_BYTES
+ * of workspace plus 256 bytes, held until the process ends). A problem whose plan
+ * needs more than SM_NOALLOC_SCRATCH_BYTES of workspace (plan_info.workspace_bytes
+ * of sm_softmax_plan_query) returns SM_ERR_WORKSPACE before launching anything; one-
+ * pass plans need none. Every call on a device shares that device's array, so calls
+ * that overlap in time on one device (different streams, or host threads) race on it
+ * and must be ordered by the caller. SPLIT waits that run out re-read their input row
+ * (out of place) and are not reported; calls in place take WIDE where AUTO would take
+ * SPLIT, as do calls on a capturing stream, so no result depends on scheduling.
+ * Returns SM_OK or a negative sm_status.
+ */
+#define SM_NOALLOC_SCRATCH_BYTES (1u << 20)
+int sm_softmax_fwd_noalloc(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,
+                           int64_t out_stride, int dtype, hipStream_t stream);
+
+/*
  * Resolve the plan a call would use, without launching anything.
  *   num_cus > 0 : evaluate on the host only for a device with that many
  *                 compute units (occupancy assumed: 8 workgroups of 256

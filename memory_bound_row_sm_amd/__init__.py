@@ -22,7 +22,7 @@ __all__ = [
     "sm_softmax_bwd_plan_query", "softmax_backward", "plan_for_backward",
     "sm_softmax_sync_failures", "sync_failures", "sm_rmsnorm_fwd", "sm_rmsnorm_fwd_ex",
     "sm_rmsnorm_plan_query", "rmsnorm", "plan_for_rmsnorm", "sm_attention_fwd",
-    "sm_attention_fwd_ex", "attention",
+    "sm_attention_fwd_ex", "attention", "sm_softmax_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 SM_F32, SM_F16, SM_BF16 = 0, 1, 2
@@ -38,7 +38,9 @@ EXPORTED_SYMBOLS = (
     "sm_softmax_version", "sm_softmax_last_hip_error", "sm_softmax_sync_failures",
     "sm_rmsnorm_fwd", "sm_rmsnorm_fwd_ex", "sm_rmsnorm_plan_query",
     "sm_attention_fwd", "sm_attention_fwd_ex", "sm_bench_copy", "sm_bench_flush",
+    "sm_softmax_fwd_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 1 << 20  # SM_NOALLOC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsm_softmax.so")
@@ -98,6 +100,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(lib_path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.sm_softmax_fwd.argtypes = [vp, vp, i64, i64, i64, i64, ci, vp]
+        L.sm_softmax_fwd_noalloc.argtypes = [vp, vp, i64, i64, i64, i64, ci, vp]
         L.sm_softmax_fwd_ex.argtypes = [vp, vp, i64, i64, i64, i64, ci, ctypes.POINTER(SmOpts),
                                         vp, ctypes.c_size_t, vp]
         L.sm_softmax_plan_query.argtypes = [vp, vp, i64, i64, i64, i64, ci,
@@ -125,7 +128,8 @@ def lib() -> ctypes.CDLL:
         L.sm_softmax_sync_failures.argtypes = [vp, ctypes.POINTER(ctypes.c_uint)]
         L.sm_bench_copy.argtypes = [vp, vp, ctypes.c_size_t, ci, ci, vp, vp, vp]
         L.sm_bench_flush.argtypes = [vp, ctypes.c_size_t, vp]
-        for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_ex, L.sm_softmax_plan_query,
+        for f in (L.sm_softmax_fwd, L.sm_softmax_fwd_noalloc, L.sm_softmax_fwd_ex,
+                  L.sm_softmax_plan_query,
                   L.sm_softmax_bwd, L.sm_softmax_bwd_ex, L.sm_softmax_bwd_plan_query,
                   L.sm_softmax_version, L.sm_softmax_last_hip_error, L.sm_softmax_sync_failures,
                   L.sm_rmsnorm_fwd, L.sm_rmsnorm_fwd_ex, L.sm_rmsnorm_plan_query,
@@ -155,6 +159,11 @@ def _opts(opts) -> SmOpts | None:
 def sm_softmax_fwd(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: int, out_stride: int,
                    dtype: int, stream: int = 0) -> int:
     return lib().sm_softmax_fwd(in_ptr, out_ptr, M, N, in_stride, out_stride, dtype, stream)
+
+
+def sm_softmax_fwd_noalloc(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: int,
+                           out_stride: int, dtype: int, stream: int = 0) -> int:
+    return lib().sm_softmax_fwd_noalloc(in_ptr, out_ptr, M, N, in_stride, out_stride, dtype, stream)
 
 
 def sm_softmax_fwd_ex(in_ptr: int, out_ptr: int, M: int, N: int, in_stride: int, out_stride: int,

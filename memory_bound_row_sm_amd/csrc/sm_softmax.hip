@@ -313,10 +313,11 @@ int split_auto_v(int64_t M, int64_t nw, int vmin, int vmax, int vround, int64_t 
     return 0;
 }
 
-// no_split: the call is being captured into a graph. SPLIT tags its slots with a
-// per-call id fixed at launch, which a graph would replay unchanged, so a replay could
-// read the previous replay's statistics before its own peers publish: AUTO takes the
-// two-pass WIDE plan instead, and a forced SPLIT is refused.
+// no_split: AUTO takes the two-pass WIDE plan where it would take SPLIT, and a forced
+// SPLIT is refused. Set when the call is being captured into a graph (SPLIT tags its
+// slots with a per-call id fixed at launch, which a graph would replay unchanged, so a
+// replay could read the previous replay's statistics before its own peers publish),
+// and by the allocation-free entry point for calls in place.
 int make_plan(const Problem& p, const sm_softmax_opts& o, const DeviceView& dev, bool no_split,
               sm_plan_info* pi) {
     *pi = sm_plan_info{};
@@ -603,8 +604,10 @@ int xcd_order(const sm_plan_info& pi, bool rows_share_lines) {
     return (pi.plan == SM_PLAN_RESIDENT && pi.lanes_per_row > 64 && rows_share_lines) ? 1 : 0;
 }
 
+// sync: SPLIT failure counter to use, or nullptr for the stream's own (created on
+// first use).
 int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_opts& o,
-           hipStream_t stream) {
+           hipStream_t stream, void* sync = nullptr) {
     const hipEvent_t ev0 = o.start_event, ev1 = o.stop_event;
     const int es = elem_bytes(p.dtype);
     const auto* in = reinterpret_cast<const unsigned char*>(p.in);
@@ -613,7 +616,7 @@ int launch(const Problem& p, const sm_plan_info& pi, void* ws, const sm_softmax_
     const int N = (int)p.N;
     hipError_t e;
     if (pi.plan == SM_PLAN_SPLIT) {
-        void* sync = split_sync(stream, true, &e);
+        if (!sync) sync = split_sync(stream, true, &e);
         if (!sync) return hip_fail(e);
         SplitKernelFn fn = split_kernel(p.dtype, pi.vecs_per_lane, pi.nt_loads);
         if (!fn) return SM_ERR_PLAN;
@@ -746,6 +749,63 @@ int run(const Problem& p, const sm_softmax_opts* opts, void* ws, size_t ws_bytes
     }
     return with_scratch((size_t)pi.workspace_bytes, capturing, stream,
                         [&](void* tmp) { return launch(p, pi, tmp, o, stream); });
+}
+
+// ------------------------------------------------------------ allocation-free forward
+// Scratch of sm_softmax_fwd_noalloc: one array per device, held until the process
+// ends. Bytes [0, 256) hold that entry point's SPLIT failure counter (a SplitSync;
+// device globals start zeroed when the code object loads), bytes [256, 256 +
+// SM_NOALLOC_SCRATCH_BYTES) its WIDE or SPLIT workspace. Host code never passes
+// `scratch` itself to a kernel (in host code the name is a host-side stand-in): it
+// takes the device's address of it from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocSyncBytes = 256;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoAllocSyncBytes + SM_NOALLOC_SCRATCH_BYTES];
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, unsigned char*> g_scratch;  // device -> address of its `scratch`
+
+hipError_t scratch_address(unsigned char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<unsigned char*>(ptr);
+    *out = static_cast<unsigned char*>(ptr);
+    return hipSuccess;
+}
+
+int run_noalloc(const Problem& p, hipStream_t stream) {
+    int rc = validate(p);
+    if (rc != SM_OK || p.M == 0 || p.N == 0) return rc;
+    DeviceView dv;
+    rc = live_device(&dv);
+    if (rc != SM_OK) return rc;
+    bool capturing = false;
+    hipError_t e = stream_capturing(stream, &capturing);
+    if (e != hipSuccess) return hip_fail(e);
+    unsigned char* base = nullptr;
+    e = scratch_address(&base);
+    if (e != hipSuccess) return hip_fail(e);
+    // In place, a SPLIT slice whose wait ran out could only write NaN (its row's input
+    // may already be overwritten), and this entry point has no counter the caller can
+    // read: rows that AUTO would split take the two-pass WIDE plan instead, so the
+    // result never depends on scheduling.
+    const sm_softmax_opts o{};
+    sm_plan_info pi;
+    rc = make_plan(p, o, dv, capturing || p.in == p.out, &pi);
+    if (rc != SM_OK) return rc;
+    if ((uint64_t)pi.workspace_bytes > (uint64_t)SM_NOALLOC_SCRATCH_BYTES) return SM_ERR_WORKSPACE;
+    return launch(p, pi, base + kNoAllocSyncBytes, o, stream, base);
 }
 
 // ------------------------------------------------------------ backward
@@ -1399,6 +1459,13 @@ int sm_softmax_fwd_ex(const void* in, void* out, int64_t M, int64_t N, int64_t i
     const Problem p{reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out), M, N,
                     in_stride, out_stride, dtype};
     return run(p, opts, workspace, workspace_bytes, stream);
+}
+
+int sm_softmax_fwd_noalloc(const void* in, void* out, int64_t M, int64_t N, int64_t in_stride,
+                           int64_t out_stride, int dtype, hipStream_t stream) {
+    const Problem p{reinterpret_cast<uintptr_t>(in), reinterpret_cast<uintptr_t>(out), M, N,
+                    in_stride, out_stride, dtype};
+    return run_noalloc(p, stream);
 }
 
 int sm_softmax_plan_query(const void* in, const void* out, int64_t M, int64_t N, int64_t in_stride,

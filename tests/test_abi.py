@@ -461,3 +461,19 @@ def test_attention_valid_call_without_device():
     assert rc in (OK, NO_DEVICE)
     rc = attn(Sk=0, k=0, v=0)  # no keys: every query gets zeros
     assert rc in (OK, NO_DEVICE)
+
+
+def test_noalloc_entry_point_validation():
+    """The allocation-free forward validates exactly as sm_softmax_fwd (before any HIP
+    call), and its scratch limit in the header matches the binding's."""
+    for args, want in [((BASE, BASE * 2, 4, 8, 8, 8, 7), DTYPE),
+                       ((BASE, BASE * 2, 4, 8, 7, 8, F32), INVALID),
+                       ((BASE, BASE + 16, 4, 8, 8, 8, F32), OVERLAP),
+                       ((BASE, BASE, 0, 8, 8, 8, F32), OK),
+                       ((0, 0, 4, 0, 0, 0, F32), OK)]:
+        assert sm.sm_softmax_fwd_noalloc(*args, 0) == want == sm.sm_softmax_fwd(*args, 0)
+    if not gpu_available():
+        assert sm.sm_softmax_fwd_noalloc(BASE, BASE * 2, 4, 8, 8, 8, F32, 0) == NO_DEVICE
+    text = open(os.path.join(INCLUDE, "sm_softmax.h")).read()
+    m = re.search(r"#define SM_NOALLOC_SCRATCH_BYTES \(1u << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == sm.NOALLOC_SCRATCH_BYTES

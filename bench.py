@@ -211,6 +211,9 @@ def main(argv=None) -> int:
                     help="HBM bytes per call of every sweep case from the counter pass's manifest "
                          "and its FETCH_SIZE and WRITE_SIZE runs (markdown on stdout), and exit")
     ap.add_argument("--sq-csv", help="with --traffic-table: an SQ counter run of the same pass")
+    ap.add_argument("--sweep-table", metavar="SWEEP_LOG",
+                    help="print the per-config table (time, %% of 8 TB/s, copy ceiling) of a "
+                         "--sweep log and exit")
     ap.add_argument("--sweep-log", help="with --traffic-table: a --sweep log, for times and GB/s")
     args = ap.parse_args(argv)
 
@@ -225,6 +228,9 @@ def main(argv=None) -> int:
         return 0
     if args.traffic_table:
         print(traffic_table(*args.traffic_table, sq_csv=args.sq_csv, sweep_log=args.sweep_log))
+        return 0
+    if args.sweep_table:
+        print(sweep_table(args.sweep_table))
         return 0
     if args.score_grid:
         with open(args.score_grid) as f:
@@ -917,6 +923,30 @@ def softmax_groups(torch, sm, workloads, s_handle, clocks_up=None):
         torch.cuda.empty_cache()
 
 
+# MI355X's last-level cache (MALL / Infinity Cache): a workload of at most this many
+# bytes can be served partly from it even after the 1 GiB sweep, on its write-backs
+MALL_BYTES = 256 << 20
+# copy-ceiling launch shapes: (workgroups, store policy) -- device-scope (sc1) stores are
+# the row kernels' own policy
+COPY_SHAPES = [(1024, 1), (4096, 1), (16384, 1), (1024, 0), (4096, 0), (16384, 0)]
+
+
+def copy_calls(torch, sm, s_handle, model_bytes: int):
+    """[(shape, call)] for a 16-byte copy of model_bytes / 2 bytes (read) into as many
+    (written), under each of COPY_SHAPES."""
+    n = max(16, (model_bytes // 2) // 16 * 16)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out = []
+    for grid, scope in COPY_SHAPES:
+        def call(events=(None, None), grid=grid, scope=scope):
+            rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), n, grid, scope, s_handle, *events)
+            if rc != 0:
+                raise sm.SoftmaxError(rc, "sm_bench_copy")
+        out.append((f"grid {grid}, {'device-scope' if scope else 'plain'} stores", call))
+    return out
+
+
 def sweep(torch, sm, workloads, flush, s_handle, log, args):
     """Cold timing of every workload under every plan that can take it (residual
     RMSNorm, then softmax forward and backward), the plans of a workload in rotating
@@ -935,17 +965,71 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
     for name, op, setup, runs in groups:
         if setup is not None:
             setup()
-        stats = time_rotating(torch, [r[2] for r in runs], flush, steps, 10)
+        # the copy ceiling of this workload: a cold 16-byte copy moving the automatic
+        # plan's model bytes (half read, half written), timed in the same rotation
+        model = runs[0][1]["model_bytes"]
+        copies = copy_calls(torch, sm, s_handle, model)
+        stats = time_rotating(torch, [r[2] for r in runs] + [c[1] for c in copies], flush, steps, 10)
+        cst = stats[len(runs):]
+        k = min(range(len(copies)), key=lambda i: cst[i]["mean_us"])
+        copy_us, copy_shape = cst[k]["mean_us"], copies[k][0]
+        log("[sweep] " + json.dumps({"workload": name, "op": op, "copy_ceiling_bytes": model,
+                                     "copy_us": round(copy_us, 3), "copy_shape": copy_shape,
+                                     "copy_GBps": round(model / (copy_us * 1e-6) / 1e9, 1)}))
         for (pname, info, _, check), st in zip(runs, stats):
             gb = info["model_bytes"] / (st["mean_us"] * 1e-6) / 1e9
             line = {"workload": name, "plan": pname, **plan_fields(info, op),
                     "mean_us": round(st["mean_us"], 3), "median_us": round(st["median_us"], 3),
-                    "GBps": round(gb, 1), "pct_peak": round(100 * gb / PEAK_GBPS, 2)}
+                    "GBps": round(gb, 1), "pct_peak": round(100 * gb / PEAK_GBPS, 2),
+                    # the copy moves the automatic plan's model bytes: a plan with more
+                    # model bytes (WIDE) is compared on the time the copy took
+                    "frac_of_copy": round(copy_us / st["mean_us"], 4),
+                    "mall_resident": model <= MALL_BYTES}
             if op != "forward":
                 line = {"workload": name, "op": op, **{k: v for k, v in line.items() if k != "workload"}}
             if check is not None:
                 line.update(check())
             log("[sweep] " + json.dumps(line))
+        del copies
+
+
+# the configurations of the forward softmax hot path, in the order they are tabled
+CONFIG_ROWS = [("c1", "normal_f32_128x781"), ("c2", "normal_bf16_4096x4096"),
+               *[(f"c3 N={n}", f"spiky_f16_8192x{n}") for n in (127, 256, 1000, 2048, 4096, 8192)],
+               ("c4", "offset_bf16_64x131072"), ("c5", "causal_bf16_524288x2048")]
+
+
+def sweep_table(path: str) -> str:
+    """Markdown tables of a --sweep log: per config, the automatic forward plan's cold
+    time, GB/s on the byte model, % of 8 TB/s, and the same-run cold copy of the same
+    bytes (its time and the plan's fraction of it); then every plan of every config."""
+    lines = []
+    with open(path) as f:
+        for ln in f:
+            if "[sweep] " in ln:
+                lines.append(json.loads(ln.split("[sweep] ", 1)[1]))
+    copies = {(d["workload"], d["op"]): d for d in lines if "copy_us" in d}
+    fwd = {(d["workload"], d["plan"]): d for d in lines if "plan" in d and "op" not in d}
+    out = ["| config | workload | plan | model bytes | µs | GB/s | % of 8 TB/s | copy µs | "
+           "copy GB/s | fraction of copy | ≤ 256 MiB (MALL) |",
+           "|---|---|---|---:|---:|---:|---:|---:|---:|---:|---|"]
+    for cfg, name in CONFIG_ROWS:
+        d, c = fwd.get((name, "auto")), copies.get((name, "forward"))
+        if d is None or c is None:
+            continue
+        out.append(f"| {cfg} | {name} | {d['resolved']} | {d['model_bytes']:,} | {d['mean_us']:.2f} | "
+                   f"{d['GBps']:.0f} | {d['pct_peak']:.1f} | {c['copy_us']:.2f} | "
+                   f"{c['copy_GBps']:.0f} | {d['frac_of_copy']:.3f} | "
+                   f"{'yes' if d['mall_resident'] else 'no'} |")
+    out += ["", "Every plan (forward):", "",
+            "| workload | plan | resolved | µs | GB/s | % of 8 TB/s | fraction of copy |",
+            "|---|---|---|---:|---:|---:|---:|"]
+    for cfg, name in CONFIG_ROWS:
+        for (w, pl), d in fwd.items():
+            if w == name:
+                out.append(f"| {name} | {pl} | {d['resolved']} | {d['mean_us']:.2f} | {d['GBps']:.0f} | "
+                           f"{d['pct_peak']:.1f} | {d['frac_of_copy']:.3f} |")
+    return "\n".join(out)
 
 
 def counter_pass(torch, sm, workloads, flush, s_handle, manifest_path, copy_bytes, log) -> int:

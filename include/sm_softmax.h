@@ -175,14 +175,16 @@ typedef struct sm_plan_info {
  *   in_stride,
  *   out_stride  : row strides in elements, >= N when M > 1
  *   dtype       : sm_dtype of both tensors
- * The WIDE and SPLIT plans take their scratch stream-ordered (hipMallocFromPoolAsync
- * / hipFreeAsync on `stream`) from a memory pool the library creates for the device
- * and keeps until the process ends (its release threshold keeps freed blocks for
- * later calls; the device's default pool is not modified), so concurrent calls on
- * different streams never share scratch; on a stream that is capturing a graph, from
- * hipMallocAsync (a graph memory node). The first SPLIT call on a stream also
- * allocates that stream's failure counter (hipMalloc + hipMemset of 256 bytes, kept
- * until the process ends).
+ * The WIDE and SPLIT plans take their scratch from a buffer the library keeps per
+ * (device, stream): allocated (hipMalloc) by the first call on the stream that needs
+ * scratch, replaced by a larger one (at least twice the size) when a call needs more,
+ * and held, with any buffer it replaced, until the process ends (32 bytes per SPLIT
+ * slice, 8 per WIDE wave: 32 KiB for 64 x 131072 BF16 rows; at least 64 KiB is
+ * allocated). Calls on one stream run in order and share it; calls on different streams
+ * never do. On a stream that is capturing a graph the scratch comes from hipMallocAsync
+ * instead (a graph memory node, freed within the graph). The first SPLIT call on a
+ * stream also allocates that stream's failure counter (hipMalloc + hipMemset of 256
+ * bytes, kept until the process ends). sm_softmax_fwd_noalloc allocates nothing.
  * Returns SM_OK or a negative sm_status.
  */
 int sm_softmax_fwd(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,

@@ -114,6 +114,18 @@ __device__ __forceinline__ void store16(unsigned char* p, const uint4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(w) : "memory");
 }
 
+// Load one stored element and decode it exactly to FP32.
+template <int DT>
+__device__ __forceinline__ float load_elem(const unsigned char* p) {
+    if constexpr (DT == kF32) {
+        return *reinterpret_cast<const float*>(p);
+    } else if constexpr (DT == kBF16) {
+        return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(p));
+    }
+}
+
 // Store one element (already encoded) of an encoded vector: element k of `v`.
 template <int DT>
 __device__ __forceinline__ void store_elem(unsigned char* p, const uint4 v, int k) {

@@ -185,30 +185,39 @@ k_rmsnorm_rows(const unsigned char* x, const unsigned char* r, const unsigned ch
     }
 }
 
-// Split fallback after a wait ran out: the workgroup forms the row's whole sum of
-// squares from x (and r, rounded in as in the slices), 256 windows per step, and
-// returns it on every lane as (hi, lo).
-template <int DT, bool NT>
-__device__ __noinline__ void rms_row_sq(const RowGeom<DT> g, const unsigned char* rrow,
-                                        const unsigned char* wvec, const unsigned char* xrow, int N,
-                                        int flags, float* lds_hi, float* lds_lo, float& hi,
-                                        float& lo) {
-    constexpr int B = kSplitBlock;
+// Split fallback after a wait ran out: wave 0's 64 lanes form the row's whole sum of
+// squares of s = rn(x + r) from the inputs, element by element (the same rounding of
+// the sum, and for FP32 data the same exact products and compensated sums as the
+// slices), reduced over the wave.
+template <int DT>
+__device__ __forceinline__ CSum wave_row_sq(const unsigned char* xrow, const unsigned char* rrow,
+                                            int N, int flags) {
+    constexpr int ES = Elem<DT>::bytes;
+    const int lane = threadIdx.x & 63;
     float acc = 0.f;
     CSum cs;
-    for (int64_t w = threadIdx.x; w < g.nwin; w += B) {
-        uint32_t rs[1][4], rw[1][4];
-        rms_load<DT, 1, NT>(rs, rw, g, rrow, wvec, xrow, N, w, 0, g.nwin, flags);
-        rms_lane_sq<DT, 1>(rs, acc, cs);
+#pragma unroll 1
+    for (int c = lane; c < N; c += 64) {
+        float v = load_elem<DT>(xrow + (size_t)c * ES);
+        if (flags & kRmsResidual) {
+            v = v + load_elem<DT>(rrow + (size_t)c * ES);
+            if constexpr (DT != kF32) v = unpack2<DT>(pack2<DT>(v, 0.f)).x;  // one rounding
+        }
+        if constexpr (DT == kF32) {
+            const float pr = v * v;
+            cs.add(pr);
+            cs.lo += __builtin_fmaf(v, v, -pr);
+        } else {
+            acc = __builtin_fmaf(v, v, acc);
+        }
     }
     if constexpr (DT == kF32) {
-        cs = row_csum<B>(cs, lds_hi, lds_lo);
+        cs = group_allreduce_csum<64>(cs);
     } else {
-        cs.hi = row_sum<B>(acc, lds_hi);
+        cs.hi = group_allreduce<64>(acc, OpAdd{});
         cs.lo = 0.f;
     }
-    hi = cs.hi;
-    lo = cs.lo;
+    return cs;
 }
 
 // mode 0: publish, wait for the row's slices, apply (one launch); mode 1: publish
@@ -226,6 +235,8 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
 
     const int lane = threadIdx.x;
     const int64_t items = M * P;
+    __shared__ int64_t failed[kSplitMaxDeferred];  // items whose wait ran out (recompute)
+    int n_failed = 0;                               // uniform over the workgroup
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int64_t row = item / P;
         const int p = (int)(item - row * P);
@@ -262,16 +273,42 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
         float rstd = rms_scale(lds_stat[1], lds_stat[2], N, eps);
         if (!ok) {
             if (lane == 0 && sync) atomicAdd(&sync->failures, 1u);
-            if (flags & kRmsRecompute) {
-                float hi, lo;
-                rms_row_sq<DT, NT>(g, r + row * r_sb, wvec, xrow, N, flags, lds_hi, lds_lo, hi, lo);
-                rstd = rms_scale(hi, lo, N, eps);
-            } else {
-                rstd = __builtin_nanf("");
+            if ((flags & kRmsRecompute) && n_failed < kSplitMaxDeferred) {  // written after the loop
+                if (lane == 0) failed[n_failed] = item;
+                ++n_failed;
+                __syncthreads();
+                continue;
             }
+            rstd = __builtin_nanf("");
         }
         rms_store<DT, V>(rs, rw, rstd, y + row * y_sb, s_out + row * s_sb, g, N, w0, B, wend, flags);
         __syncthreads();  // lds_stat is rewritten by the next item's gather
+    }
+    // Slices whose wait ran out: wave 0 forms the row's sum of squares from the whole
+    // input rows, then every lane rewrites its windows of y (and s) from a re-read.
+    for (int f = 0; f < n_failed; ++f) {
+        const int64_t item = failed[f];
+        const int64_t row = item / P;
+        const int p = (int)(item - row * P);
+        const unsigned char* xrow = x + row * x_sb;
+        const RowGeom<DT> g(xrow, N);
+        if (lane < 64) {
+            const CSum q = wave_row_sq<DT>(xrow, r + row * r_sb, N, flags);
+            if (lane == 0) {
+                lds_stat[1] = q.hi;
+                lds_stat[2] = q.lo;
+            }
+        }
+        __syncthreads();
+        const float rstd = rms_scale(lds_stat[1], lds_stat[2], N, eps);
+        const int64_t wend = ((int64_t)p * S + S < g.nwin) ? (int64_t)p * S + S : g.nwin;
+#pragma unroll 1
+        for (int64_t w = (int64_t)p * S + lane; w < wend; w += B) {
+            uint32_t fs[1][4], fw[1][4];
+            rms_load<DT, 1, NT>(fs, fw, g, r + row * r_sb, wvec, xrow, N, w, 0, wend, flags);
+            rms_store<DT, 1>(fs, fw, rstd, y + row * y_sb, s_out + row * s_sb, g, N, w, 0, wend, flags);
+        }
+        __syncthreads();
     }
 }
 

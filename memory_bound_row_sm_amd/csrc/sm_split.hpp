@@ -31,11 +31,14 @@
 // write-back or invalidate is needed, and no slot is ever cleared: a stale word
 // carries another call's tag. Every wait is bounded (spin_limit polls per
 // workgroup), so a kernel always drains. A workgroup that runs out counts the
-// failure and, when the output does not alias the input (`recompute`), derives
-// the row's statistics itself from the whole input row -- the same definition, in
-// another summation order -- so the result does not depend on scheduling; in place,
-// where the row's other slices may already have overwritten their input, it writes
-// NaN over its slice instead.
+// failure and, when the output does not alias the input (`recompute`), leaves that
+// slice for after its item loop: there wave 0 derives the row's statistics from the
+// whole input row -- the same definition, in another summation order -- and the
+// workgroup writes the slice from a re-read of its input, so the result does not
+// depend on scheduling. (Done inside the loop, the fallback's registers added to the
+// live slice and cut the occupancy of the common path; after the loop nothing of a
+// slice is live.) In place, where the row's other slices may already have
+// overwritten their input, it writes NaN over its slice instead.
 #pragma once
 
 #include "sm_bwd.hpp"
@@ -129,64 +132,93 @@ __device__ __forceinline__ void split_gather(const SplitSlot* row_slots, int P, 
     }
 }
 
-// Fallback after a wait ran out: the whole workgroup walks the entire input row
-// (window grid as in the slice loads, 256 windows per step) twice -- the row
-// maximum, then the sum of exp(x - max) with the same exponential as the slices --
-// and returns (m, s_hi, s_lo) on every lane.
+// Wave 0's fallback after a wait ran out: its 64 lanes walk the whole input row
+// (16-byte windows lane, lane + 64, ...) with a per-lane online (max, sum), two
+// elements at a time, merged over the wave afterwards: the same definition as the
+// slices' statistics, in another order. Kept small: it shares the kernel's register
+// budget with the hot path.
 template <int DT, bool NT>
-__device__ __noinline__ void split_row_stats(const RowGeom<DT> g, int N, float* lds_a,
-                                             float* lds_b, float* lds_c, float& m, float& s_hi,
-                                             float& s_lo) {
+__device__ __forceinline__ void wave_row_stats(const RowGeom<DT>& g, int N, float& m, CSum& s) {
     constexpr int E = Elem<DT>::per_vec;
-    constexpr int B = kSplitBlock;
-    const int lane = threadIdx.x;
-    auto window = [&](int64_t w, float (&x)[E]) {
+    const int lane = threadIdx.x & 63;
+    m = kNegInf;
+    s = CSum{};
+#pragma unroll 1
+    for (int w = lane; w < g.nwin; w += 64) {
+        const uint4 raw = load16<NT>(g.base + 16 * (size_t)w);
+        const uint32_t word[4] = {raw.x, raw.y, raw.z, raw.w};
+        const int c0 = w * E - g.head;
+#pragma unroll
+        for (int k = 0; k < E; k += 2) {
+            float a, b;
+            if constexpr (DT == kF32) {
+                a = __uint_as_float(word[k]);
+                b = __uint_as_float(word[k + 1]);
+            } else {
+                const f2_t pr = unpack2<DT>(word[k / 2]);
+                a = pr.x;
+                b = pr.y;
+            }
+            if (c0 + k < 0 || c0 + k >= N) a = kNegInf;
+            if (c0 + k + 1 < 0 || c0 + k + 1 >= N) b = kNegInf;
+            const float pm = fmax_nan(a, b);
+            const float sh = (pm == kNegInf) ? 0.f : pm;  // shift 0 for an all -inf pair
+            if constexpr (DT == kF32) {
+                CSum c;
+                c.add(exp_diff_acc(a, sh));
+                c.add(exp_diff_acc(b, sh));
+                merge_acc(m, s, pm, c);
+            } else {
+                merge_fast(m, s.hi, pm, exp2_fast((a - sh) * kLog2e) + exp2_fast((b - sh) * kLog2e));
+            }
+        }
+    }
+    if constexpr (DT == kF32) {
+        group_merge_acc<64>(m, s);
+    } else {
+        group_merge_fast<64>(m, s.hi);
+    }
+}
+
+// Fallback output of one slice: its windows re-read one at a time and written as
+// exp(x - m) / s with the row statistics (m, s) of wave_row_stats.
+template <int DT, int V, bool NT>
+__device__ __forceinline__ void split_write_from_input(const RowGeom<DT>& g, int N, int64_t w0,
+                                                       int64_t wend, unsigned char* orow,
+                                                       int same_phase, float m, float s) {
+    constexpr int E = Elem<DT>::per_vec;
+    constexpr int ES = Elem<DT>::bytes;
+    const float r = (s == 0.f) ? 0.f : 1.0f / s;
+    const float ms = (m == kNegInf) ? 0.f : m;
+#pragma unroll 1
+    for (int64_t w = w0; w < wend; w += kSplitBlock) {
+        float x[E], y[E];
         decode<DT>(load16<NT>(g.base + 16 * (size_t)w), x);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            if constexpr (DT == kF32) {
+                y[k] = exp_diff_acc(x[k], ms) * r;
+            } else {
+                y[k] = exp2_fast((x[k] - ms) * kLog2e) * r;
+            }
+        }
+        const uint4 enc = encode<DT>(y);
         const int64_t c0 = w * E - g.head;
-        if (c0 < 0 || c0 + E > N) {
+        if (same_phase && c0 >= 0 && c0 + E <= N) {
+            store16(orow + (size_t)c0 * ES, enc);
+        } else {
 #pragma unroll
             for (int k = 0; k < E; ++k) {
                 const int64_t c = c0 + k;
-                if (c < 0 || c >= N) x[k] = kNegInf;
+                if (c >= 0 && c < N) store_elem<DT>(orow + (size_t)c * ES, enc, k);
             }
         }
-    };
-    float lm = kNegInf;
-    for (int64_t w = lane; w < g.nwin; w += B) {
-        float x[E];
-        window(w, x);
-#pragma unroll
-        for (int k = 0; k + 1 < E; k += 2) lm = max3f(lm, x[k], x[k + 1]);
-    }
-    m = row_max<B>(lm, lds_a);
-    const float ms = (m == kNegInf) ? 0.f : m;
-    if constexpr (DT == kF32) {
-        CSum cs;
-        for (int64_t w = lane; w < g.nwin; w += B) {
-            float x[E];
-            window(w, x);
-#pragma unroll
-            for (int k = 0; k < E; ++k) cs.add(exp_diff_acc(x[k], ms));
-        }
-        cs = row_csum<B>(cs, lds_b, lds_c);
-        s_hi = cs.hi;
-        s_lo = cs.lo;
-    } else {
-        const bool fast = __builtin_fabsf(ms) <= 0x1p125f;
-        const float mL = ms * kLog2e;
-        float acc = 0.f;
-        for (int64_t w = lane; w < g.nwin; w += B) {
-            float x[E];
-            window(w, x);
-#pragma unroll
-            for (int k = 0; k < E; ++k)
-                acc += fast ? exp2_fast(__builtin_fmaf(x[k], kLog2e, -mL))
-                            : exp2_fast((x[k] - ms) * kLog2e);
-        }
-        s_hi = row_sum<B>(acc, lds_b);
-        s_lo = 0.f;
     }
 }
+
+// Slices per workgroup whose output is deferred after a timed-out wait (one per round;
+// further timed-out slices of a workgroup with more rounds than this are written NaN)
+constexpr int kSplitMaxDeferred = 32;
 
 template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
@@ -202,6 +234,8 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
 
     const int lane = threadIdx.x;
     const int64_t items = M * P;
+    __shared__ int64_t failed[kSplitMaxDeferred];  // items whose wait ran out (out of place)
+    int n_failed = 0;                               // uniform over the workgroup
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int64_t row = item / P;
         const int p = (int)(item - row * P);
@@ -276,16 +310,19 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
         }
         split_gather<DT>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
-        float m = lds_stat[0];
-        float s = csum_value(lds_stat[1], lds_stat[2]);
-        bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
+        const float m = lds_stat[0];
+        const float s = csum_value(lds_stat[1], lds_stat[2]);
+        const bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
+        unsigned char* orow = out + row * out_sb;
         if (!ok) {
             if (lane == 0) atomicAdd(&sync->failures, 1u);
-            if (recompute) {
-                float hi, lo;
-                split_row_stats<DT, NT>(g, N, lds_a, lds_b, lds_c, m, hi, lo);
-                s = csum_value(hi, lo);
-                ok = true;
+            if (recompute && n_failed < kSplitMaxDeferred) {
+                // out of place: the slice is written after the item loop, from the
+                // input, once no slice data is live (see below)
+                if (lane == 0) failed[n_failed] = item;
+                ++n_failed;
+                __syncthreads();  // lds_stat is rewritten by the next item's gather
+                continue;
             }
         }
 
@@ -299,7 +336,6 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
         }
         if (!ok) r = __builtin_nanf("");
         const float mr = (m == kNegInf) ? 0.f : m;
-        unsigned char* orow = out + row * out_sb;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int64_t w = w0 + (int64_t)B * v;
@@ -327,6 +363,29 @@ k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, S
             }
         }
         __syncthreads();  // lds_stat is rewritten by the next item's gather
+    }
+    // Slices whose wait ran out: wave 0 forms the row's statistics from the whole input
+    // row, then every lane rewrites its windows of the slice from the input.
+    for (int f = 0; f < n_failed; ++f) {
+        const int64_t item = failed[f];
+        const int64_t row = item / P;
+        const int p = (int)(item - row * P);
+        const RowGeom<DT> g(in + row * in_sb, N);
+        const int64_t w0 = (int64_t)p * S + lane;
+        const int64_t wend = ((int64_t)p * S + S < g.nwin) ? (int64_t)p * S + S : g.nwin;
+        if (lane < 64) {
+            float mf;
+            CSum sf;
+            wave_row_stats<DT, NT>(g, N, mf, sf);
+            if (lane == 0) {
+                lds_stat[0] = mf;
+                lds_stat[1] = csum_value(sf.hi, sf.lo);
+            }
+        }
+        __syncthreads();
+        split_write_from_input<DT, V, NT>(g, N, w0, wend, out + row * out_sb, same_phase, lds_stat[0],
+                                          lds_stat[1]);
+        __syncthreads();
     }
 }
 
@@ -363,29 +422,33 @@ __device__ __forceinline__ void split_gather_sum(const SplitSlot* row_slots, int
     }
 }
 
-// Backward fallback after a wait ran out: the workgroup forms the row's whole dot
-// product sum(y * dy) from the inputs (256 windows per step), on every lane.
-template <int DT, bool NT>
-__device__ __noinline__ float split_row_dot(const RowGeom<DT> g, const unsigned char* dyrow, int N,
-                                            int dy_phase, float* lds_hi, float* lds_lo) {
-    constexpr int E = Elem<DT>::per_vec;
-    constexpr int B = kSplitBlock;
-    const int lane = threadIdx.x;
+// Backward fallback after a wait ran out: wave 0's 64 lanes form the row's whole dot
+// product sum(y * dy) from the inputs, element by element (compensated with exact
+// products for FP32 data, as the slices), reduced over the wave.
+template <int DT>
+__device__ __forceinline__ float wave_row_dot(const unsigned char* yrow, const unsigned char* dyrow,
+                                              int N) {
+    constexpr int ES = Elem<DT>::bytes;
+    const int lane = threadIdx.x & 63;
     float acc = 0.f;
     CSum cs;
-    for (int64_t w = lane; w < g.nwin; w += B) {
-        float fy[1][E], fd[1][E];
-        decode<DT>(load16<NT>(g.base + 16 * (size_t)w), fy[0]);
-        load_dy<DT, 1>(fd, dyrow, g.head, N, w, 0, g.nwin, dy_phase != 0);
-        zero_outside<DT, 1>(fy, g.head, N, w, 0);
-        zero_outside<DT, 1>(fd, g.head, N, w, 0);
-        lane_dot<DT, 1>(fy, fd, acc, cs);
+#pragma unroll 1
+    for (int c = lane; c < N; c += 64) {
+        const float a = load_elem<DT>(yrow + (size_t)c * ES);
+        const float b = load_elem<DT>(dyrow + (size_t)c * ES);
+        if constexpr (DT == kF32) {
+            const float pr = a * b;
+            cs.add(pr);
+            cs.lo += __builtin_fmaf(a, b, -pr);  // the product's exact rounding error
+        } else {
+            acc = __builtin_fmaf(a, b, acc);
+        }
     }
     if constexpr (DT == kF32) {
-        cs = row_csum<B>(cs, lds_hi, lds_lo);
+        cs = group_allreduce_csum<64>(cs);
         return csum_value(cs.hi, cs.lo);
     } else {
-        return row_sum<B>(acc, lds_hi);
+        return group_allreduce<64>(acc, OpAdd{});
     }
 }
 
@@ -405,6 +468,8 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
 
     const int lane = threadIdx.x;
     const int64_t items = M * P;
+    __shared__ int64_t failed[kSplitMaxDeferred];  // items whose wait ran out (out of place)
+    int n_failed = 0;                               // uniform over the workgroup
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int64_t row = item / P;
         const int p = (int)(item - row * P);
@@ -452,10 +517,15 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
         split_gather_sum<DT == kF32>(row_slots, P, tag, spin_limit, lds_stat);
         __syncthreads();
         const bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
-        float dot = ok ? csum_value(lds_stat[1], lds_stat[2]) : __builtin_nanf("");
+        const float dot = ok ? csum_value(lds_stat[1], lds_stat[2]) : __builtin_nanf("");
         if (!ok) {
             if (lane == 0) atomicAdd(&sync->failures, 1u);
-            if (recompute) dot = split_row_dot<DT, NT>(g, dy + row * dy_sb, N, dy_phase, lds_hi, lds_lo);
+            if (recompute && n_failed < kSplitMaxDeferred) {  // written after the loop
+                if (lane == 0) failed[n_failed] = item;
+                ++n_failed;
+                __syncthreads();
+                continue;
+            }
         }
 
         unsigned char* dxrow = dx + row * dx_sb;
@@ -472,6 +542,30 @@ k_softmax_bwd_split(const unsigned char* y, const unsigned char* dy, unsigned ch
                 decode_words<DT>(rd[v], fd[0]);
                 store_dx<DT, 1>(fy, fd, dot, dxrow, g.head, N, w, 0, g.nwin, dx_phase);
             }
+        }
+        __syncthreads();
+    }
+    // Slices whose wait ran out: wave 0 forms the row's dot from the whole input rows,
+    // then every lane rewrites its windows of dx from a re-read of y and dy.
+    for (int f = 0; f < n_failed; ++f) {
+        const int64_t item = failed[f];
+        const int64_t row = item / P;
+        const int p = (int)(item - row * P);
+        const RowGeom<DT> g(y + row * y_sb, N);
+        const unsigned char* dyrow = dy + row * dy_sb;
+        if (lane < 64) {
+            const float d = wave_row_dot<DT>(y + row * y_sb, dyrow, N);
+            if (lane == 0) lds_stat[1] = d;
+        }
+        __syncthreads();
+        const float d = lds_stat[1];
+        const int64_t wend = ((int64_t)p * S + S < g.nwin) ? (int64_t)p * S + S : g.nwin;
+#pragma unroll 1
+        for (int64_t w = (int64_t)p * S + lane; w < wend; w += B) {
+            float fy[1][E], fd[1][E];
+            decode<DT>(load16<NT>(g.base + 16 * (size_t)w), fy[0]);
+            load_dy<DT, 1>(fd, dyrow, g.head, N, w, 0, g.nwin, dy_phase != 0);
+            store_dx<DT, 1>(fy, fd, d, dx + row * dx_sb, g.head, N, w, 0, g.nwin, dx_phase);
         }
         __syncthreads();
     }

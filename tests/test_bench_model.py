@@ -175,3 +175,23 @@ def test_traffic_table_groups_calls_at_cache_sweeps(tmp_path):
         json.dump(man, f)
     with pytest.raises(RuntimeError, match="dispatches"):
         bench.traffic_table(str(tmp_path / "m.json"), str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+
+
+def test_sweep_table_from_a_log(tmp_path):
+    """The per-config table: the automatic plan's time against the same-run copy of the
+    same bytes, and the MALL flag from the model bytes."""
+    log = tmp_path / "sweep.log"
+    rows = [
+        {"workload": "normal_bf16_4096x4096", "op": "forward", "copy_ceiling_bytes": 67108864,
+         "copy_us": 10.9, "copy_shape": "grid 1024", "copy_GBps": 6156.8},
+        {"workload": "normal_bf16_4096x4096", "plan": "auto", "resolved": "persistent", "G": 256,
+         "V": 2, "cpw": 0, "grid": 2048, "model_bytes": 67108864, "mean_us": 11.8, "median_us": 11.7,
+         "GBps": 5687.2, "pct_peak": 71.09, "frac_of_copy": 0.9237, "mall_resident": True},
+        {"workload": "normal_bf16_4096x4096", "op": "backward", "plan": "auto", "mean_us": 17.0},
+    ]
+    log.write_text("".join("[sweep] " + json.dumps(r) + "\n" for r in rows))
+    t = bench.sweep_table(str(log))
+    line = [ln for ln in t.splitlines() if ln.startswith("| c2 |")][0]
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    assert cells[2] == "persistent" and cells[3] == "67,108,864" and cells[4] == "11.80"
+    assert cells[7] == "10.90" and cells[9] == "0.924" and cells[10] == "yes"

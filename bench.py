@@ -211,6 +211,10 @@ def main(argv=None) -> int:
                     help="HBM bytes per call of every sweep case from the counter pass's manifest "
                          "and its FETCH_SIZE and WRITE_SIZE runs (markdown on stdout), and exit")
     ap.add_argument("--sq-csv", help="with --traffic-table: an SQ counter run of the same pass")
+    ap.add_argument("--bytes-fit", action="store_true",
+                    help="cold time against bytes (16 MiB - 1 GiB) for the softmax and the copy, "
+                         "with a least-squares fit t = a + bytes / B of each; prints a table")
+    ap.add_argument("--fit-table", metavar="FIT_JSON", help="print a --bytes-fit result as markdown")
     ap.add_argument("--sweep-table", metavar="SWEEP_LOG",
                     help="print the per-config table (time, %% of 8 TB/s, copy ceiling) of a "
                          "--sweep log and exit")
@@ -231,6 +235,10 @@ def main(argv=None) -> int:
         return 0
     if args.sweep_table:
         print(sweep_table(args.sweep_table))
+        return 0
+    if args.fit_table:
+        with open(args.fit_table) as f:
+            print(fit_table(json.loads(f.read().strip().splitlines()[-1])))
         return 0
     if args.score_grid:
         with open(args.score_grid) as f:
@@ -259,6 +267,8 @@ def main(argv=None) -> int:
 
     if args.plan_grid:
         return plan_grid(torch, sm, s_handle, log, args)
+    if args.bytes_fit:
+        return bytes_fit(torch, sm, s_handle, make_flush(torch, sm, s_handle), log, args)
     if args.counter_pass:
         return counter_pass(torch, sm, workloads, make_flush(torch, sm, s_handle), s_handle,
                             args.counter_pass, 64 << 20, log)
@@ -927,8 +937,9 @@ def softmax_groups(torch, sm, workloads, s_handle, clocks_up=None):
 # bytes can be served partly from it even after the 1 GiB sweep, on its write-backs
 MALL_BYTES = 256 << 20
 # copy-ceiling launch shapes: (workgroups, store policy) -- device-scope (sc1) stores are
-# the row kernels' own policy
-COPY_SHAPES = [(1024, 1), (4096, 1), (16384, 1), (1024, 0), (4096, 0), (16384, 0)]
+# the row kernels' own policy; workgroups 0: one 16-byte vector per thread (a grid that
+# covers the copy once, like the resident row plans)
+COPY_SHAPES = [(1024, 1), (4096, 1), (16384, 1), (0, 1), (1024, 0), (4096, 0), (16384, 0), (0, 0)]
 
 
 def copy_calls(torch, sm, s_handle, model_bytes: int):
@@ -939,6 +950,7 @@ def copy_calls(torch, sm, s_handle, model_bytes: int):
     dst = torch.empty_like(src)
     out = []
     for grid, scope in COPY_SHAPES:
+        grid = grid or -(-(n // 16) // 256)
         def call(events=(None, None), grid=grid, scope=scope):
             rc = sm.sm_bench_copy(src.data_ptr(), dst.data_ptr(), n, grid, scope, s_handle, *events)
             if rc != 0:
@@ -991,6 +1003,83 @@ def sweep(torch, sm, workloads, flush, s_handle, log, args):
                 line.update(check())
             log("[sweep] " + json.dumps(line))
         del copies
+
+
+# series of the bytes fit: (dtype, row width, row counts) -- BF16 rows of 4096 (the
+# headline's rows) and FP16 rows of 2048, 16 MiB to 1 GiB of model bytes
+FIT_SERIES = [("bf16", 4096, (1024, 2048, 4096, 8192, 16384, 32768, 65536)),
+              ("f16", 2048, (2048, 4096, 8192, 16384, 32768, 65536, 131072))]
+
+
+def linfit(xs, ys):
+    """Least-squares line y = a + b x: (a, b)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    return my - b * mx, b
+
+
+def bytes_fit(torch, sm, s_handle, flush, log, args) -> int:
+    """Cold time of the automatic softmax plan and of the best copy shape moving the same
+    bytes, at sizes from 16 MiB to 1 GiB, each series fitted as t = a + bytes / B: the
+    intercept a is the fixed cost of a call (launch, ramp, tail), B its streaming rate.
+    The headline's gap to the copy splits into the difference of intercepts and of
+    slopes."""
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}
+    code = {"bf16": sm.SM_BF16, "f16": sm.SM_F16}
+    steps = max(50, args.steps // 2)
+    out = {"series": []}
+    for dt, N, rows in FIT_SERIES:
+        pts = []
+        for M in rows:
+            x = torch.randn(M, N, device="cuda").to(tdt[dt])
+            y = torch.empty_like(x)
+            o = sm.SmOpts()
+
+            def call(events=(None, None), x=x, y=y, M=M, o=o):
+                o.start_event, o.stop_event = events
+                rc = sm.sm_softmax_fwd_ex(x.data_ptr(), y.data_ptr(), M, N, N, N, code[dt], o, 0, 0,
+                                          s_handle)
+                if rc != 0:
+                    raise sm.SoftmaxError(rc)
+            info = sm.plan_for(x, y)
+            model = info["model_bytes"]
+            copies = copy_calls(torch, sm, s_handle, model)
+            st = time_rotating(torch, [call] + [c[1] for c in copies], flush, steps, 5)
+            k = 1 + min(range(len(copies)), key=lambda i: st[1 + i]["mean_us"])
+            pt = {"M": M, "N": N, "dtype": dt, "plan": info["plan_name"], "model_bytes": model,
+                  "softmax_us": round(st[0]["mean_us"], 3), "copy_us": round(st[k]["mean_us"], 3),
+                  "copy_shape": copies[k - 1][0]}
+            log("[fit] " + json.dumps(pt))
+            pts.append(pt)
+            del x, y, copies
+            torch.cuda.empty_cache()
+        xs = [p["model_bytes"] for p in pts]
+        fits = {}
+        for key in ("softmax_us", "copy_us"):
+            a, b = linfit(xs, [p[key] for p in pts])
+            fits[key] = {"intercept_us": round(a, 3), "GBps": round(1e-3 / b, 1)}
+        out["series"].append({"dtype": dt, "N": N, "points": pts, "fit": fits})
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def fit_table(d: dict) -> str:
+    """Markdown of a --bytes-fit result."""
+    lines = []
+    for ser in d["series"]:
+        f = ser["fit"]
+        lines += [f"{ser['dtype'].upper()} rows of {ser['N']}: softmax t = "
+                  f"{f['softmax_us']['intercept_us']:.2f} us + bytes / {f['softmax_us']['GBps']:.0f} GB/s; "
+                  f"copy t = {f['copy_us']['intercept_us']:.2f} us + bytes / {f['copy_us']['GBps']:.0f} GB/s",
+                  "", "| M | plan | model bytes | softmax µs | copy µs | softmax / copy time | copy shape |",
+                  "|---:|---|---:|---:|---:|---:|---|"]
+        for p in ser["points"]:
+            lines.append(f"| {p['M']} | {p['plan']} | {p['model_bytes']:,} | {p['softmax_us']:.2f} | "
+                         f"{p['copy_us']:.2f} | {p['softmax_us'] / p['copy_us']:.3f} | {p['copy_shape']} |")
+        lines.append("")
+    return "\n".join(lines)
 
 
 # the configurations of the forward softmax hot path, in the order they are tabled

@@ -195,3 +195,17 @@ def test_sweep_table_from_a_log(tmp_path):
     cells = [c.strip() for c in line.strip("|").split("|")]
     assert cells[2] == "persistent" and cells[3] == "67,108,864" and cells[4] == "11.80"
     assert cells[7] == "10.90" and cells[9] == "0.924" and cells[10] == "yes"
+
+
+def test_bytes_fit_line_and_table():
+    """The least-squares line of the bytes fit recovers an exact line, and the table
+    reports the fitted intercept and rate."""
+    xs = [16 << 20, 32 << 20, 64 << 20, 1 << 30]
+    a, b = bench.linfit(xs, [2.5 + x / 6e6 for x in xs])  # 2.5 us + bytes / 6 TB/s (us)
+    assert abs(a - 2.5) < 1e-9 and abs(1e-3 / b - 6000) < 1e-6
+    d = {"series": [{"dtype": "bf16", "N": 4096, "fit": {
+        "softmax_us": {"intercept_us": 3.1, "GBps": 6800.0}, "copy_us": {"intercept_us": 2.5, "GBps": 6900.0}},
+        "points": [{"M": 4096, "plan": "persistent", "model_bytes": 67108864, "softmax_us": 11.8,
+                    "copy_us": 10.9, "copy_shape": "grid 1024"}]}]}
+    t = bench.fit_table(d)
+    assert "3.10 us + bytes / 6800 GB/s" in t and "| 4096 | persistent | 67,108,864 | 11.80 | 10.90 | 1.083 |" in t

@@ -220,8 +220,19 @@ __device__ __forceinline__ void split_write_from_input(const RowGeom<DT>& g, int
 // further timed-out slices of a workgroup with more rounds than this are written NaN)
 constexpr int kSplitMaxDeferred = 32;
 
+// Waves per SIMD requested of the 4-vector forward instances: 8, i.e. at most 64 VGPRs
+// and about 80 SGPRs (the rest spill to VGPR lanes). Left to itself the compiler takes
+// 105 SGPRs, which allows 7 waves, and rows of 16 slices of 4 vectors then fill only 7/8
+// of a round (measured, MI355X, cold: BF16 64 x 131072 9.32 -> 8.8 us, 1024 x 131072 120.7
+// -> 112.7 us, FP32 64 x 65536 12.86 -> 12.1 us; the spills cost 2-3% where the plan
+// does not change, e.g. 1 x 2^20 BF16 5.68 -> 5.81 us). Other instances keep the
+// compiler's choice.
+template <int V>
+constexpr int kSplitWaves = V == 4 ? 8 : 1;
+
 template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
+__attribute__((amdgpu_waves_per_eu(kSplitWaves<V>)))
 k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, SplitSync* sync,
                 int64_t M, int N, int64_t in_sb, int64_t out_sb, int P, int S, uint32_t tag,
                 int spin_limit, int same_phase, int recompute) {

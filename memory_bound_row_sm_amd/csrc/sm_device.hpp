@@ -103,7 +103,10 @@ __device__ __forceinline__ uint4 load16(const unsigned char* p) {
 // dirty output lines to write back. Measured cold on MI355X against plain stores:
 // BF16 4096 x 4096 softmax 12.11 -> 11.80 us, FP16 8192 x 2048 -8%, BF16 64 x 131072
 // (SPLIT) -16%, 158 plan/workload cells -2.4% geomean; nontemporal stores were 6-12%
-// slower. No builtin emits a 16-byte global store with a scope bit, hence the asm.
+// slower. No builtin emits a 16-byte global store with a scope bit, hence the asm;
+// the compiler-visible alternative, two 8-byte relaxed device-scope atomic stores per
+// vector, writes half lines through the L2 and ran 2.2-2.7x slower on every large
+// shape (BF16 4096 x 4096 11.8 -> 27.5 us, causal 524288 x 2048 617 -> 1443 us).
 // A store of more than 8 bytes reads its data VGPRs after it issues, and a VALU
 // write of those VGPRs must wait two wait states (gfx940 and later). The compiler
 // pads its own stores for this but cannot see inside an asm block, so the block

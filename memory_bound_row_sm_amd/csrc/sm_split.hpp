@@ -225,14 +225,17 @@ constexpr int kSplitMaxDeferred = 32;
 // 105 SGPRs, which allows 7 waves, and rows of 16 slices of 4 vectors then fill only 7/8
 // of a round (measured, MI355X, cold: BF16 64 x 131072 9.32 -> 8.8 us, 1024 x 131072 120.7
 // -> 112.7 us, FP32 64 x 65536 12.86 -> 12.1 us; the spills cost 2-3% where the plan
-// does not change, e.g. 1 x 2^20 BF16 5.68 -> 5.81 us). Other instances keep the
+// does not change, e.g. 1 x 2^20 BF16 5.68 -> 5.81 us). The FP32 1- and 8-vector
+// instances, which FP32 rows take for few and for many rows per call, are held at the
+// occupancy they had before the timed-out-slice fallback was added (8 and 6 waves; the
+// fallback's code otherwise cost each of them a wave). Other instances keep the
 // compiler's choice.
-template <int V>
-constexpr int kSplitWaves = V == 4 ? 8 : 1;
+template <int DT, int V>
+constexpr int kSplitWaves = V == 4 ? 8 : (DT == kF32 && V == 1) ? 8 : (DT == kF32 && V == 8) ? 6 : 1;
 
 template <int DT, int V, bool NT>
 __global__ void __launch_bounds__(kSplitBlock)
-__attribute__((amdgpu_waves_per_eu(kSplitWaves<V>)))
+__attribute__((amdgpu_waves_per_eu(kSplitWaves<DT, V>)))
 k_softmax_split(const unsigned char* in, unsigned char* out, SplitSlot* slots, SplitSync* sync,
                 int64_t M, int N, int64_t in_sb, int64_t out_sb, int P, int S, uint32_t tag,
                 int spin_limit, int same_phase, int recompute) {

@@ -280,6 +280,34 @@ def test_plan_forcing_and_limits():
     assert p["grid"] == 256 * 8  # occupancy assumed 8 workgroups per CU on the host path
 
 
+def test_plan_grid_capped_at_2_32_threads():
+    """A dispatch counts its work-items in 32 bits: one-pass grids are capped at 2^32 - 1
+    threads and the row kernels stride over the rows beyond (64-bit row indices), forward,
+    backward and RMSNorm alike; the two-pass WIDE plan, which gives every wave fixed
+    chunks, refuses a grid it cannot launch."""
+    M = 1 << 34  # rows of 2 BF16 elements: 2^30 workgroups of 16 rows would be needed
+    cap = 0xFFFFFFFF
+    for opts in (None, {"plan": sm.SM_PLAN_RESIDENT}, {"plan": sm.SM_PLAN_PERSISTENT}):
+        rc, info = sm.sm_softmax_plan_query(1 << 40, 1 << 41, M, 2, 2, 2, BF16, opts, 256)
+        p = info.as_dict()
+        assert rc == OK and p["plan_name"] in ("resident", "persistent"), (opts, rc, p)
+        rows_per_group = p["block"] // p["lanes_per_row"]
+        assert p["grid"] * p["block"] <= cap
+        if p["plan_name"] == "resident":
+            assert p["grid"] == cap // p["block"] < M // rows_per_group
+        rc, info = sm.sm_softmax_bwd_plan_query(1 << 40, 1 << 41, 1 << 42, M, 2, 2, 2, 2, BF16,
+                                                opts, 256)
+        p = info.as_dict()
+        assert rc == OK and p["grid"] * p["block"] <= cap, (opts, rc, p)
+        rc, info = sm.sm_rmsnorm_plan_query(1 << 40, 2 << 40, 3 << 40, 4 << 40, 0, M, 2, 2, 2, 2,
+                                            2, 1e-6, BF16, opts, 256)
+        p = info.as_dict()
+        assert rc == OK and p["grid"] * p["block"] <= cap, (opts, rc, p)
+    rc, _ = sm.sm_softmax_plan_query(1 << 40, 1 << 41, M, 2, 2, 2, BF16, {"plan": sm.SM_PLAN_WIDE},
+                                     256)
+    assert rc == PLAN
+
+
 def test_plan_phase_flag():
     rc, p = plan(4, 64, F16)
     assert p["same_phase"] == 1

@@ -1,0 +1,143 @@
+"""More than 2^31 rows: 2^31 + 33 rows of two BF16 elements (8 GiB per tensor).
+
+A dispatch counts its work-items in 32 bits, so one-pass grids are capped at 2^32 - 1
+threads and the row kernels stride over the rows beyond with 64-bit row indices. Here
+the grid is capped, rows and byte offsets pass 2^31 and 2^32, and every row of the
+forward, the backward and the residual RMSNorm is checked: against the FP64 oracle on
+sampled rows (the first rows, a band across row 2^31, 2^20 seeded random rows), and on
+every row through properties that hold exactly at any size and that an output written
+to another row would break."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_sm_amd as sm
+from parity import compare, compare_bwd, compare_rms, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+M = (1 << 31) + 33
+N = 2
+CHUNK = 1 << 28  # rows per generation / check step
+U = 2.0 ** -8    # BF16 ulp of [1/2, 1): half of it bounds one rounding of a probability
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    free, _ = torch.cuda.mem_get_info()
+    if free < (48 << 30):
+        pytest.skip(f"needs 48 GiB of free device memory, {free >> 30} GiB free")
+    sm.lib()
+
+
+def _randn(seed, scale):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    t = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    for i in range(0, M, CHUNK):
+        j = min(M, i + CHUNK)
+        t[i:j] = (torch.randn(j - i, N, generator=g, device=DEV) * scale).to(torch.bfloat16)
+    return t
+
+
+def _sample_rows():
+    rng = np.random.default_rng(2026)
+    parts = [np.arange(0, 1 << 16), np.arange((1 << 31) - (1 << 16), M),
+             rng.integers(0, M, size=1 << 20)]
+    return torch.from_numpy(np.unique(np.concatenate(parts)).astype(np.int64))
+
+
+def _grid_capped(info):
+    rows_per_group = info["block"] // info["lanes_per_row"]
+    assert info["grid"] * info["block"] <= 0xFFFFFFFF
+    assert info["grid"] * rows_per_group < M, info  # the kernels stride past the grid
+
+
+@pytest.fixture(scope="module")
+def forward():
+    x = _randn(11, 3.0)
+    y = torch.full_like(x, float("nan"))
+    info = sm.plan_for(x, y)
+    log(f"[huge] forward {M} x {N} bf16: {info['plan_name']} {info['lanes_per_row']} x "
+        f"{info['vecs_per_lane']}, grid {info['grid']} x {info['block']}")
+    _grid_capped(info)
+    sm.softmax(x, out=y)
+    torch.cuda.synchronize()
+    return x, y
+
+
+def test_forward_sampled_rows(forward):
+    x, y = forward
+    idx = _sample_rows()
+    r = compare(y[idx.to(DEV)], x[idx.to(DEV)].cpu(), what=f"{M} x {N} forward, {idx.numel()} rows")
+    log(f"[huge] forward sampled rows: {r}")
+
+
+def test_forward_every_row(forward):
+    x, y = forward
+    for i in range(0, M, CHUNK):
+        j = min(M, i + CHUNK)
+        xf, yf = x[i:j].float(), y[i:j].float()
+        assert not torch.isnan(yf).any(), (i, j)
+        # two probabilities each rounded once (within U/2 of the exact value, which sums to 1)
+        assert (yf.sum(1) - 1).abs().max().item() <= U + 1e-6, (i, j)
+        # the larger input keeps the larger (or an equal) probability
+        d, e = xf[:, 0] - xf[:, 1], yf[:, 0] - yf[:, 1]
+        assert not ((d > 0) & (e < 0)).any() and not ((d < 0) & (e > 0)).any(), (i, j)
+        assert ((d != 0) | (e == 0)).all(), (i, j)  # equal inputs, equal probabilities
+    log(f"[huge] forward: every row ordered and summing to 1")
+
+
+def test_backward(forward):
+    _, y = forward
+    dy = _randn(12, 1.0)
+    dx = torch.full_like(y, float("nan"))
+    info = sm.plan_for_backward(y, dy, dx=dx)
+    log(f"[huge] backward: {info['plan_name']} grid {info['grid']} x {info['block']}")
+    _grid_capped(info)
+    sm.softmax_backward(y, dy, dx=dx)
+    torch.cuda.synchronize()
+    idx = _sample_rows()
+    idd = idx.to(DEV)
+    r = compare_bwd(dx[idd], y[idd].cpu(), dy[idd].cpu(), what=f"{M} x {N} backward")
+    log(f"[huge] backward sampled rows: {r}")
+    for i in range(0, M, CHUNK):
+        j = min(M, i + CHUNK)
+        yf, gf, df = y[i:j].float(), dy[i:j].float(), dx[i:j].float()
+        assert not torch.isnan(df).any(), (i, j)
+        # the exact dx sums to S (1 - y0 - y1), S = y0 dy0 + y1 dy1, |1 - y0 - y1| <= U;
+        # each dx is then rounded once (half an ulp, relative 2^-8 at most)
+        lhs = (df[:, 0] + df[:, 1]).abs()
+        rhs = 2 * U * (yf * gf).abs().sum(1) + U * df.abs().sum(1) + 2.0 ** -125
+        assert (lhs <= rhs).all(), (i, j, (lhs - rhs).max().item())
+    del dy, dx
+    log("[huge] backward: every row's dx sums to the bound")
+
+
+def test_rmsnorm(forward):
+    x, _ = forward
+    r = _randn(13, 1.0)
+    w = torch.ones(N, dtype=torch.bfloat16, device=DEV)
+    out = torch.full_like(x, float("nan"))
+    info = sm.plan_for_rmsnorm(x, w, residual=r, out=out)
+    log(f"[huge] rmsnorm: {info['plan_name']} grid {info['grid']} x {info['block']}")
+    _grid_capped(info)
+    sm.rmsnorm(x, w, residual=r, out=out)
+    torch.cuda.synchronize()
+    idx = _sample_rows()
+    idd = idx.to(DEV)
+    res = compare_rms(out[idd], x[idd].cpu(), r[idd].cpu(), w.cpu(), 1e-6, what=f"{M} x {N} rmsnorm")
+    log(f"[huge] rmsnorm sampled rows: {res}")
+    for i in range(0, M, CHUNK):
+        j = min(M, i + CHUNK)
+        s = (x[i:j].float() + r[i:j].float()).to(torch.bfloat16).float()
+        yf = out[i:j].float()
+        assert not torch.isnan(yf).any(), (i, j)
+        # unit weight: y = s / rms(s), so y0^2 + y1^2 = 2 q / (q + eps) with q = mean(s^2);
+        # each y is rounded once (relative 2^-8 at most: the square moves by 2^-7)
+        q = (s * s).mean(1)
+        want = 2 * q / (q + 1e-6)
+        got = (yf * yf).sum(1)
+        assert ((got - want).abs() <= 2 * U * want + 1e-6).all(), (i, j)
+    log("[huge] rmsnorm: every row normalised")

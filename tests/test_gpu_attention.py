@@ -178,3 +178,38 @@ def test_running_maximum_grows_along_the_keys(causal):
     k3[:, S - 40, 0] = 60.0  # score +240 (x 0.3 scale: ~104 binades) for every query that sees it
     o, ls = run(q3, k3, v, causal, scale=0.3, lse=True)
     compare_attn(o, q3, k3, v, 0.3, causal, lse_gpu=ls, what=f"one dominant key causal={causal}")
+
+
+def test_heads_past_4_gib():
+    """2^17 heads of 256 queries and keys, d = 128, BF16, causal: 8 GiB per tensor, so
+    head offsets pass 2^32 bytes. Heads at the start, around 2^15 and 2^16, at the end and
+    32 seeded random heads against the oracle; on every head, the first query (which sees
+    only key 0) returns v_0 exactly and nothing is NaN."""
+    BH, S, d = 1 << 17, 256, 128
+    if torch.cuda.mem_get_info()[0] < (40 << 30):
+        pytest.skip("needs 40 GiB of free device memory")
+    g = torch.Generator(device=DEV).manual_seed(2026)
+
+    def make():
+        t = torch.empty(BH, S, d, dtype=torch.bfloat16, device=DEV)
+        for h in range(0, BH, 1 << 14):
+            t[h:h + (1 << 14)] = torch.randn(1 << 14, S, d, generator=g, device=DEV).to(torch.bfloat16)
+        return t
+
+    q, k, v = make(), make(), make()
+    o = torch.full_like(q, float("nan"))
+    ls = torch.full((BH * S,), float("nan"), device=DEV)
+    sm.attention(q, k, v, causal=True, out=o, lse=ls)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2026)
+    heads = sorted({0, 1, 2, (1 << 15) - 1, 1 << 15, (1 << 16) - 1, 1 << 16, (1 << 16) + 1,
+                    BH - 2, BH - 1, *rng.integers(0, BH, size=32).tolist()})
+    idx = torch.tensor(heads, device=DEV)
+    st = compare_attn(o[idx], q[idx].cpu(), k[idx].cpu(), v[idx].cpu(), 1.0 / math.sqrt(d), True,
+                      lse_gpu=ls.view(BH, S)[idx], what=f"{BH} heads x {S}, {len(heads)} heads")
+    log(f"[attn] {BH} heads past 4 GiB, {len(heads)} heads against the oracle: {st}")
+    for h in range(0, BH, 1 << 14):
+        oc = o[h:h + (1 << 14)]
+        assert not torch.isnan(oc).any(), h
+        assert torch.equal(oc[:, 0].view(torch.int16), v[h:h + (1 << 14), 0].view(torch.int16)), h
+    assert not torch.isnan(ls).any()

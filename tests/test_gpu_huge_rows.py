@@ -1,4 +1,5 @@
-"""More than 2^31 rows: 2^31 + 33 rows of two BF16 elements (8 GiB per tensor).
+"""More than 2^31 rows (2^31 + 33 rows of two BF16 elements, 8 GiB per tensor), and the
+widest row the ABI takes (2^31 - 1 BF16 elements).
 
 A dispatch counts its work-items in 32 bits, so one-pass grids are capped at 2^32 - 1
 threads and the row kernels stride over the rows beyond with 64-bit row indices. Here
@@ -7,12 +8,15 @@ forward, the backward and the residual RMSNorm is checked: against the FP64 orac
 sampled rows (the first rows, a band across row 2^31, 2^20 seeded random rows), and on
 every row through properties that hold exactly at any size and that an output written
 to another row would break."""
+import math
+
 import numpy as np
 import pytest
 import torch
 
 import memory_bound_row_sm_amd as sm
-from parity import compare, compare_bwd, compare_rms, log
+import oracle
+from parity import TOL_BWD, ULP_GATE, compare, compare_bwd, compare_rms, log, ulp
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -141,3 +145,84 @@ def test_rmsnorm(forward):
         got = (yf * yf).sum(1)
         assert ((got - want).abs() <= 2 * U * want + 1e-6).all(), (i, j)
     log("[huge] rmsnorm: every row normalised")
+
+
+# ------------------------------------------------------------------ the widest row
+# One row of N = 2^31 - 1 BF16 elements (4 GiB), the widest the ABI takes: the two-pass
+# WIDE plan, with window, chunk and element offsets past 2^31. Periodic inputs make the
+# exact result a closed form: x_i = (i mod 3) - 1 gives three values, so the softmax is
+# e^(c-2) / sum_c n_c e^(c-2) on class c = i mod 3 (n_c elements each); dy_i = ((i mod 5)
+# - 2) / 4 gives the backward on the 15 classes i mod 15. Every element of a class
+# computes the same thing and must match its class bit for bit (an element read or
+# written at a wrong offset lands in another class); each class is then held to the
+# bounds of the sampled-row comparisons (the one-ulp gate; R16).
+NW = (1 << 31) - 1
+
+
+def _classes(i, j, period):
+    return torch.arange(i, j, device=DEV, dtype=torch.int64) % period
+
+
+def _count(period):
+    return [len(range(c, NW, period)) for c in range(period)]
+
+
+@pytest.fixture(scope="module")
+def widest():
+    x = torch.empty(1, NW, dtype=torch.bfloat16, device=DEV)
+    for i in range(0, NW, CHUNK):
+        j = min(NW, i + CHUNK)
+        x[0, i:j] = (_classes(i, j, 3) - 1).to(torch.bfloat16)
+    y = torch.full_like(x, float("nan"))
+    info = sm.plan_for(x, y)
+    log(f"[huge] widest row {NW} bf16: {info['plan_name']}, {info['waves_per_row']} waves, "
+        f"{info['chunks_per_wave']} chunks per wave")
+    assert info["plan_name"] == "wide"
+    sm.softmax(x, out=y)
+    torch.cuda.synchronize()
+    return x, y
+
+
+def test_widest_row_forward(widest):
+    x, y = widest
+    n = _count(3)
+    z = sum(n[c] * math.exp(c - 2) for c in range(3))
+    exact = np.array([math.exp(c - 2) / z for c in range(3)])
+    want = oracle.decode(oracle.encode(exact, "bf16"), "bf16")  # rounded once, to nearest even
+    got = y[0, :3].double().cpu().numpy()
+    gate = ulp(want, "bf16") + ULP_GATE["bf16"][2]
+    assert (np.abs(got - want) <= gate).all(), (got, want)
+    table = y[0, :3].clone()
+    for i in range(0, NW, CHUNK):
+        j = min(NW, i + CHUNK)
+        assert torch.equal(y[0, i:j], table[_classes(i, j, 3)]), (i, j)
+    log(f"[huge] widest row forward: classes {got.tolist()} against {want.tolist()}, every element equal to its class")
+
+
+def test_widest_row_backward(widest):
+    _, y = widest
+    dy = torch.empty_like(y)
+    for i in range(0, NW, CHUNK):
+        j = min(NW, i + CHUNK)
+        dy[0, i:j] = ((_classes(i, j, 5) - 2).float() / 4).to(torch.bfloat16)
+    dx = torch.full_like(y, float("nan"))
+    info = sm.plan_for_backward(y, dy, dx=dx)
+    log(f"[huge] widest row backward: {info['plan_name']}")
+    sm.softmax_backward(y, dy, dx=dx)
+    torch.cuda.synchronize()
+    yc = y[0, :3].double().cpu().numpy()             # the forward's three values
+    dyc = np.array([(c - 2) / 4 for c in range(5)])
+    n15 = _count(15)
+    s = sum(n15[k] * yc[k % 3] * dyc[k % 5] for k in range(15))
+    sabs = sum(n15[k] * abs(yc[k % 3] * dyc[k % 5]) for k in range(15))
+    exact = np.array([yc[k % 3] * (dyc[k % 5] - s) for k in range(15)])
+    ref = oracle.decode(oracle.encode(exact, "bf16"), "bf16")
+    got = dx[0, :15].double().cpu().numpy()
+    rt, sc, at = TOL_BWD["bf16"]
+    scale = np.array([abs(yc[k % 3]) * (abs(dyc[k % 5]) + sabs) for k in range(15)])
+    assert (np.abs(got - ref) <= rt * np.abs(ref) + sc * scale + at).all(), (got, ref)
+    table = dx[0, :15].clone()
+    for i in range(0, NW, CHUNK):
+        j = min(NW, i + CHUNK)
+        assert torch.equal(dx[0, i:j], table[_classes(i, j, 15)]), (i, j)
+    log(f"[huge] widest row backward: 15 classes within R16, every element equal to its class")

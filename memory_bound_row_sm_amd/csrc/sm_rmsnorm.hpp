@@ -223,8 +223,13 @@ __device__ __forceinline__ CSum wave_row_sq(const unsigned char* xrow, const uns
 // mode 0: publish, wait for the row's slices, apply (one launch); mode 1: publish
 // only; mode 2: gather the partials published by an earlier launch and apply (every
 // word already carries the tag, so no wait can run out; `sync` may be null).
+// The 4-vector instances are held at the 6 waves per SIMD they reach without the
+// second launch's gather (80 VGPRs; left to the compiler that path costs them a wave).
+template <int V>
+constexpr int kRmsSplitWaves = V == 4 ? 6 : 1;
+
 template <int DT, int V, bool NT>
-__global__ void __launch_bounds__(kSplitBlock)
+__global__ void __launch_bounds__(kSplitBlock) __attribute__((amdgpu_waves_per_eu(kRmsSplitWaves<V>)))
 k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned char* wvec,
                 unsigned char* y, unsigned char* s_out, SplitSlot* slots, SplitSync* sync,
                 int64_t M, int N, int64_t x_sb, int64_t r_sb, int64_t y_sb, int64_t s_sb, int P,
@@ -237,6 +242,14 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
     const int64_t items = M * P;
     __shared__ int64_t failed[kSplitMaxDeferred];  // items whose wait ran out (recompute)
     int n_failed = 0;                               // uniform over the workgroup
+    // Mode 2 on rows of more than 256 slices reads partials that are all published
+    // already: a workgroup sums a row's partials with all its lanes and keeps the total
+    // while its items stay in that row (rows of more slices than the grid has
+    // workgroups). Shorter rows keep wave 0's gather, one load per lane or two.
+    const bool wide_gather = mode == 2 && P > kSplitBlock;
+    int64_t have_row = -1;  // wide_gather: the row whose total (q_hi, q_lo, q_ok) is held
+    float q_hi = 0.f, q_lo = 0.f;
+    bool q_ok = true;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int64_t row = item / P;
         const int p = (int)(item - row * P);
@@ -245,9 +258,15 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
         const int64_t w0 = (int64_t)p * S + lane;
         const int64_t wend = ((int64_t)p * S + S < g.nwin) ? (int64_t)p * S + S : g.nwin;
 
+        SplitSlot* row_slots = slots + row * P;
+        if (wide_gather && row != have_row) {  // before the slice's loads: none of it is live
+            const CSum q = split_sum_published<DT == kF32>(row_slots, P, tag, lds_hi, lds_lo, q_ok);
+            q_hi = q.hi;
+            q_lo = q.lo;
+            have_row = row;
+        }
         uint32_t rs[V][4], rw[V][4];
         rms_load<DT, V, NT>(rs, rw, g, r + row * r_sb, wvec, xrow, N, w0, B, wend, flags);
-        SplitSlot* row_slots = slots + row * P;
         if (mode != 2) {
             float acc = 0.f;
             CSum cs;
@@ -267,10 +286,17 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
             __syncthreads();  // the next item's reduction rewrites lds_hi
             continue;
         }
-        split_gather_sum<DT == kF32>(row_slots, P, tag, spin_limit, lds_stat);
-        __syncthreads();
-        const bool ok = lds_stat[3] != 0.f;  // uniform over the workgroup
-        float rstd = rms_scale(lds_stat[1], lds_stat[2], N, eps);
+        bool ok;  // uniform over the workgroup
+        float rstd;
+        if (wide_gather) {
+            ok = q_ok;
+            rstd = rms_scale(q_hi, q_lo, N, eps);
+        } else {
+            split_gather_sum<DT == kF32>(row_slots, P, tag, spin_limit, lds_stat);
+            __syncthreads();
+            ok = lds_stat[3] != 0.f;
+            rstd = rms_scale(lds_stat[1], lds_stat[2], N, eps);
+        }
         if (!ok) {
             if (lane == 0 && sync) atomicAdd(&sync->failures, 1u);
             if ((flags & kRmsRecompute) && n_failed < kSplitMaxDeferred) {  // written after the loop
@@ -282,7 +308,7 @@ k_rmsnorm_split(const unsigned char* x, const unsigned char* r, const unsigned c
             rstd = __builtin_nanf("");
         }
         rms_store<DT, V>(rs, rw, rstd, y + row * y_sb, s_out + row * s_sb, g, N, w0, B, wend, flags);
-        __syncthreads();  // lds_stat is rewritten by the next item's gather
+        __syncthreads();  // the next item's gather rewrites lds_stat (wide_gather: lds_hi, lds_lo)
     }
     // Slices whose wait ran out: wave 0 forms the row's sum of squares from the whole
     // input rows, then every lane rewrites its windows of y (and s) from a re-read.

@@ -436,6 +436,49 @@ __device__ __forceinline__ void split_gather_sum(const SplitSlot* row_slots, int
     }
 }
 
+// Gather of the second launch of a two-launch form: every word was published by the
+// earlier launch, so nothing is waited for. All lanes of the workgroup read the row's
+// slots (lane t takes slots t, t + 256, ..., four loads issued before any is used), sum
+// them in slot order with the compensated step, then reduce over the workgroup in a
+// fixed tree, so every workgroup derives bitwise the same total. `ok` is false if a word
+// lacks the tag (which the publishing launch rules out). A row of P slices costs P/256
+// independent loads per lane instead of P/64 dependent ones on one wave.
+template <bool ACC>
+__device__ __forceinline__ CSum split_sum_published(const SplitSlot* row_slots, int P, uint32_t tag,
+                                                    float* lds_hi, float* lds_lo, bool& ok) {
+    constexpr int B = kSplitBlock;
+    constexpr int U = 4;
+    const int t = threadIdx.x;
+    CSum s;
+    bool good = true;
+    for (int j0 = t; j0 < P; j0 += U * B) {
+        uint64_t hw[U], lw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * B;
+            hw[u] = lw[u] = 0;
+            if (j < P) {
+                hw[u] = __hip_atomic_load(row_slots[j].w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if constexpr (ACC)
+                    lw[u] = __hip_atomic_load(row_slots[j].w + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (j0 + u * B < P) {
+                good = good && (uint32_t)(hw[u] >> 32) == tag && (!ACC || (uint32_t)(lw[u] >> 32) == tag);
+                float tt, e;
+                two_sum(s.hi, __uint_as_float((uint32_t)hw[u]), tt, e);
+                s.hi = tt;
+                s.lo = (s.lo + (ACC ? __uint_as_float((uint32_t)lw[u]) : 0.f)) + e;
+            }
+        }
+    }
+    s = row_csum<B>(s, lds_hi, lds_lo);
+    ok = __syncthreads_and(good ? 1 : 0) != 0;
+    return s;
+}
+
 // Backward fallback after a wait ran out: wave 0's 64 lanes form the row's whole dot
 // product sum(y * dy) from the inputs, element by element (compensated with exact
 // products for FP32 data, as the slices), reduced over the wave.

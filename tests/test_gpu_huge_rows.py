@@ -226,3 +226,37 @@ def test_widest_row_backward(widest):
         j = min(NW, i + CHUNK)
         assert torch.equal(dx[0, i:j], table[_classes(i, j, 15)]), (i, j)
     log(f"[huge] widest row backward: 15 classes within R16, every element equal to its class")
+
+
+def test_widest_row_rmsnorm(widest):
+    """Residual RMSNorm on the widest row: x as above, r_i = ((i mod 5) - 2) / 4, weight 1.
+    s = x + r is exact in BF16 (multiples of 1/4 below 2), so residual_out must equal it
+    bit for bit; y = s / sqrt(mean(s^2) + eps) has a closed form per class i mod 15."""
+    x, _ = widest
+    r = torch.empty_like(x)
+    for i in range(0, NW, CHUNK):
+        j = min(NW, i + CHUNK)
+        r[0, i:j] = ((_classes(i, j, 5) - 2).float() / 4).to(torch.bfloat16)
+    w = torch.ones(NW, dtype=torch.bfloat16, device=DEV)
+    out = torch.full_like(x, float("nan"))
+    s_out = torch.full_like(x, float("nan"))
+    eps = 1e-6
+    info = sm.plan_for_rmsnorm(x, w, residual=r, eps=eps, out=out, residual_out=s_out)
+    log(f"[huge] widest row rmsnorm: {info['plan_name']}, {info['launches']} launch(es)")
+    sm.rmsnorm(x, w, residual=r, eps=eps, out=out, residual_out=s_out)
+    torch.cuda.synchronize()
+    n15 = _count(15)
+    sc = np.array([(k % 3 - 1) + (k % 5 - 2) / 4 for k in range(15)])
+    q = sum(n15[k] * sc[k] ** 2 for k in range(15)) / NW
+    exact = sc / math.sqrt(q + eps)
+    want = oracle.decode(oracle.encode(exact, "bf16"), "bf16")
+    got = out[0, :15].double().cpu().numpy()
+    assert (np.abs(got - want) <= ulp(want, "bf16") + ULP_GATE["bf16"][2]).all(), (got, want)
+    assert (s_out[0, :15].double().cpu().numpy() == sc).all()
+    ty, ts = out[0, :15].clone(), s_out[0, :15].clone()
+    for i in range(0, NW, CHUNK):
+        j = min(NW, i + CHUNK)
+        cls = _classes(i, j, 15)
+        assert torch.equal(out[0, i:j], ty[cls]), (i, j)
+        assert torch.equal(s_out[0, i:j], ts[cls]), (i, j)
+    log("[huge] widest row rmsnorm: 15 classes within one ulp, residual_out exact, every element equal to its class")

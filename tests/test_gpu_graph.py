@@ -89,12 +89,16 @@ def test_backward_replays():
         compare_bwd(dxs, y, dy, what=f"backward replay {i}")
 
 
-def test_rmsnorm_replays():
-    M, N = 16, 1 << 18
+@pytest.mark.parametrize("M,N", [(16, 1 << 18), (4, 1 << 22)])
+def test_rmsnorm_replays(M, N):
     xs = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
     rs, ys, ss = (torch.empty_like(xs) for _ in range(3))
     wv = torch.empty(N, dtype=torch.bfloat16, device=DEV)
-    assert sm.plan_for_rmsnorm(xs, wv, residual=rs)["plan_name"] == "split"
+    info = sm.plan_for_rmsnorm(xs, wv, residual=rs)
+    # one-launch SPLIT eagerly (two launches under capture), or already the two-launch form
+    # on rows of more than 256 slices, whose second launch sums each row once per workgroup
+    assert info["plan_name"] == ("wide" if N >= 1 << 22 else "split"), info
+    assert N < 1 << 22 or info["waves_per_row"] > 256
     sm.rmsnorm(xs.fill_(1), wv.fill_(1), residual=rs.fill_(0), out=ys, residual_out=ss)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()

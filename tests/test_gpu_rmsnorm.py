@@ -214,6 +214,24 @@ def test_widest_rows_automatic_launch_count(M):
     compare_rms(y, x, r, w, 1e-6, s_gpu=s, what=f"widest {M}x{N}")
 
 
+@pytest.mark.parametrize("dt,M,N", [("bf16", 4, 1 << 22), ("f32", 3, 1 << 21), ("f16", 2, (1 << 22) + 12345)])
+def test_two_launch_rows_of_many_slices(dt, M, N):
+    """Rows of more than 256 slices in the two-launch form: the second launch sums each
+    row's published partials once per workgroup with all its lanes (a fixed tree, so
+    every slice applies bitwise the same total); against the oracle with a residual and
+    residual_out, and repeatable bit for bit."""
+    x, r, w = inputs(M, N, dt, seed=N % 1000 + M)
+    info = sm.plan_for_rmsnorm(x.to(DEV), w.to(DEV), residual=r.to(DEV))
+    log(f"[rms] {dt} {M}x{N}: plan {info['plan_name']} launches {info['launches']} "
+        f"P={info['waves_per_row']} grid={info['grid']}")
+    assert info["launches"] == 2 and info["waves_per_row"] > 256
+    y, s = run(x, r, w, s_out=True)
+    st = compare_rms(y, x, r, w, 1e-6, s_gpu=s, what=f"two launches {dt} {M}x{N}")
+    log(f"[rms] {dt} {M}x{N}: {st}")
+    y2, _ = run(x, r, w, s_out=True)
+    assert torch.equal(y.view(torch.uint8), y2.view(torch.uint8))
+
+
 def test_split_wait_budget_runs_out():
     """The one-launch SPLIT form with a one-poll wait budget (forced from the host):
     slices that give up count the failure and, since neither output aliases x or the

@@ -517,12 +517,11 @@ def record_traffic(fetch_csv: str, write_csv: str) -> dict:
            "hbm_bytes_per_launch": int(round(fetch + write)),
            "traffic_over_algorithmic": round((fetch + write) / alg, 5),
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {os.path.dirname(fetch_csv)} -o fetch -- "
                "python3 -u bench.py --steps 20 --warmup 2 --no-warm --no-cpu-baseline --no-backward",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {os.path.dirname(write_csv)} -o write -- "
                "python3 -u bench.py --steps 20 --warmup 2 --no-warm --no-cpu-baseline --no-backward",
-               "python bench.py --record-traffic gpurun_out/pmc_fetch/fetch_counter_collection.csv "
-               "gpurun_out/pmc_write/write_counter_collection.csv"]}
+               f"python bench.py --record-traffic {fetch_csv} {write_csv}"]}
     path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.json")
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)

@@ -102,9 +102,12 @@ typedef enum sm_status {
  * (the same holds for the backward; the RMSNorm call takes its two-launch form).
  * sm_softmax_plan_query reports the plan of a call on a stream that is not
  * capturing.
- * AUTO takes SPLIT for N > 8192 when a row's slices fit the resident capacity
- * (WIDE otherwise). For N <= 8192 it holds the row in the narrowest
- * measured-best group (16 to 1024 lanes, 1 to 8 vectors per lane), and takes
+ * AUTO runs a row one-pass when N <= 8192, or when the row fits in 4096
+ * 16-byte windows (8192 for FP32 forward rows) and there are at least 128 rows;
+ * otherwise it takes SPLIT when a row's slices fit the resident capacity, WIDE
+ * when they do not (and, for FP32 forward rows of at least 2^17 windows, WIDE
+ * when SPLIT would need four or more rounds). A one-pass row is held in the
+ * narrowest measured-best group (16 to 1024 lanes, 1 to 8 vectors per lane),
  * PERSISTENT when the row groups fit in at most two rounds of resident
  * workgroups, RESIDENT when there are more. */
 typedef enum sm_plan {

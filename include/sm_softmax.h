@@ -197,8 +197,8 @@ int sm_softmax_fwd(const void *in, void *out, int64_t M, int64_t N, int64_t in_s
  * As sm_softmax_fwd, with launch overrides and optional caller scratch.
  *   opts        : NULL = automatic
  *   workspace   : device memory of at least plan_info.workspace_bytes, 16-byte
- *                 aligned, used only by the WIDE and SPLIT plans; NULL = allocate
- *                 stream-ordered as sm_softmax_fwd does. The caller must not
+ *                 aligned, used only by the WIDE and SPLIT plans; NULL = the
+ *                 library's per-stream buffer, as sm_softmax_fwd. The caller must not
  *                 reuse it until the call's work on `stream` has finished.
  */
 int sm_softmax_fwd_ex(const void *in, void *out, int64_t M, int64_t N, int64_t in_stride,
@@ -248,15 +248,17 @@ int sm_softmax_plan_query(const void *in, const void *out, int64_t M, int64_t N,
  *                 overlap of dx with y or dy -> SM_ERR_OVERLAP (y and dy may
  *                 overlap each other: both are only read)
  *   strides     : row strides in elements, >= N when M > 1
- * Plans as for the forward call: one-pass RESIDENT/PERSISTENT for N <= 8192
- * (3*M*N*elem bytes); wider rows SPLIT (one launch, the slices' partial dots
+ * Plans as for the forward call: one-pass RESIDENT/PERSISTENT for N <= 8192, and
+ * for rows of up to 4096 16-byte windows when there are at least 128 of them
+ * (3*M*N*elem bytes); other rows SPLIT (one launch, the slices' partial dots
  * exchanged as the forward exchanges its (max, sum) pairs: 3*M*N*elem bytes; a
  * wait that runs out is counted, and its workgroup then re-reads the row's y and
  * dy for the dot when dx aliases neither, or writes NaN over its slice), or WIDE
  * where a row's slices cannot be resident together or the stream is capturing a
  * graph (two passes, a partial dot per wave, then merge and apply: 5*M*N*elem
- * bytes). SPLIT and WIDE take stream-ordered scratch (M * slices * 32 or
- * M * waves_per_row * 8 bytes), or caller workspace through the _ex form.
+ * bytes). SPLIT and WIDE take their scratch (M * slices * 32 or M * waves_per_row
+ * * 8 bytes) from the library's per-stream buffer, as the forward, or caller
+ * workspace through the _ex form.
  * Returns SM_OK or a negative sm_status; validation as for sm_softmax_fwd.
  */
 int sm_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
@@ -305,9 +307,9 @@ int sm_softmax_bwd_plan_query(const void *y, const void *dy, const void *dx, int
  * graph. A SPLIT wait that runs out is counted as for the softmax; the workgroup
  * then re-reads its row's x (and residual) for the sum of squares when neither y
  * nor residual_out aliases x or the residual, and writes NaN over its slice
- * otherwise. model_bytes counts the compulsory
- * HBM bytes: x, y and, when present, the residual and residual_out once per element,
- * w once (N elements); WIDE reads x and the residual twice. (The pages' requested-
+ * otherwise. model_bytes counts the compulsory HBM bytes: x, y and, when present,
+ * the residual and residual_out once per element, w once (N elements); WIDE reads x
+ * and the residual twice. (The pages' requested-
  * byte convention counts w once per row in addition.)
  * Returns SM_OK or a negative sm_status; validation as for sm_softmax_fwd.
  */

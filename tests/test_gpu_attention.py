@@ -127,9 +127,8 @@ def test_no_keys_and_no_queries():
 
 ATTN_WL = (8 * 32, 2048, 128)   # heads, queries = keys, head dim
 ATTN_CHUNK = 64                  # heads per oracle comparison
-# heads compared whole against the oracle: all 256 in BF16 (the bench's dtype), the
-# first 64 in FP16
-ATTN_CASES = [("bf16", h0) for h0 in range(0, ATTN_WL[0], ATTN_CHUNK)] + [("f16", 0)]
+# every head compared whole against the oracle, in BF16 (the bench's dtype) and FP16
+ATTN_CASES = [(dt, h0) for dt in ("bf16", "f16") for h0 in range(0, ATTN_WL[0], ATTN_CHUNK)]
 _attn_cache = {}
 
 

@@ -246,8 +246,8 @@ def main(argv=None) -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(rows shard across GPUs with no communication; see the design notes).",
-              file=sys.stderr)
+              "(rows shard across GPUs with no communication: each GPU would run the same "
+              "kernel on its own block of rows).", file=sys.stderr)
         return 2
 
     import torch

@@ -59,7 +59,7 @@
  *   2. P = softmax(S) exactly as above (an all -inf row gives zeros);
  *   3. O_id = sum_j P_j v_jd; lse_i = m + log(s) (-inf for an all -inf row).
  *
- * Readings where the pages are silent (listed in the design notes too):
+ * Readings where the pages are silent:
  *   - a row whose entries are all -inf (and an empty row) has no finite
  *     maximum; the online-merge guard of "Measured optimization case studies",
  *     section "Wide rows: loop in one program, or split across programs",
